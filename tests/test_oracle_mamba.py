@@ -1,0 +1,237 @@
+"""Pins for the sequential Mamba oracle (oracle.mamba_seq_fwd / mamba_seq_bwd).
+
+The pages print no test vectors, so the oracle is pinned to things other than
+itself:
+  * central finite differences of its float64 forward under a non-uniform
+    objective that includes the final-state region (the llama.cpp page's
+    verification method), on the small Mamba-2 workload in full and on random
+    tiny shapes (Mamba-2 and Mamba-1, one or two groups);
+  * torch.autograd of an independently written float64 torch forward;
+  * a hand-derived two-step worked example (tests/golden/mamba_scalar_T2.txt);
+  * scipy.signal.lfilter for the time-invariant scalar case (a first-order IIR
+    filter and its time-reversed adjoint);
+  * homogeneity identities that hold exactly for the VJP of this forward;
+  * the five mutations of the llama.cpp page's verification table, each of
+    which must fail the finite-difference gate by a wide margin.
+"""
+import ast
+import math
+import operator
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import fd_grads, rel_maxabs, rel_maxabs_probed
+from selective_state_space_vjp_amd import synth
+
+FD_GATE = 1e-7
+GRADS = (("x", "dx"), ("dt", "d_dt"), ("B", "dB"), ("C", "dC"), ("s0", "d_s0"))
+
+
+def _objective(inp):
+    y, sf = oracle.mamba_seq_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"], nthreads=1)
+    return float(np.sum(inp["dy"] * y) + np.sum(inp["ds_final"] * sf))
+
+
+def _bwd(inp, mutation=oracle.MUT_NONE):
+    return oracle.mamba_seq_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"], inp["dy"],
+                                inp["ds_final"], mutation=mutation, nthreads=1)
+
+
+def _fd_errors(inp, grads, max_per_key=None):
+    fd, counts = fd_grads(_objective, inp, [k for k, _ in GRADS], eps=1e-5, max_per_key=max_per_key)
+    assert all(c > 0 for c in counts.values())
+    return {g: rel_maxabs_probed(grads[g], fd[k]) for k, g in GRADS}
+
+
+def test_fd_small_mamba2_workload_all_elements():
+    w = synth.WORKLOADS["mamba2_seq_small"]
+    inp = synth.mamba_inputs(w["b"], w["T"], w["H"], w["P"], w["N"], w["G"], False, w["seed"])
+    errs = _fd_errors(inp, _bwd(inp))
+    assert max(errs.values()) < FD_GATE, errs
+
+
+@pytest.mark.parametrize("per_state", [False, True])
+@pytest.mark.parametrize("seed", range(4))
+def test_fd_random_tiny_shapes(per_state, seed):
+    rng = np.random.default_rng(100 + seed)
+    G = int(rng.integers(1, 3))
+    H = G * int(rng.integers(1, 3))
+    T, P, N = int(rng.integers(1, 9)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    inp = synth.mamba_inputs(int(rng.integers(1, 3)), T, H, P, N, G, per_state, seed=seed)
+    errs = _fd_errors(inp, _bwd(inp))
+    assert max(errs.values()) < FD_GATE, (T, H, P, N, G, errs)
+
+
+def test_fd_mamba1_workload_sampled():
+    w = synth.WORKLOADS["mamba1_seq"]
+    inp = synth.mamba_inputs(1, 64, 8, 1, w["N"], 1, True, w["seed"])
+    errs = _fd_errors(inp, _bwd(inp), max_per_key=40)
+    assert max(errs.values()) < FD_GATE, errs
+
+
+def _torch_forward(x, dt, A, B, C, s0):
+    """Independent float64 torch forward of the selective scan (for autograd)."""
+    import torch
+    import torch.nn.functional as F
+
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    Bh = B.repeat_interleave(H // G, dim=2)
+    Ch = C.repeat_interleave(H // G, dim=2)
+    delta = F.softplus(dt)
+    s = s0
+    ys = []
+    for t in range(T):
+        d = delta[:, t, :, None, None]
+        a = torch.exp(d * (A[None, :, None, :] if A.dim() == 2 else A[None, :, None, None]))
+        s = a * s + d * x[:, t, :, :, None] * Bh[:, t, :, None, :]
+        ys.append((s * Ch[:, t, :, None, :]).sum(-1))
+    return torch.stack(ys, 1), s
+
+
+@pytest.mark.parametrize("per_state,G", [(False, 1), (False, 2), (True, 1)])
+def test_autograd_independent_forward(per_state, G):
+    import torch
+
+    inp = synth.mamba_inputs(2, 24, 4, 3, 5, G, per_state, seed=7)
+    ts = {k: torch.tensor(v, dtype=torch.float64, requires_grad=k in ("x", "dt", "B", "C", "s0"))
+          for k, v in inp.items()}
+    y, sf = _torch_forward(ts["x"], ts["dt"], ts["A"], ts["B"], ts["C"], ts["s0"])
+    J = (ts["dy"] * y).sum() + (ts["ds_final"] * sf).sum()
+    auto = torch.autograd.grad(J, [ts[k] for k, _ in GRADS])
+    got = _bwd(inp)
+    for (k, g), a in zip(GRADS, auto):
+        assert rel_maxabs(got[g], a.numpy()) < 1e-12, (k, rel_maxabs(got[g], a.numpy()))
+    # and the forward itself
+    y_o, sf_o = oracle.mamba_seq_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"])
+    assert rel_maxabs(y_o, y.detach().numpy()) < 1e-12
+    assert rel_maxabs(sf_o, sf.detach().numpy()) < 1e-12
+
+
+_OPS = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul, ast.Div: operator.truediv}
+
+
+def _eval_expr(text):
+    """Evaluate an arithmetic expression in numbers and L = ln 2 (no names besides L)."""
+    def ev(node):
+        if isinstance(node, ast.Expression):
+            return ev(node.body)
+        if isinstance(node, ast.Constant):
+            return float(node.value)
+        if isinstance(node, ast.Name) and node.id == "L":
+            return math.log(2.0)
+        if isinstance(node, ast.UnaryOp) and isinstance(node.op, ast.USub):
+            return -ev(node.operand)
+        if isinstance(node, ast.BinOp) and type(node.op) in _OPS:
+            return _OPS[type(node.op)](ev(node.left), ev(node.right))
+        raise ValueError(f"unsupported expression: {text}")
+    return ev(ast.parse(text, mode="eval"))
+
+
+def _load_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "mamba_scalar_T2.txt")
+    inputs, outputs = {}, {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            kind, name, idx, expr = line.split(None, 3)
+            table = inputs if kind == "input" else outputs
+            table.setdefault(name, {})[idx] = _eval_expr(expr)
+    return inputs, outputs
+
+
+def test_golden_hand_derived_example():
+    gi, go = _load_golden()
+
+    def seq(name):
+        return np.array([gi[name]["0"], gi[name]["1"]])
+    T = 2
+    inp = dict(
+        x=seq("x").reshape(1, T, 1, 1), dt=seq("dt").reshape(1, T, 1), A=np.array([gi["A"]["-"]]),
+        B=seq("B").reshape(1, T, 1, 1), C=seq("C").reshape(1, T, 1, 1), s0=np.full((1, 1, 1, 1), gi["s0"]["-"]),
+        dy=seq("dy").reshape(1, T, 1, 1), ds_final=np.full((1, 1, 1, 1), gi["ds_final"]["-"]))
+    y, sf = oracle.mamba_seq_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"])
+    g = _bwd(inp)
+    checked = 0
+    for t in ("0", "1"):
+        ti = int(t)
+        for name, arr in (("y", y[0, ti, 0, 0]), ("dx", g["dx"][0, ti, 0, 0]), ("dB", g["dB"][0, ti, 0, 0]),
+                          ("dC", g["dC"][0, ti, 0, 0]), ("d_dt", g["d_dt"][0, ti, 0])):
+            assert arr == pytest.approx(go[name][t], abs=1e-14), (name, t)
+            checked += 1
+    assert sf[0, 0, 0, 0] == pytest.approx(go["s_final"]["-"], abs=1e-14)
+    assert g["d_s0"][0, 0, 0, 0] == pytest.approx(go["d_s0"]["-"], abs=1e-14)
+    assert _objective(inp) == pytest.approx(go["J"]["-"], abs=1e-14)
+    assert checked == 10
+
+
+def test_time_invariant_case_matches_iir_filter():
+    """Constant step, B = C = 1, one scalar state: y is lfilter([delta], [1, -a], x)
+    with initial condition a*s0, and dx is delta times the time-reversed filter of
+    dy plus the seed's geometric tail."""
+    from scipy.signal import lfilter
+
+    T = 50
+    rng = np.random.default_rng(3)
+    dtv = -1.3
+    delta = math.log1p(math.exp(dtv))
+    A = -0.7
+    a = math.exp(delta * A)
+    x = rng.standard_normal(T)
+    dy = rng.standard_normal(T)
+    s0, dsf = 0.37, -1.1
+    inp = dict(x=x.reshape(1, T, 1, 1), dt=np.full((1, T, 1), dtv), A=np.array([A]),
+               B=np.ones((1, T, 1, 1)), C=np.ones((1, T, 1, 1)), s0=np.full((1, 1, 1, 1), s0),
+               dy=dy.reshape(1, T, 1, 1), ds_final=np.full((1, 1, 1, 1), dsf))
+    y, sf = oracle.mamba_seq_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"])
+    y_ref, _ = lfilter([delta], [1.0, -a], x, zi=[a * s0])
+    assert rel_maxabs(y[0, :, 0, 0], y_ref) < 1e-13
+    g = _bwd(inp)
+    adj = lfilter([1.0], [1.0, -a], dy[::-1])[::-1]      # sum_{tau >= t} a^{tau-t} dy_tau
+    tail = dsf * a ** (T - 1 - np.arange(T))              # seed carried back to step t
+    assert rel_maxabs(g["dx"][0, :, 0, 0], delta * (adj + tail)) < 1e-13
+    ds0_ref = a * (adj[0] + dsf * a ** (T - 1))
+    assert g["d_s0"][0, 0, 0, 0] == pytest.approx(ds0_ref, rel=1e-13)
+
+
+@pytest.mark.parametrize("per_state", [False, True])
+def test_homogeneity_identities(per_state):
+    inp = synth.mamba_inputs(2, 96, 4, 5, 6, 2, per_state, seed=11)
+    y, sf = oracle.mamba_seq_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["s0"])
+    J = np.sum(inp["dy"] * y) + np.sum(inp["ds_final"] * sf)
+    g = _bwd(inp)
+    xdx = np.sum(g["dx"] * inp["x"])
+    assert xdx + np.sum(g["d_s0"] * inp["s0"]) == pytest.approx(J, rel=1e-12)
+    assert np.sum(g["dC"] * inp["C"]) == pytest.approx(np.sum(inp["dy"] * y), rel=1e-12)
+    assert np.sum(g["dB"] * inp["B"]) == pytest.approx(xdx, rel=1e-12)
+
+
+def test_mamba1_with_head_constant_decay_equals_mamba2():
+    """Mamba-1 with A[d, n] = A_d is Mamba-2 with one decay per head."""
+    inp = synth.mamba_inputs(1, 40, 6, 1, 5, 1, False, seed=5)
+    per_state = dict(inp)
+    per_state["A"] = np.repeat(inp["A"][:, None], 5, axis=1)
+    g2 = _bwd(inp)
+    g1 = _bwd(per_state)
+    for _, k in GRADS:
+        assert rel_maxabs(g1[k], g2[k]) < 1e-14
+
+
+MUTATIONS = [oracle.MUT_DROP_DA_PATH, oracle.MUT_ZERO_SEED, oracle.MUT_DROP_Y_TO_DS,
+             oracle.MUT_PREV_STATE_IN_DC, oracle.MUT_DROP_SOFTPLUS]
+
+
+@pytest.mark.parametrize("per_state", [False, True])
+@pytest.mark.parametrize("mutation", MUTATIONS)
+def test_mutations_are_caught(mutation, per_state):
+    """Each defect of the llama.cpp page's table fails the FD gate by >= 100x."""
+    inp = synth.mamba_inputs(1, 12, 2, 2, 3, 1, per_state, seed=21)
+    errs = _fd_errors(inp, _bwd(inp, mutation))
+    assert max(errs.values()) > 100 * FD_GATE, errs
+    clean = _fd_errors(inp, _bwd(inp))
+    assert max(clean.values()) < FD_GATE
