@@ -1,0 +1,167 @@
+/*
+ * ssmvjp.h -- C ABI of libssmvjp: the backward pass (VJP) of the selective
+ * state-space scan on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The forward scan keeps a state s_t[h,p,n] per (batch, head):
+ *     delta_t,h = softplus(dt_t,h)                  (dt is the raw, pre-softplus value)
+ *     a_t       = exp(delta_t,h * A)                (A = A_h: Mamba-2, one decay per head;
+ *                                                    A = A_h,n: Mamba-1, one decay per state)
+ *     s_t       = a_t * s_{t-1} + delta_t,h * x_t[h,p] * B_t[g,n]
+ *     y_t[h,p]  = sum_n C_t[g,n] * s_t[h,p,n]       (reads the state after the update)
+ * with s_{-1} = s0 and head h reading group g = h / (H/G).  Given the upstream
+ * gradients dy (of y) and ds_final (of the final state s_{T-1}), the library
+ * returns the five gradients dx, d_dt, dB, dC, d_s0 of
+ *     J = <dy, y> + <ds_final, s_{T-1}>.
+ * This is the reverse-time recurrence of llama.cpp PR "S1-31: SSM_SCAN_BACK --
+ * Mamba has a backward" (the op paragraph: five gradients from one op, both the
+ * per-head and the per-state decay branch), seeded at t = T with the non-zero
+ * final-state gradient (its point 1) and needing s_{t-1} for the decay path of
+ * d_dt (its point 2).
+ *
+ * The chunked entry point computes the same gradients with the chunked SSD
+ * algorithm of burn-mamba "combined_backward.rs" (combined_backward: K1..K4
+ * recompute, reverse chunk loop over the BLUE / ORANGE / K4 backwards, batched
+ * K3 / K2 / K1 backwards), including the fused L*M length of the MIMO form.
+ * The delta-rule entry point is the KDA backward of the K3 notes section
+ * "反向传播推导" (forward F1..F6, BPTT steps 1..6, GVA view+sum).
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are dense, row-major, innermost axis last, and live in device
+ *    memory of the current HIP device.  The caller allocates every input,
+ *    output and workspace buffer; the library allocates nothing and keeps no
+ *    state between calls, so concurrent calls on different streams are safe.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; the caller synchronises.
+ *  - Outputs are overwritten, never accumulated into.  Inputs, outputs and the
+ *    workspace must not overlap.
+ *  - Validation errors (SSMVJP_EINVAL, SSMVJP_EUNSUPPORTED, SSMVJP_EWORKSPACE)
+ *    are returned before anything is enqueued.  SSMVJP_EHIP means a launch
+ *    failed; outputs are then undefined.
+ *  - Results are deterministic: the same inputs give bitwise-identical outputs
+ *    on every call (all reductions run in a fixed order, no float atomics).
+ *  - "big" tensors (x or v, B, C, dy and their gradients) are float32 or
+ *    bfloat16 as selected by `dtype`; everything else is float32.
+ */
+#ifndef SSMVJP_H
+#define SSMVJP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSMVJP_OK = 0,
+  SSMVJP_EINVAL = 1,        /* bad descriptor, NULL required pointer, misaligned pointer */
+  SSMVJP_EUNSUPPORTED = 2,  /* valid arguments outside what the kernels implement */
+  SSMVJP_EWORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace query */
+  SSMVJP_EHIP = 4           /* a HIP launch or runtime call failed */
+} ssmvjp_status;
+
+enum { SSMVJP_F32 = 0, SSMVJP_BF16 = 1 };                         /* dtype of the big tensors */
+enum { SSMVJP_DECAY_PER_HEAD = 0, SSMVJP_DECAY_PER_STATE = 1 };   /* Mamba-2 / Mamba-1 */
+enum { SSMVJP_FORM_MAMBA2 = 0, SSMVJP_FORM_RAW = 1 };             /* (x, dt, A) or (v, da) */
+
+/* ------------------------------------------------------------------------ */
+/* ssm_scan_bwd: sequential reverse recurrence                               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups; /* b, T, H, P, N, G */
+  int32_t decay;      /* SSMVJP_DECAY_PER_HEAD (A is [H]) or SSMVJP_DECAY_PER_STATE (A is [H,N]) */
+  int32_t dtype;      /* SSMVJP_F32 or SSMVJP_BF16 for x, B, C, dy, dx, dB, dC */
+  int32_t ckpt_every; /* K: states are checkpointed every K steps and recomputed per
+                         segment (llama.cpp PR, point 2: checkpoint-every-K against
+                         store-all).  0 = library default.  Outputs are bitwise
+                         identical for every K. */
+  int32_t reserved;   /* must be 0 */
+} ssmvjp_scan_desc;
+
+/* Bytes of device workspace ssm_scan_bwd needs for `desc` (0 is valid). */
+ssmvjp_status ssm_scan_bwd_workspace(const ssmvjp_scan_desc* desc, size_t* bytes);
+
+/* Backward of the sequential selective scan.
+ *   x [b,T,H,P] (dtype)   dt [b,T,H] f32 (raw)   A [H] or [H,N] f32
+ *   B, C [b,T,G,N] (dtype)   s0 [b,H,P,N] f32 (NULL = zeros)
+ *   dy [b,T,H,P] (dtype)   ds_final [b,H,P,N] f32 (NULL = zeros)
+ * Outputs:
+ *   dx [b,T,H,P] (dtype)   d_dt [b,T,H] f32   dB, dC [b,T,G,N] (dtype)
+ *   d_s0 [b,H,P,N] f32
+ * Constraints: b, T >= 0 (an empty batch or sequence enqueues nothing except
+ * d_s0 = ds_final for T = 0); H % G == 0; P*N <= 32768; N <= 1024.
+ * Pointers must be 4-byte aligned (f32) or 2-byte aligned (bf16). */
+ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc,
+                           const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* s0,
+                           const void* dy, const float* ds_final,
+                           void* dx, float* d_dt, void* dB, void* dC, float* d_s0,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* ssd_chunk_bwd: chunked SSD backward (Mamba-2 and Mamba-3 MIMO)            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups; /* b, T, H, P, N, G */
+  int64_t mimo_rank;  /* M: rank of the per-step input (1 for Mamba-2) */
+  int64_t chunk_len;  /* L: steps per chunk; the fused chunk length is L*M */
+  int32_t form;       /* SSMVJP_FORM_MAMBA2: inputs x, dt, A (requires M == 1);
+                         SSMVJP_FORM_RAW: pre-scaled inputs v, da (burn-mamba's
+                         combined_backward arguments) */
+  int32_t dtype;      /* SSMVJP_F32 or SSMVJP_BF16 for x/v, B, C, dy and their gradients */
+} ssmvjp_ssd_desc;
+
+ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes);
+
+/* Chunked backward.  Layouts (all row-major):
+ *   FORM_MAMBA2: x_or_v = x [b,T,H,P], dt_or_da = dt [b,T,H] (raw), A [H]
+ *   FORM_RAW:    x_or_v = v [b,T,M,H,P], dt_or_da = da [b,T,H] (= delta*A), A = NULL
+ *   B, C [b,T,M,G,N]   s0, ds_final, d_s0 [b,H,P,N] f32 (s0/ds_final NULL = zeros)
+ *   dy, dx_or_dv like x_or_v;  d_dt_or_dda like dt_or_da;  dB, dC like B.
+ * A last chunk shorter than L (T % L != 0) is handled as a shorter chunk.
+ * Constraints: H % G == 0; P % 16 == 0, N % 16 == 0, P <= 128, N <= 256;
+ * L*M % 16 == 0 and L*M <= 64 (SSMVJP_EUNSUPPORTED otherwise). */
+ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
+                            const void* x_or_v, const float* dt_or_da, const float* A,
+                            const void* B, const void* C, const float* s0,
+                            const void* dy, const float* ds_final,
+                            void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC, float* d_s0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* delta_rule_bwd: KDA gated delta rule backward                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t batch, seqlen, nqk_heads, nv_heads, dk, dv; /* b, T, H, HV, K, V */
+  float scale;        /* q enters the output as scale * q */
+  int32_t reserved;   /* must be 0 */
+} ssmvjp_delta_desc;
+
+ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* bytes);
+
+/* KDA backward (all float32).
+ *   q, k [b,T,H,K]   v [b,T,HV,V]   beta [b,T,HV]   g [b,T,HV,K] (log gate)
+ *   S0 [b,HV,K,V] (NULL = zeros)   d_o [b,T,HV,V]   dS_final [b,HV,K,V] (NULL = zeros)
+ * Outputs: dq, dk [b,T,H,K]   dv [b,T,HV,V]   dg [b,T,HV,K]   dbeta [b,T,HV]
+ *   dS0 [b,HV,K,V] (NULL = not written).
+ * Value head hv reads qk head hv / (HV/H).  Constraint: HV % H == 0. */
+ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc,
+                             const float* q, const float* k, const float* v, const float* beta,
+                             const float* g, const float* S0, const float* d_o, const float* dS_final,
+                             float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ssmvjp_status_str(ssmvjp_status status);
+
+/* Library version, e.g. "0.1.0" (static storage). */
+const char* ssmvjp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMVJP_H */

@@ -1,0 +1,268 @@
+"""ctypes binding of libssmvjp (C ABI in include/ssmvjp.h).
+
+Argument marshalling only: shape/dtype checks, output and workspace
+allocation through torch's caching allocator, and the current HIP stream.
+Every step of the computation runs in the HIP kernels; there is no CPU path.
+If the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libssmvjp.so"
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
+FORM_MAMBA2, FORM_RAW = 0, 1
+
+EXPORTS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
+           "delta_rule_bwd_workspace", "delta_rule_bwd", "ssmvjp_status_str", "ssmvjp_version")
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("decay", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ckpt_every", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class SsdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("mimo_rank", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
+                ("form", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class DeltaDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nqk_heads", ctypes.c_int64),
+                ("nv_heads", ctypes.c_int64), ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+class SsmVjpError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libssmvjp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(str(LIB_PATH))
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.ssm_scan_bwd_workspace.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(sz)]
+        L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [sz, vp]
+        L.ssd_chunk_bwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
+        L.ssd_chunk_bwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 14 + [sz, vp]
+        L.delta_rule_bwd_workspace.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.POINTER(sz)]
+        L.delta_rule_bwd.argtypes = [ctypes.POINTER(DeltaDesc)] + [vp] * 15 + [sz, vp]
+        for name in ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
+                     "delta_rule_bwd_workspace", "delta_rule_bwd"):
+            getattr(L, name).restype = ctypes.c_int
+        L.ssmvjp_status_str.argtypes = [ctypes.c_int]
+        L.ssmvjp_status_str.restype = ctypes.c_char_p
+        L.ssmvjp_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().ssmvjp_status_str(int(status)).decode()
+
+
+def version():
+    return lib().ssmvjp_version().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; big tensors are float32 or bfloat16")
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _check(fn, status):
+    if status != OK:
+        raise SsmVjpError(fn, status)
+
+
+# --------------------------------------------------------------------------- #
+def scan_desc(x, A, B, ckpt_every=0):
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    decay = DECAY_PER_STATE if A.dim() == 2 else DECAY_PER_HEAD
+    return ScanDesc(b, T, H, P, N, G, decay, _dtype_code(x), int(ckpt_every), 0)
+
+
+def ssm_scan_bwd_workspace(desc):
+    n = ctypes.c_size_t(0)
+    _check("ssm_scan_bwd_workspace", lib().ssm_scan_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, out=None, workspace=None, stream=None):
+    """Sequential selective-scan backward.  Returns dict dx, d_dt, dB, dC, d_s0.
+
+    x, dy [b,T,H,P] and B, C [b,T,G,N] are float32 or bfloat16 (all the same);
+    dt [b,T,H], A [H] (Mamba-2) or [H,N] (Mamba-1), s0, ds_final [b,H,P,N] float32
+    (s0 / ds_final may be None = zeros).
+    """
+    desc = scan_desc(x, A, B, ckpt_every)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev, big = x.device, x.dtype
+    _need(x, "x", big, (b, T, H, P), dev)
+    _need(dy, "dy", big, (b, T, H, P), dev)
+    _need(B, "B", big, (b, T, G, N), dev)
+    _need(C, "C", big, (b, T, G, N), dev)
+    _need(dt, "dt", torch.float32, (b, T, H), dev)
+    _need(A, "A", torch.float32, tuple(A.shape), dev)
+    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
+    _need(ds_final, "ds_final", torch.float32, (b, H, P, N), dev)
+    if out is None:
+        out = dict(dx=torch.empty_like(x), d_dt=torch.empty_like(dt), dB=torch.empty_like(B),
+                   dC=torch.empty_like(C), d_s0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
+    ws, wsb = _workspace(ssm_scan_bwd_workspace(desc), dev, workspace)
+    st = lib().ssm_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy),
+                            _ptr(ds_final), _ptr(out["dx"]), _ptr(out["d_dt"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                            _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
+    _check("ssm_scan_bwd", st)
+    return out
+
+
+# --------------------------------------------------------------------------- #
+def ssd_desc(xv, B, chunk_len, form):
+    if form == FORM_MAMBA2:
+        b, T, H, P = xv.shape
+        M = 1
+        G, N = B.shape[2], B.shape[3]
+    else:
+        b, T, M, H, P = xv.shape
+        G, N = B.shape[3], B.shape[4]
+    return SsdDesc(b, T, H, P, N, G, M, int(chunk_len), form, _dtype_code(xv))
+
+
+def ssd_chunk_bwd_workspace(desc):
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_bwd_workspace", lib().ssd_chunk_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, workspace=None, stream=None):
+    """Chunked SSD backward.
+
+    Mamba-2 form (A given): xv = x [b,T,H,P], dtda = dt [b,T,H] (raw),
+    B, C [b,T,G,N]; returns dict dx, d_dt, dB, dC, d_s0.
+    RAW form (A None): xv = v [b,T,M,H,P], dtda = da [b,T,H], B, C [b,T,M,G,N];
+    returns dict dv, d_da, dB, dC, d_s0.
+    """
+    form = FORM_MAMBA2 if A is not None else FORM_RAW
+    desc = ssd_desc(xv, B, chunk_len, form)
+    b, T, H, P, N = desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate
+    dev, big = xv.device, xv.dtype
+    _need(xv, "x/v", big, tuple(xv.shape), dev)
+    _need(dy, "dy", big, tuple(xv.shape), dev)
+    _need(B, "B", big, tuple(B.shape), dev)
+    _need(C, "C", big, tuple(B.shape), dev)
+    _need(dtda, "dt/da", torch.float32, (b, T, H), dev)
+    if A is not None:
+        _need(A, "A", torch.float32, (H,), dev)
+    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
+    _need(ds_final, "ds_final", torch.float32, (b, H, P, N), dev)
+    names = ("dx", "d_dt") if form == FORM_MAMBA2 else ("dv", "d_da")
+    if out is None:
+        out = {names[0]: torch.empty_like(xv), names[1]: torch.empty_like(dtda), "dB": torch.empty_like(B),
+               "dC": torch.empty_like(C), "d_s0": torch.empty((b, H, P, N), dtype=torch.float32, device=dev)}
+    ws, wsb = _workspace(ssd_chunk_bwd_workspace(desc), dev, workspace)
+    st = lib().ssd_chunk_bwd(ctypes.byref(desc), _ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0),
+                             _ptr(dy), _ptr(ds_final), _ptr(out[names[0]]), _ptr(out[names[1]]), _ptr(out["dB"]),
+                             _ptr(out["dC"]), _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
+    _check("ssd_chunk_bwd", st)
+    return out
+
+
+# --------------------------------------------------------------------------- #
+def delta_desc(q, v, scale):
+    b, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    return DeltaDesc(b, T, H, HV, K, V, float(scale), 0)
+
+
+def delta_rule_bwd_workspace(desc):
+    n = ctypes.c_size_t(0)
+    _check("delta_rule_bwd_workspace", lib().delta_rule_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def delta_rule_bwd(q, k, v, beta, g, S0, d_o, dS_final=None, *, scale, want_dS0=True, out=None, workspace=None,
+                   stream=None):
+    """KDA gated delta-rule backward (float32).  Returns dict dq, dk, dv, dg, dbeta, dS0."""
+    desc = delta_desc(q, v, scale)
+    b, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev, f32 = q.device, torch.float32
+    _need(q, "q", f32, (b, T, H, K), dev)
+    _need(k, "k", f32, (b, T, H, K), dev)
+    _need(v, "v", f32, (b, T, HV, V), dev)
+    _need(beta, "beta", f32, (b, T, HV), dev)
+    _need(g, "g", f32, (b, T, HV, K), dev)
+    _need(S0, "S0", f32, (b, HV, K, V), dev)
+    _need(d_o, "d_o", f32, (b, T, HV, V), dev)
+    _need(dS_final, "dS_final", f32, (b, HV, K, V), dev)
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+                   dbeta=torch.empty_like(beta),
+                   dS0=torch.empty((b, HV, K, V), dtype=f32, device=dev) if want_dS0 else None)
+    ws, wsb = _workspace(delta_rule_bwd_workspace(desc), dev, workspace)
+    st = lib().delta_rule_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
+                              _ptr(d_o), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(ws), wsb,
+                              _stream(stream))
+    _check("delta_rule_bwd", st)
+    return out

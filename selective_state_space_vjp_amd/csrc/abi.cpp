@@ -1,0 +1,184 @@
+// abi.cpp -- the C ABI of libssmvjp: argument validation, workspace sizing and
+// dispatch to the kernel launchers.  Validation runs on the host and returns
+// before anything is enqueued; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ssmvjp.h"
+#include "kernels.h"
+
+using namespace ssmvjp;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t big_elem(int32_t dtype) { return dtype == SSMVJP_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dtype) { return dtype == SSMVJP_F32 || dtype == SSMVJP_BF16; }
+
+ssmvjp_status scan_check(const ssmvjp_scan_desc* d) {
+  if (!d) return SSMVJP_EINVAL;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+    return SSMVJP_EINVAL;
+  if (d->nheads % d->ngroups) return SSMVJP_EINVAL;
+  if (d->decay != SSMVJP_DECAY_PER_HEAD && d->decay != SSMVJP_DECAY_PER_STATE) return SSMVJP_EINVAL;
+  if (!valid_dtype(d->dtype) || d->ckpt_every < 0 || d->reserved != 0) return SSMVJP_EINVAL;
+  if (d->dstate > 1024 || d->headdim * d->dstate > 32768) return SSMVJP_EUNSUPPORTED;
+  const SeqPlan plan = seq_plan(*d);
+  if ((int64_t)plan.NPG * d->dstate > 1024) return SSMVJP_EUNSUPPORTED;
+  if (seq_lds_bytes(*d, plan) > 64 * 1024) return SSMVJP_EUNSUPPORTED;
+  if (d->batch * d->nheads > 0x7fffffff) return SSMVJP_EUNSUPPORTED;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status ssd_check(const ssmvjp_ssd_desc* d) {
+  if (!d) return SSMVJP_EINVAL;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0 ||
+      d->mimo_rank <= 0 || d->chunk_len <= 0)
+    return SSMVJP_EINVAL;
+  if (d->nheads % d->ngroups) return SSMVJP_EINVAL;
+  if (d->form != SSMVJP_FORM_MAMBA2 && d->form != SSMVJP_FORM_RAW) return SSMVJP_EINVAL;
+  if (d->form == SSMVJP_FORM_MAMBA2 && d->mimo_rank != 1) return SSMVJP_EINVAL;
+  if (!valid_dtype(d->dtype)) return SSMVJP_EINVAL;
+  const int64_t LM = d->chunk_len * d->mimo_rank;
+  if (d->headdim % 16 || d->dstate % 16 || d->headdim > 128 || d->dstate > 256) return SSMVJP_EUNSUPPORTED;
+  if (LM % 16 || LM > 64) return SSMVJP_EUNSUPPORTED;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status delta_check(const ssmvjp_delta_desc* d) {
+  if (!d) return SSMVJP_EINVAL;
+  if (d->batch < 0 || d->seqlen < 0 || d->nqk_heads <= 0 || d->nv_heads <= 0 || d->dk <= 0 || d->dv <= 0)
+    return SSMVJP_EINVAL;
+  if (d->nv_heads % d->nqk_heads || d->reserved != 0) return SSMVJP_EINVAL;
+  if (d->dk > 256 || d->dv > 256) return SSMVJP_EUNSUPPORTED;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status hip_status(hipError_t e) { return e == hipSuccess ? SSMVJP_OK : SSMVJP_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ssmvjp_version(void) { return "0.1.0"; }
+
+const char* ssmvjp_status_str(ssmvjp_status s) {
+  switch (s) {
+    case SSMVJP_OK: return "ok";
+    case SSMVJP_EINVAL: return "invalid argument";
+    case SSMVJP_EUNSUPPORTED: return "unsupported shape or option";
+    case SSMVJP_EWORKSPACE: return "workspace missing or too small";
+    case SSMVJP_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+// ------------------------------- ssm_scan_bwd -------------------------------
+
+ssmvjp_status ssm_scan_bwd_workspace(const ssmvjp_scan_desc* desc, size_t* bytes) {
+  if (!bytes) return SSMVJP_EINVAL;
+  ssmvjp_status s = scan_check(desc);
+  if (s != SSMVJP_OK) return s;
+  *bytes = seq_plan(*desc).bytes;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
+                           void* dx, float* d_dt, void* dB, void* dC, float* d_s0, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  ssmvjp_status s = scan_check(desc);
+  if (s != SSMVJP_OK) return s;
+  const ssmvjp_scan_desc& d = *desc;
+  const size_t be = big_elem(d.dtype);
+  const bool has_tokens = d.batch * d.seqlen > 0;
+  const bool has_state = d.batch > 0;
+  if (has_tokens && (!x || !dt || !B || !C || !dy || !dx || !d_dt || !dB || !dC)) return SSMVJP_EINVAL;
+  if (has_state && (!A || !d_s0)) return SSMVJP_EINVAL;
+  const void* pa[] = {x, B, C, dy, dx, dB, dC};
+  for (const void* p : pa)
+    if (p && !aligned(p, be)) return SSMVJP_EINVAL;
+  const void* pf[] = {dt, A, s0, ds_final, d_dt, d_s0};
+  for (const void* p : pf)
+    if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
+  const SeqPlan plan = seq_plan(d);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+    return SSMVJP_EWORKSPACE;
+  if (!has_state) return SSMVJP_OK;
+  SeqPointers ptr{x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, workspace};
+  return hip_status(launch_seq_bwd(d, plan, ptr, (hipStream_t)stream));
+}
+
+// ------------------------------- ssd_chunk_bwd ------------------------------
+
+ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes) {
+  if (!bytes) return SSMVJP_EINVAL;
+  ssmvjp_status s = ssd_check(desc);
+  if (s != SSMVJP_OK) return s;
+  *bytes = ssd_plan(*desc).bytes;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                            const float* A, const void* B, const void* C, const float* s0, const void* dy,
+                            const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
+                            float* d_s0, void* workspace, size_t workspace_bytes, void* stream) {
+  ssmvjp_status s = ssd_check(desc);
+  if (s != SSMVJP_OK) return s;
+  const ssmvjp_ssd_desc& d = *desc;
+  const size_t be = big_elem(d.dtype);
+  const bool has_tokens = d.batch * d.seqlen > 0;
+  const bool has_state = d.batch > 0;
+  if (has_tokens && (!x_or_v || !dt_or_da || !B || !C || !dy || !dx_or_dv || !d_dt_or_dda || !dB || !dC))
+    return SSMVJP_EINVAL;
+  if (has_state && !d_s0) return SSMVJP_EINVAL;
+  if (d.form == SSMVJP_FORM_MAMBA2 && has_tokens && !A) return SSMVJP_EINVAL;
+  // 16-byte alignment lets the kernels use vector loads on the big tensors
+  const void* pa[] = {x_or_v, B, C, dy, dx_or_dv, dB, dC};
+  for (const void* p : pa)
+    if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
+  (void)be;
+  const void* pf[] = {dt_or_da, A, s0, ds_final, d_dt_or_dda, d_s0};
+  for (const void* p : pf)
+    if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
+  const SsdPlan plan = ssd_plan(d);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+    return SSMVJP_EWORKSPACE;
+  if (!has_state) return SSMVJP_OK;
+  SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace};
+  return hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream));
+}
+
+// ------------------------------- delta_rule_bwd -----------------------------
+
+ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* bytes) {
+  if (!bytes) return SSMVJP_EINVAL;
+  ssmvjp_status s = delta_check(desc);
+  if (s != SSMVJP_OK) return s;
+  *bytes = delta_plan(*desc).bytes;
+  return SSMVJP_OK;
+}
+
+ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, const float* k, const float* v,
+                             const float* beta, const float* g, const float* S0, const float* d_o,
+                             const float* dS_final, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                             float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  ssmvjp_status s = delta_check(desc);
+  if (s != SSMVJP_OK) return s;
+  const ssmvjp_delta_desc& d = *desc;
+  const bool has_tokens = d.batch * d.seqlen > 0;
+  if (has_tokens && (!q || !k || !v || !beta || !g || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+    return SSMVJP_EINVAL;
+  const void* pf[] = {q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0};
+  for (const void* p : pf)
+    if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
+  const DeltaPlan plan = delta_plan(d);
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+    return SSMVJP_EWORKSPACE;
+  if (d.batch == 0) return SSMVJP_OK;
+  DeltaPointers ptr{q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace};
+  return hip_status(launch_delta_bwd(d, plan, ptr, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// kernels.h -- host-side launch interface between the C ABI layer (abi.cpp)
+// and the kernel translation units.  Internal to libssmvjp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ssmvjp.h"
+
+namespace ssmvjp {
+
+// ----------------------------- sequential scan -----------------------------
+struct SeqPlan {
+  int64_t K, J;       // checkpoint interval and count
+  int PPT, NPG;       // p values per thread, p groups per workgroup
+  int64_t off_delta, off_sig, off_ck, off_seg, off_dBh, off_dCh;
+  size_t bytes;
+};
+
+struct SeqPointers {
+  const void* x;
+  const float* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* s0;
+  const void* dy;
+  const float* ds_final;
+  void* dx;
+  float* d_dt;
+  void* dB;
+  void* dC;
+  float* d_s0;
+  void* workspace;
+};
+
+SeqPlan seq_plan(const ssmvjp_scan_desc& d);
+size_t seq_lds_bytes(const ssmvjp_scan_desc& d, const SeqPlan& plan);
+hipError_t launch_seq_bwd(const ssmvjp_scan_desc& d, const SeqPlan& plan, const SeqPointers& ptr,
+                          hipStream_t stream);
+
+// ------------------------------ chunked SSD --------------------------------
+struct SsdPlan {
+  int64_t nc;          // number of chunks (last one may be shorter)
+  int64_t LM;          // fused chunk length L*M
+  int64_t hsplit;      // head-split factor of the chunk kernel (1 = writes dB/dC directly)
+  int64_t state_elem;  // bytes per stored state element (2 for bf16, 4 for f32)
+  int64_t off_S, off_dS, off_part;
+  size_t bytes;
+};
+
+struct SsdPointers {
+  const void* xv;
+  const float* dtda;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* s0;
+  const void* dy;
+  const float* ds_final;
+  void* dxv;
+  float* d_dtda;
+  void* dB;
+  void* dC;
+  float* d_s0;
+  void* workspace;
+};
+
+SsdPlan ssd_plan(const ssmvjp_ssd_desc& d);
+hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
+                          hipStream_t stream);
+
+// ------------------------------ delta rule ---------------------------------
+struct DeltaPlan {
+  int64_t CK;          // checkpoint interval (steps)
+  int64_t nck;         // checkpoints per (b, hv)
+  int64_t vsplit;      // value-column blocks per (b, hv)
+  int64_t off_ck, off_dqe, off_dke, off_part;
+  size_t bytes;
+};
+
+struct DeltaPointers {
+  const float *q, *k, *v, *beta, *g, *S0, *d_o, *dS_final;
+  float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+  void* workspace;
+};
+
+DeltaPlan delta_plan(const ssmvjp_delta_desc& d);
+hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
+                            hipStream_t stream);
+
+}  // namespace ssmvjp

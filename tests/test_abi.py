@@ -1,0 +1,129 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_vjp_amd import binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ssmvjp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) >= 8
+    lib = ctypes.CDLL(str(bd.LIB_PATH))
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(bd.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert bd.version() == "0.1.0"
+    assert bd.status_str(bd.EINVAL) == "invalid argument"
+    assert bd.status_str(99) == "unknown status"
+
+
+def _scan(**kw):
+    d = dict(batch=1, seqlen=8, nheads=2, headdim=4, dstate=8, ngroups=1, decay=0, dtype=0, ckpt_every=0, reserved=0)
+    d.update(kw)
+    return bd.ScanDesc(**d)
+
+
+def _ws(fn, desc):
+    n = ctypes.c_size_t(0)
+    st = getattr(bd.lib(), fn)(ctypes.byref(desc), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), bd.OK),
+    (dict(nheads=3, ngroups=2), bd.EINVAL),
+    (dict(headdim=0), bd.EINVAL),
+    (dict(seqlen=-1), bd.EINVAL),
+    (dict(decay=7), bd.EINVAL),
+    (dict(dtype=5), bd.EINVAL),
+    (dict(reserved=1), bd.EINVAL),
+    (dict(ckpt_every=-2), bd.EINVAL),
+    (dict(dstate=2048), bd.EUNSUPPORTED),
+    (dict(headdim=512, dstate=128), bd.EUNSUPPORTED),
+])
+def test_scan_descriptor_validation(kw, status):
+    st, n = _ws("ssm_scan_bwd_workspace", _scan(**kw))
+    assert st == status
+    if status == bd.OK:
+        assert n > 0
+
+
+def test_scan_workspace_shrinks_with_checkpointing():
+    big = _ws("ssm_scan_bwd_workspace", _scan(seqlen=4096, headdim=64, dstate=128, ckpt_every=1))[1]
+    small = _ws("ssm_scan_bwd_workspace", _scan(seqlen=4096, headdim=64, dstate=128, ckpt_every=64))[1]
+    assert small < big / 10
+
+
+def test_scan_rejects_null_pointers_and_small_workspace_without_launching():
+    L = bd.lib()
+    d = _scan()
+    nulls = [None] * 14
+    assert L.ssm_scan_bwd(ctypes.byref(d), *nulls, 0, None) == bd.EINVAL
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(13)]
+    assert L.ssm_scan_bwd(ctypes.byref(d), *fake, None, 0, None) == bd.EWORKSPACE
+    mis = list(fake)
+    mis[1] = ctypes.c_void_p(4096 + 2)  # dt misaligned for float32
+    ws = ctypes.c_void_p(1 << 20)
+    assert L.ssm_scan_bwd(ctypes.byref(d), *mis, ws, 1 << 30, None) == bd.EINVAL
+
+
+def _ssd(**kw):
+    d = dict(batch=1, seqlen=128, nheads=4, headdim=64, dstate=128, ngroups=1, mimo_rank=1, chunk_len=64, form=0,
+             dtype=1)
+    d.update(kw)
+    return bd.SsdDesc(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), bd.OK),
+    (dict(seqlen=100), bd.OK),
+    (dict(nheads=3, ngroups=2), bd.EINVAL),
+    (dict(form=0, mimo_rank=2), bd.EINVAL),
+    (dict(form=3), bd.EINVAL),
+    (dict(chunk_len=0), bd.EINVAL),
+    (dict(headdim=20), bd.EUNSUPPORTED),
+    (dict(dstate=40), bd.EUNSUPPORTED),
+    (dict(chunk_len=72), bd.EUNSUPPORTED),
+])
+def test_ssd_descriptor_validation(kw, status):
+    st, _ = _ws("ssd_chunk_bwd_workspace", _ssd(**kw))
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), bd.OK),
+    (dict(nv_heads=3, nqk_heads=2), bd.EINVAL),
+    (dict(dk=0), bd.EINVAL),
+    (dict(reserved=1), bd.EINVAL),
+])
+def test_delta_descriptor_validation(kw, status):
+    d = dict(batch=1, seqlen=64, nqk_heads=2, nv_heads=4, dk=32, dv=32, scale=0.25, reserved=0)
+    d.update(kw)
+    st, _ = _ws("delta_rule_bwd_workspace", bd.DeltaDesc(**d))
+    assert st == status
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 4, 2, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bd.ssm_scan_bwd(x, torch.zeros(1, 4, 2), torch.zeros(2), torch.zeros(1, 4, 1, 8), torch.zeros(1, 4, 1, 8),
+                        None, x, None)
