@@ -117,8 +117,19 @@ def _check(rc, name):
         raise RuntimeError(f"oracle {name} failed with code {rc}")
 
 
+def default_threads():
+    """Threads for the oracle: OMP_NUM_THREADS if set, else the CPUs this process may use."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def _threads(nthreads):
-    return int(nthreads) if nthreads else (os.cpu_count() or 1)
+    return int(nthreads) if nthreads else default_threads()
 
 
 # --------------------------------------------------------------------------- #

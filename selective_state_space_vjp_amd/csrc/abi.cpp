@@ -40,9 +40,7 @@ ssmvjp_status ssd_check(const ssmvjp_ssd_desc* d) {
   if (d->form != SSMVJP_FORM_MAMBA2 && d->form != SSMVJP_FORM_RAW) return SSMVJP_EINVAL;
   if (d->form == SSMVJP_FORM_MAMBA2 && d->mimo_rank != 1) return SSMVJP_EINVAL;
   if (!valid_dtype(d->dtype)) return SSMVJP_EINVAL;
-  const int64_t LM = d->chunk_len * d->mimo_rank;
-  if (d->headdim % 16 || d->dstate % 16 || d->headdim > 128 || d->dstate > 256) return SSMVJP_EUNSUPPORTED;
-  if (LM % 16 || LM > 64) return SSMVJP_EUNSUPPORTED;
+  if (!ssd_shape_supported(*d)) return SSMVJP_EUNSUPPORTED;
   return SSMVJP_OK;
 }
 

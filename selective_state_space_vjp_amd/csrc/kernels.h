@@ -67,6 +67,7 @@ struct SsdPointers {
   void* workspace;
 };
 
+bool ssd_shape_supported(const ssmvjp_ssd_desc& d);
 SsdPlan ssd_plan(const ssmvjp_ssd_desc& d);
 hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
                           hipStream_t stream);

@@ -100,6 +100,8 @@ def _ssd(**kw):
     (dict(chunk_len=0), bd.EINVAL),
     (dict(headdim=20), bd.EUNSUPPORTED),
     (dict(dstate=40), bd.EUNSUPPORTED),
+    (dict(dstate=256), bd.EUNSUPPORTED),
+    (dict(headdim=112, dstate=80), bd.EUNSUPPORTED),
     (dict(chunk_len=72), bd.EUNSUPPORTED),
 ])
 def test_ssd_descriptor_validation(kw, status):

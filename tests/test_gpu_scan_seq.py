@@ -35,6 +35,7 @@ def _oracle(inp, dtype):
 
 def _compare(got, ref, tol):
     errs = {k: rel_maxabs(got[k], ref[k]) for k in OUTS if ref[k].size}
+    print("[rel_maxabs]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert errs and max(errs.values()) < tol, errs
     return errs
 
