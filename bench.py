@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked selective-scan backward on one MI355X.
+
+Workload: Mamba-2 chunked SSD backward, b=4, T=4096, H=32, P=64, N=128, G=1,
+chunk length 64, bf16 storage with float32 accumulation; seeded synthetic
+inputs already resident in HBM.  One step is one complete backward
+(ssd_chunk_bwd: both stages, every kernel) over the batch.
+
+Prints one JSON line with the metric (tokens/s = b*T per second of wall time
+over exactly --steps steps, bracketed by device synchronisation), the
+roofline of the dominant kernel (algorithmic bytes per launch over its average
+launch time, from HIP events on the launch stream), and the float64 oracle
+timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "scan-backward tokens/s (B·T/s) at Mamba-2 bf16 shape; % of HBM/MFMA roofline"
+WORKLOAD = "mamba2_chunk"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, elem=2, state_elem=2):
+    """Compulsory HBM bytes per launch of each kernel and of the whole path.
+
+    Every input read once, every output written once; the stored chunk states
+    count once written (state scans) and once read (chunk gradients).
+    """
+    b, T, H, P, N, G, L = w["b"], w["T"], w["H"], w["P"], w["N"], w["G"], w["L"]
+    nc = -(-T // L)
+    big_x = b * T * H * P * elem           # x, dy, dx each
+    big_bc = b * T * G * N * elem          # B, C, dB, dC each
+    small = b * T * H * 4                  # dt, d_dt each
+    state32 = b * H * P * N * 4            # s0, ds_final, d_s0 each
+    states = b * nc * H * P * N * state_elem  # stored S or dS
+    scans = 2 * big_x + 2 * big_bc + 2 * small + 3 * state32 + 2 * states
+    grads = 3 * big_x + 4 * big_bc + 2 * small + 2 * states
+    path = 3 * big_x + 4 * big_bc + 2 * small + 3 * state32
+    return {"state_scans": scans, "chunk_grads": grads, "path": path}
+
+
+def traffic_from_profile(kernel_name, src_file):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, src_file), "rb").read()
+        if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return float(rec["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(inp_bf16, w):
+    """The float64 oracle on one of the b sequences (all heads, all T steps)."""
+    import oracle
+
+    threads = oracle.default_threads()
+    c = {k: (v[:1] if hasattr(v, "ndim") and v.ndim >= 3 else v) for k, v in inp_bf16.items()}
+    t0 = time.perf_counter()
+    oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"], nthreads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": w["T"] / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 of {w['b']} sequences (T={w['T']}, all {w['H']} heads), float64 store-all "
+                      f"sequential reverse recurrence, {sec:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py measures one GPU: this build runs on a single MI355X and launches no multi-GPU work "
+            "(the backward shards by batch and B/C group with no exchange; see the design notes).")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from selective_state_space_vjp_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = dict(synth.WORKLOADS[WORKLOAD])
+    inp = synth.workload_inputs(WORKLOAD)
+    c = synth.as_dtype(inp, "bf16", "mamba")
+
+    def dt_(a, dtype=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(dtype).to(dev).contiguous()
+
+    bf = torch.bfloat16
+    x, dy, B, C = dt_(c["x"], bf), dt_(c["dy"], bf), dt_(c["B"], bf), dt_(c["C"], bf)
+    dt, A, s0, dsf = dt_(c["dt"]), dt_(c["A"]), dt_(c["s0"]), dt_(c["ds_final"])
+    call = binding.SsdCall(x, dt, A, B, C, s0, dy, dsf, chunk_len=w["L"])
+
+    for _ in range(args.warmup):
+        call.states()
+        call.grads()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        call.states()
+        ev[i][1].record()
+        call.grads()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    scans_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    grads_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    tokens = w["b"] * w["T"]
+    value = tokens / (ms_per_step / 1e3)
+
+    ab = algorithmic_bytes(w)
+    phases = {
+        "state_scans": {"kernel": "ssd_state_scan_kernel", "ms": scans_ms, "bytes": ab["state_scans"],
+                        "GBps": ab["state_scans"] / (scans_ms * 1e6)},
+        "chunk_grads": {"kernel": "ssd_chunk_bwd_kernel", "ms": grads_ms, "bytes": ab["chunk_grads"],
+                        "GBps": ab["chunk_grads"] / (grads_ms * 1e6)},
+    }
+    dom_name = max(phases, key=lambda k: phases[k]["ms"])
+    dom = phases[dom_name]
+    traffic = traffic_from_profile(dom["kernel"], "selective_state_space_vjp_amd/csrc/ssd_chunk.hip")
+    roofline = {"bound": "hbm", "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom["kernel"],
+                "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_ms": round(dom["ms"], 4)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": w["b"], "seqlen": w["T"], "heads": w["H"], "headdim": w["P"],
+                   "dstate": w["N"], "ngroups": w["G"], "chunk_len": w["L"], "accumulate": "fp32"},
+        "roofline": roofline,
+        "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in phases.items()},
+        "path_roofline": {"algorithmic_bytes": ab["path"], "achieved_GBps": round(ab["path"] / (ms_per_step * 1e6), 1),
+                          "frac": round(ab["path"] / (ms_per_step * 1e6) / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

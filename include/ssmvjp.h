@@ -131,6 +131,29 @@ ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
                             void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC, float* d_s0,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two stages of ssd_chunk_bwd as separate calls, for callers that want to
+ * schedule or time them apart.  ssd_chunk_bwd_states followed by
+ * ssd_chunk_bwd_grads on the same stream, with the same descriptor, inputs and
+ * workspace, is exactly ssd_chunk_bwd.
+ *  - ssd_chunk_bwd_states: the forward and reverse state passing over chunks
+ *    (burn-mamba combined_backward's K1..K4 recompute and the K4 backward with
+ *    the BLUE state gradient).  Writes d_s0 and leaves the chunk-input states
+ *    and the chunk-output state gradients in the workspace.
+ *  - ssd_chunk_bwd_grads: the per-chunk BLUE / ORANGE / K3 / K2 / K1 backwards
+ *    and the Mamba-2 chain, reading the states the previous call left in the
+ *    workspace.  The workspace must not be modified in between.
+ * Arguments mean what they mean for ssd_chunk_bwd. */
+ssmvjp_status ssd_chunk_bwd_states(const ssmvjp_ssd_desc* desc,
+                                   const void* x_or_v, const float* dt_or_da, const float* A,
+                                   const void* B, const void* C, const float* s0,
+                                   const void* dy, const float* ds_final, float* d_s0,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc,
+                                  const void* x_or_v, const float* dt_or_da, const float* A,
+                                  const void* B, const void* C, const void* dy,
+                                  void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* delta_rule_bwd: KDA gated delta rule backward                             */
 /* ------------------------------------------------------------------------ */

@@ -20,7 +20,8 @@ DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
 FORM_MAMBA2, FORM_RAW = 0, 1
 
 EXPORTS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-           "delta_rule_bwd_workspace", "delta_rule_bwd", "ssmvjp_status_str", "ssmvjp_version")
+           "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd",
+           "ssmvjp_status_str", "ssmvjp_version")
 
 
 class ScanDesc(ctypes.Structure):
@@ -64,10 +65,12 @@ def lib():
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [sz, vp]
         L.ssd_chunk_bwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
         L.ssd_chunk_bwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 14 + [sz, vp]
+        L.ssd_chunk_bwd_states.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 10 + [sz, vp]
+        L.ssd_chunk_bwd_grads.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11 + [sz, vp]
         L.delta_rule_bwd_workspace.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.POINTER(sz)]
         L.delta_rule_bwd.argtypes = [ctypes.POINTER(DeltaDesc)] + [vp] * 15 + [sz, vp]
         for name in ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-                     "delta_rule_bwd_workspace", "delta_rule_bwd"):
+                     "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd"):
             getattr(L, name).restype = ctypes.c_int
         L.ssmvjp_status_str.argtypes = [ctypes.c_int]
         L.ssmvjp_status_str.restype = ctypes.c_char_p
@@ -225,6 +228,49 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, w
                              _ptr(out["dC"]), _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
     _check("ssd_chunk_bwd", st)
     return out
+
+
+class SsdCall:
+    """A prepared ssd_chunk_bwd call on fixed device buffers (for repeated timing).
+
+    ``run()`` enqueues the whole backward; ``states()`` then ``grads()`` enqueue
+    its two stages separately (together they are exactly ``run()``).
+    """
+
+    def __init__(self, xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, stream=None):
+        self.form = FORM_MAMBA2 if A is not None else FORM_RAW
+        self.desc = ssd_desc(xv, B, chunk_len, self.form)
+        d = self.desc
+        dev = xv.device
+        names = ("dx", "d_dt") if self.form == FORM_MAMBA2 else ("dv", "d_da")
+        if out is None:
+            out = {names[0]: torch.empty_like(xv), names[1]: torch.empty_like(dtda), "dB": torch.empty_like(B),
+                   "dC": torch.empty_like(C),
+                   "d_s0": torch.empty((d.batch, d.nheads, d.headdim, d.dstate), dtype=torch.float32, device=dev)}
+        self.out = out
+        self.ws, self.wsb = _workspace(ssd_chunk_bwd_workspace(d), dev, None)
+        self.stream = stream
+        p = _ptr
+        self._in = (p(xv), p(dtda), p(A), p(B), p(C))
+        self._s0, self._dy, self._dsf = p(s0), p(dy), p(ds_final)
+        self._o = (p(out[names[0]]), p(out[names[1]]), p(out["dB"]), p(out["dC"]))
+        self._ds0 = p(out["d_s0"])
+        self._keep = (xv, dtda, A, B, C, s0, dy, ds_final)
+
+    def run(self):
+        st = lib().ssd_chunk_bwd(ctypes.byref(self.desc), *self._in, self._s0, self._dy, self._dsf, *self._o,
+                                 self._ds0, _ptr(self.ws), self.wsb, _stream(self.stream))
+        _check("ssd_chunk_bwd", st)
+
+    def states(self):
+        st = lib().ssd_chunk_bwd_states(ctypes.byref(self.desc), *self._in, self._s0, self._dy, self._dsf,
+                                        self._ds0, _ptr(self.ws), self.wsb, _stream(self.stream))
+        _check("ssd_chunk_bwd_states", st)
+
+    def grads(self):
+        st = lib().ssd_chunk_bwd_grads(ctypes.byref(self.desc), *self._in, self._dy, *self._o, _ptr(self.ws),
+                                       self.wsb, _stream(self.stream))
+        _check("ssd_chunk_bwd_grads", st)
 
 
 # --------------------------------------------------------------------------- #

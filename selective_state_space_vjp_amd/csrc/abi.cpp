@@ -118,25 +118,24 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
   return SSMVJP_OK;
 }
 
-ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
-                            const float* A, const void* B, const void* C, const float* s0, const void* dy,
-                            const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
-                            float* d_s0, void* workspace, size_t workspace_bytes, void* stream) {
+static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                             const float* A, const void* B, const void* C, const float* s0, const void* dy,
+                             const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
+                             float* d_s0, void* workspace, size_t workspace_bytes, void* stream, int stages) {
   ssmvjp_status s = ssd_check(desc);
   if (s != SSMVJP_OK) return s;
   const ssmvjp_ssd_desc& d = *desc;
-  const size_t be = big_elem(d.dtype);
   const bool has_tokens = d.batch * d.seqlen > 0;
   const bool has_state = d.batch > 0;
-  if (has_tokens && (!x_or_v || !dt_or_da || !B || !C || !dy || !dx_or_dv || !d_dt_or_dda || !dB || !dC))
-    return SSMVJP_EINVAL;
-  if (has_state && !d_s0) return SSMVJP_EINVAL;
+  const bool states = stages & SSD_STAGE_STATES, grads = stages & SSD_STAGE_GRADS;
+  if (has_tokens && (!x_or_v || !dt_or_da || !B || !C || !dy)) return SSMVJP_EINVAL;
+  if (has_tokens && grads && (!dx_or_dv || !d_dt_or_dda || !dB || !dC)) return SSMVJP_EINVAL;
+  if (has_state && states && !d_s0) return SSMVJP_EINVAL;
   if (d.form == SSMVJP_FORM_MAMBA2 && has_tokens && !A) return SSMVJP_EINVAL;
   // 16-byte alignment lets the kernels use vector loads on the big tensors
   const void* pa[] = {x_or_v, B, C, dy, dx_or_dv, dB, dC};
   for (const void* p : pa)
     if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
-  (void)be;
   const void* pf[] = {dt_or_da, A, s0, ds_final, d_dt_or_dda, d_s0};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
@@ -145,7 +144,31 @@ ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, con
     return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
   SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace};
-  return hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream));
+  return hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+}
+
+ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                            const float* A, const void* B, const void* C, const float* s0, const void* dy,
+                            const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
+                            float* d_s0, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_run(desc, x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace,
+                 workspace_bytes, stream, SSD_STAGE_ALL);
+}
+
+ssmvjp_status ssd_chunk_bwd_states(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                                   const float* A, const void* B, const void* C, const float* s0, const void* dy,
+                                   const float* ds_final, float* d_s0, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return ssd_run(desc, x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, nullptr, nullptr, nullptr, nullptr, d_s0,
+                 workspace, workspace_bytes, stream, SSD_STAGE_STATES);
+}
+
+ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                                  const float* A, const void* B, const void* C, const void* dy, void* dx_or_dv,
+                                  float* d_dt_or_dda, void* dB, void* dC, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return ssd_run(desc, x_or_v, dt_or_da, A, B, C, nullptr, dy, nullptr, dx_or_dv, d_dt_or_dda, dB, dC, nullptr,
+                 workspace, workspace_bytes, stream, SSD_STAGE_GRADS);
 }
 
 // ------------------------------- delta_rule_bwd -----------------------------

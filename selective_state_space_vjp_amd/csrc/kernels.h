@@ -69,8 +69,9 @@ struct SsdPointers {
 
 bool ssd_shape_supported(const ssmvjp_ssd_desc& d);
 SsdPlan ssd_plan(const ssmvjp_ssd_desc& d);
+enum { SSD_STAGE_STATES = 1, SSD_STAGE_GRADS = 2, SSD_STAGE_ALL = 3 };
 hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
-                          hipStream_t stream);
+                          hipStream_t stream, int stages);
 
 // ------------------------------ delta rule ---------------------------------
 struct DeltaPlan {

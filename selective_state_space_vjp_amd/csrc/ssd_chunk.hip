@@ -691,8 +691,7 @@ SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
 }
 
 template <typename T>
-static hipError_t launch_ssd_t(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
-                               hipStream_t stream) {
+static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr) {
   char* ws = (char*)ptr.workspace;
   SsdArgs a;
   a.b = d.batch; a.T = d.seqlen; a.H = d.nheads; a.P = d.headdim; a.N = d.dstate; a.G = d.ngroups;
@@ -704,32 +703,46 @@ static hipError_t launch_ssd_t(const ssmvjp_ssd_desc& d, const SsdPlan& plan, co
   a.S = ws + plan.off_S;
   a.dS = ws + plan.off_dS;
   a.part = (float*)(ws + plan.off_part);
+  return a;
+}
 
-  const int NB = scan_nb(d);
+template <typename T>
+static void launch_states_t(const SsdArgs& a, hipStream_t stream, int NB) {
   const int LDK = (int)a.LM + (sizeof(T) == 2 ? 8 : 4);
   const size_t lds1 = 68 * sizeof(float) + sizeof(T) * (size_t)LDK * (a.P + NB);
   const i64 grid1 = a.b * a.H * 2 * (a.N / NB);
   hipLaunchKernelGGL(ssd_state_scan_kernel<T>, dim3((unsigned)grid1), dim3(256), lds1, stream, a, NB);
-  if (a.T > 0) {
-    const int LDP = (int)a.P + (sizeof(T) == 2 ? 8 : 4);
-    const int LDN = (int)a.N + (sizeof(T) == 2 ? 8 : 4);
-    const size_t lds2 = sizeof(float) * ((size_t)a.LM * (a.LM + 4) + 2 * PB_N * 8 * 64) +
-                        sizeof(T) * (2 * (size_t)a.LM * LDP + (size_t)a.P * LDN);
-    const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
-    hipLaunchKernelGGL(ssd_chunk_bwd_kernel<T>, dim3((unsigned)grid2), dim3(256), lds2, stream, a);
-    if (a.hsplit > 1) {
-      const i64 n = a.b * a.T * a.M * a.G * a.N;
-      hipLaunchKernelGGL(ssd_head_sum_kernel<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, a.part, n,
-                         a.hsplit, (T*)a.dB, (T*)a.dC);
-    }
+}
+
+template <typename T>
+static void launch_grads_t(const SsdArgs& a, hipStream_t stream) {
+  if (a.T == 0) return;
+  const int LDP = (int)a.P + (sizeof(T) == 2 ? 8 : 4);
+  const int LDN = (int)a.N + (sizeof(T) == 2 ? 8 : 4);
+  const size_t lds2 = sizeof(float) * ((size_t)a.LM * (a.LM + 4) + 2 * PB_N * 8 * 64) +
+                      sizeof(T) * (2 * (size_t)a.LM * LDP + (size_t)a.P * LDN);
+  const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
+  hipLaunchKernelGGL(ssd_chunk_bwd_kernel<T>, dim3((unsigned)grid2), dim3(256), lds2, stream, a);
+  if (a.hsplit > 1) {
+    const i64 n = a.b * a.T * a.M * a.G * a.N;
+    hipLaunchKernelGGL(ssd_head_sum_kernel<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, a.part, n,
+                       a.hsplit, (T*)a.dB, (T*)a.dC);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
-                          hipStream_t stream) {
-  if (d.dtype == SSMVJP_BF16) return launch_ssd_t<bf16>(d, plan, ptr, stream);
-  return launch_ssd_t<float>(d, plan, ptr, stream);
+                          hipStream_t stream, int stages) {
+  const int NB = scan_nb(d);
+  if (d.dtype == SSMVJP_BF16) {
+    const SsdArgs a = make_args<bf16>(d, plan, ptr);
+    if (stages & SSD_STAGE_STATES) launch_states_t<bf16>(a, stream, NB);
+    if (stages & SSD_STAGE_GRADS) launch_grads_t<bf16>(a, stream);
+  } else {
+    const SsdArgs a = make_args<float>(d, plan, ptr);
+    if (stages & SSD_STAGE_STATES) launch_states_t<float>(a, stream, NB);
+    if (stages & SSD_STAGE_GRADS) launch_grads_t<float>(a, stream);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace ssmvjp
