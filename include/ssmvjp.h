@@ -121,9 +121,11 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
  *   B, C [b,T,M,G,N]   s0, ds_final, d_s0 [b,H,P,N] f32 (s0/ds_final NULL = zeros)
  *   dy, dx_or_dv like x_or_v;  d_dt_or_dda like dt_or_da;  dB, dC like B.
  * A last chunk shorter than L (T % L != 0) is handled as a shorter chunk.
- * Constraints: H % G == 0; P % 16 == 0, N % 16 == 0, P <= 128, N <= 128;
- * L*M % 16 == 0 and L*M <= 64; (P/16) * (N/16) <= 32 unless N is a multiple
- * of 32 (SSMVJP_EUNSUPPORTED otherwise). */
+ * Constraints (SSMVJP_EUNSUPPORTED otherwise): H % G == 0; P % 16 == 0,
+ * N % 16 == 0, P <= 128, N <= 128; L*M % 16 == 0 and L*M <= 64;
+ * (P/16) * (N/16) <= 32 unless N is a multiple of 32; and the per-chunk
+ * working set fits one workgroup's 160 KiB of LDS (P*N <= 8192 with bf16
+ * at L*M = 64; P*N <= 4096 more or less with float32). */
 ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
                             const void* x_or_v, const float* dt_or_da, const float* A,
                             const void* B, const void* C, const float* s0,

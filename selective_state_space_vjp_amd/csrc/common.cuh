@@ -91,44 +91,131 @@ __device__ __forceinline__ float wave_incl_suffix(float v, int lane) {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-struct frag4 {
-  float v[4];
-};
-
 __device__ __forceinline__ short bf16_bits(float f) {
   bf16 b = (bf16)f;
   return __builtin_bit_cast(short, b);
 }
 
-// D += A * B over one 16-wide k block, with operands rounded to bf16.
-__device__ __forceinline__ void mma_bf16(f32x4& d, const frag4& a, const frag4& b) {
-  s16x4 av = {bf16_bits(a.v[0]), bf16_bits(a.v[1]), bf16_bits(a.v[2]), bf16_bits(a.v[3])};
-  s16x4 bv = {bf16_bits(b.v[0]), bf16_bits(b.v[1]), bf16_bits(b.v[2]), bf16_bits(b.v[3])};
-  d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, d, 0, 0, 0);
-}
-
-// D += A * B over one 16-wide k block in full float32.
-__device__ __forceinline__ void mma_f32(f32x4& d, const frag4& a, const frag4& b) {
-  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], d, 0, 0, 0);
-  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], d, 0, 0, 0);
-  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], d, 0, 0, 0);
-  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], d, 0, 0, 0);
-}
-
-template <typename T>
-struct Mma;
-template <>
-struct Mma<float> {
-  static __device__ __forceinline__ void run(f32x4& d, const frag4& a, const frag4& b) { mma_f32(d, a, b); }
-};
-template <>
-struct Mma<bf16> {
-  static __device__ __forceinline__ void run(f32x4& d, const frag4& a, const frag4& b) { mma_bf16(d, a, b); }
-};
-
 __device__ __forceinline__ f32x4 zero4() {
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return z;
+}
+
+// ---------------------------------------------------------------------------
+// Typed MFMA operand fragments (frag4 layout, see above): four k values per
+// lane, packed bf16 or plain float.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Frag;
+template <>
+struct Frag<float> {
+  float v[4];
+};
+template <>
+struct Frag<bf16> {
+  s16x4 v;
+};
+
+__device__ __forceinline__ float bits_bf16(short s) { return (float)__builtin_bit_cast(bf16, s); }
+
+__device__ __forceinline__ void frag_get(const Frag<float>& f, float o[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = f.v[j];
+}
+__device__ __forceinline__ void frag_get(const Frag<bf16>& f, float o[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = bits_bf16(f.v[j]);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_make(const float v[4]);
+template <>
+__device__ __forceinline__ Frag<float> frag_make<float>(const float v[4]) {
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = v[j];
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<bf16> frag_make<bf16>(const float v[4]) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = bf16_bits(v[j]);
+  return f;
+}
+
+__device__ __forceinline__ void mma(f32x4& d, const Frag<bf16>& a, const Frag<bf16>& b) {
+  d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& d, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], d, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Fragment reads from LDS tiles.
+//
+// colk: the contraction index runs along a row of a row-major tile: lane
+//       (q = lane/16, c = lane%16) gets tile[(c0 + c) * pitch + k0 + 4q + j].
+// rowk: the contraction index runs down the rows: lane gets
+//       tile[(k0 + 4q + j) * pitch + c0 + c].  For bf16 this is one gfx950
+//       transpose read (ds_read_b64_tr_b16): within each 16-lane group, output
+//       lane i, slot j, is element i%4 of the 8-byte chunk addressed by lane
+//       i/4 + 4j, so lane m addresses row k0 + 4q + m/4, columns c0 + 4(m%4)...+3.
+// native: a 16x16 tile stored in MFMA output order (lane-major, 4 values per
+//       lane: element (row 4*(l/16)+j, col l%16) at l*4 + j).  ntv reads it
+//       as-is (k = row); ntv_t reads it transposed (lane gets element
+//       (row c, col 4q + j)), again one transpose read for bf16.
+// All bf16 addresses are 8-byte aligned by construction (pitches and column
+// offsets are multiples of 4 elements).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ Frag<bf16> lds_tr_b16(const bf16* p) {
+  Frag<bf16> f;
+  f.v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16*>(p)));
+  return f;
+}
+
+__device__ __forceinline__ Frag<bf16> ld_colk(const bf16* tile, int pitch, int c0, int k0, int lane) {
+  Frag<bf16> f;
+  f.v = *(const s16x4*)(tile + (c0 + (lane & 15)) * pitch + k0 + 4 * (lane >> 4));
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_colk(const float* tile, int pitch, int c0, int k0, int lane) {
+  const float4 u = *(const float4*)(tile + (c0 + (lane & 15)) * pitch + k0 + 4 * (lane >> 4));
+  Frag<float> f = {{u.x, u.y, u.z, u.w}};
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> ld_rowk(const bf16* tile, int pitch, int k0, int c0, int lane) {
+  const int m = lane & 15;
+  return lds_tr_b16(tile + (k0 + 4 * (lane >> 4) + (m >> 2)) * pitch + c0 + 4 * (m & 3));
+}
+__device__ __forceinline__ Frag<float> ld_rowk(const float* tile, int pitch, int k0, int c0, int lane) {
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = tile[(k0 + 4 * (lane >> 4) + j) * pitch + c0 + (lane & 15)];
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> ld_ntv(const bf16* t, int lane) {
+  Frag<bf16> f;
+  f.v = *(const s16x4*)(t + 4 * lane);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_ntv(const float* t, int lane) {
+  const float4 u = *(const float4*)(t + 4 * lane);
+  Frag<float> f = {{u.x, u.y, u.z, u.w}};
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> ld_ntv_t(const bf16* t, int lane) {
+  const int m = lane & 15;
+  return lds_tr_b16(t + 4 * ((m & 3) * 16 + 4 * (lane >> 4) + (m >> 2)));
+}
+__device__ __forceinline__ Frag<float> ld_ntv_t(const float* t, int lane) {
+  const int c = lane & 15;
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = t[4 * ((c >> 2) * 16 + 4 * (lane >> 4) + j) + (c & 3)];
+  return f;
 }
 
 }  // namespace ssmvjp

@@ -74,29 +74,6 @@ __device__ __forceinline__ i64 native_off(int N, int pt, int nt, int lane, int j
   return ((i64)(pt * (N / 16) + nt) * 64 + lane) * 4 + j;
 }
 
-// 8 consecutive elements -> float[8]
-__device__ __forceinline__ void load8(const float* p, float* o) {
-  const float4 u = *(const float4*)p, v = *(const float4*)(p + 4);
-  o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w; o[4] = v.x; o[5] = v.y; o[6] = v.z; o[7] = v.w;
-}
-__device__ __forceinline__ void load8(const bf16* p, float* o) {
-  typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  const bf16x8 u = *(const bf16x8*)p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (float)u[e];
-}
-// 4 consecutive elements -> frag4
-__device__ __forceinline__ frag4 load4(const float* p) {
-  const float4 u = *(const float4*)p;
-  frag4 f = {{u.x, u.y, u.z, u.w}};
-  return f;
-}
-__device__ __forceinline__ frag4 load4(const bf16* p) {
-  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 u = *(const bf16x4*)p;
-  frag4 f = {{(float)u[0], (float)u[1], (float)u[2], (float)u[3]}};
-  return f;
-}
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
 __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
   typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -104,8 +81,33 @@ __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
   *(bf16x4*)p = u;
 }
 
+// 16-byte global <-> register chunks for staging (8 bf16 or 4 float)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 zero_u4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
+// scale the elements of a 16-byte chunk by s (float math, result in T)
+__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const float*) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(__uint_as_float(u[e]) * s);
+  return o;
+}
+__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __uint_as_float(u[e] << 16) * s, hi = __uint_as_float(u[e] & 0xffff0000u) * s;
+    o[e] = (unsigned)(unsigned short)bf16_bits(lo) | ((unsigned)(unsigned short)bf16_bits(hi) << 16);
+  }
+  return o;
+}
+
 // Per-chunk step sizes for one head, one lane per step l < L (lanes >= L and
 // steps past T get zeros, which keeps cumA flat over a short last chunk).
+// z is this lane's dt (Mamba-2) or da (RAW) value.
 struct ChunkScalars {
   float delta;  // softplus(dt) (Mamba-2) or 1 (RAW)
   float sig;    // sigmoid(dt) (Mamba-2)
@@ -113,10 +115,8 @@ struct ChunkScalars {
   float end;    // cumsum at the last step of the chunk (same in every lane)
 };
 
-__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, i64 bi, i64 h, i64 t0, int Lc, int lane) {
+__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z, bool valid, i64 h, int lane) {
   ChunkScalars s;
-  const bool valid = lane < Lc;
-  const float z = valid ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
   float da;
   if (a.raw) {
     s.delta = 1.0f;
@@ -135,20 +135,30 @@ __device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, i64 bi, 
 // ===========================================================================
 // kernel 1: forward and reverse state scans over chunks
 // ===========================================================================
+constexpr int SCAN_NTH = 256;
 constexpr int SCAN_MAXT = 8;  // state tiles per wave
 
-template <typename T>
-__global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int NB) {
+// Shape parameters CP, CNB (n block), CL, CM: a non-zero value fixes P, the n
+// block, the chunk length or the rank at compile time (the workload shape gets
+// its own instantiation); zero reads it from the arguments.
+template <typename T, int CP, int CNB, int CL, int CM>
+__global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_arg) {
+  constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr bool FIXED = CP && CNB && CL && CM;
+  constexpr int MAXC_O = FIXED ? (CL * CM * CP / E16 + SCAN_NTH - 1) / SCAN_NTH : 64 * 128 / E16 / SCAN_NTH;
+  constexpr int MAXC_B = FIXED ? (CL * CM * CNB / E16 + SCAN_NTH - 1) / SCAN_NTH : 64 * 128 / E16 / SCAN_NTH;
+  constexpr int MAXC = MAXC_O > MAXC_B ? MAXC_O : MAXC_B;  // staging chunks per thread
+  constexpr int PAD = 16 / sizeof(T);
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int P = (int)a.P, N = (int)a.N, LM = (int)a.LM, L = (int)a.L, M = (int)a.M;
+  const int P = CP ? CP : (int)a.P, N = (int)a.N, L = CL ? CL : (int)a.L, M = CM ? CM : (int)a.M;
+  const int NB = CNB ? CNB : nb_arg, LM = L * M;
   const int PT = P / 16, NTB = NB / 16, RB = LM / 16;
-  const int LDK = LM + (sizeof(T) == 2 ? 8 : 4);  // row pitch (elements) of the time-contiguous tiles
-  float* sc = (float*)smem_raw;                    // [64] per-step scale
-  float* misc = sc + 64;                           // [4]
-  T* opT = (T*)(misc + 4);                         // [P][LDK]   v or dy, scaled, time-contiguous
-  T* bcT = opT + P * LDK;                          // [NB][LDK]  B or C, time-contiguous
+  const int PPO = P + PAD, PPB = NB + PAD;  // row pitches (elements) of the staged tiles
+  T* opS = (T*)smem_raw;                    // [LM][PPO]  v or dy rows, scaled per step
+  T* bcS = opS + LM * PPO;                  // [LM][PPB]  B or C rows (this n block)
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
+            r16 = lane & 15;
   const int nblk = N / NB;
   i64 bid = blockIdx.x;
   const int nbi = (int)(bid % nblk);
@@ -162,8 +172,7 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int NB) 
   T* out = (T*)(dir == 0 ? a.S : a.dS);
   const float* init = dir == 0 ? a.s0 : a.dsf;
 
-  // tiles of this wave: ti = pt * NTB + nt, ti % 4 == w
-  const int ntiles = PT * NTB;
+  const int ntiles = PT * NTB;  // tiles of this wave: ti = pt * NTB + nt, ti % 4 == w
   f32x4 st[SCAN_MAXT];
 #pragma unroll
   for (int k = 0; k < SCAN_MAXT; ++k) {
@@ -177,34 +186,48 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int NB) 
     }
   }
 
-  for (i64 step = 0; step < a.nc; ++step) {
-    const i64 c = dir == 0 ? step : a.nc - 1 - step;
+  // register prefetch of one chunk: operand rows, B/C rows, the step values
+  const int oc_row = P / E16, bc_row = NB / E16;
+  u32x4 ro[MAXC], rb[MAXC];
+  float rz = 0.0f;
+  auto issue = [&](i64 c) {
     const i64 t0 = c * L;
     const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
-    if (w == 0) {
-      const ChunkScalars cs = chunk_scalars(a, bi, h, t0, Lc, lane);
-      if (lane < L) sc[lane] = dir == 0 ? cs.delta * expf(cs.end - cs.cum) : expf(cs.cum);
-      if (lane == 0) misc[0] = expf(cs.end);
-    }
-    __syncthreads();
-    // stage the operand rows (scaled per step) and B/C rows, time-contiguous
-    for (int idx = tid; idx < LM * (P / 8); idx += 256) {
-      const int r = idx / (P / 8), p0 = (idx % (P / 8)) * 8, l = r / M, m = r % M;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (l < Lc) load8(op + ix_xv(a, bi, t0 + l, m, h, p0), v);
-      const float s = sc[l];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) opT[(p0 + e) * LDK + r] = (T)(v[e] * s);
+    for (int it = 0; it < MAXC; ++it) {
+      const int idx = tid + it * SCAN_NTH;
+      ro[it] = zero_u4();
+      rb[it] = zero_u4();
+      if (idx < LM * oc_row) {
+        const int r = idx / oc_row, col = (idx % oc_row) * E16, l = r / M, m = r % M;
+        if (l < Lc) ro[it] = load16(op + ix_xv(a, bi, t0 + l, m, h, col));
+      }
+      if (idx < LM * bc_row) {
+        const int r = idx / bc_row, col = (idx % bc_row) * E16, l = r / M, m = r % M;
+        if (l < Lc) rb[it] = load16(bc + ix_bc(a, bi, t0 + l, m, g, n0 + col));
+      }
     }
-    for (int idx = tid; idx < LM * (NB / 8); idx += 256) {
-      const int r = idx / (NB / 8), c0 = (idx % (NB / 8)) * 8, l = r / M, m = r % M;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (l < Lc) load8(bc + ix_bc(a, bi, t0 + l, m, g, n0 + c0), v);
+    rz = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
+  };
+
+  if (a.nc > 0) issue(dir == 0 ? 0 : a.nc - 1);  // T = 0 has no chunk to prefetch
+  for (i64 step = 0; step < a.nc; ++step) {
+    const i64 c = dir == 0 ? step : a.nc - 1 - step;
+    const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
+    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
+    const float sc = dir == 0 ? cs.delta * expf(cs.end - cs.cum) : expf(cs.cum);
+    const float e_end = expf(cs.end);
+    __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bcT[(c0 + e) * LDK + r] = (T)v[e];
+    for (int it = 0; it < MAXC; ++it) {
+      const int idx = tid + it * SCAN_NTH;
+      const int r = idx / oc_row;
+      const float s_r = __shfl(sc, (r / M) & 63, 64);
+      if (idx < LM * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(ro[it], s_r, (const T*)0);
+      if (idx < LM * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = rb[it];
     }
+    if (step + 1 < a.nc) issue(dir == 0 ? c + 1 : c - 1);
     __syncthreads();
-    const float e_end = misc[0];
     T* outc = out + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
 #pragma unroll
     for (int k = 0; k < SCAN_MAXT; ++k) {
@@ -213,11 +236,8 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int NB) 
       const int pt = ti / NTB, nt = ti % NTB;
       store4(outc + native_off(N, pt, n0 / 16 + nt, lane, 0), st[k]);
       f32x4 acc = zero4();
-      for (int kb = 0; kb < RB; ++kb) {
-        const frag4 fa = load4(opT + (16 * pt + r16) * LDK + 16 * kb + 4 * q);
-        const frag4 fb = load4(bcT + (16 * nt + r16) * LDK + 16 * kb + 4 * q);
-        Mma<T>::run(acc, fa, fb);
-      }
+      for (int kb = 0; kb < RB; ++kb)
+        mma(acc, ld_rowk(opS, PPO, 16 * kb, 16 * pt, lane), ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane));
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[k][j] = e_end * st[k][j] + acc[j];
     }
@@ -238,26 +258,52 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int NB) 
 // ===========================================================================
 // kernel 2: per-chunk backward, heads of a group in a loop
 // ===========================================================================
-constexpr int MAXRB = 4;  // L*M <= 64
-constexpr int MAXNW = 2;  // n tiles per wave (N <= 128)
-constexpr int MAXPW = 2;  // p tiles per wave (P <= 128)
-constexpr int MAXG = 3;   // lower-triangular (t, s) tile pairs per wave (RB <= 4)
+constexpr int CH_NW = 8;              // waves per workgroup
+constexpr int CH_NTH = 64 * CH_NW;
+constexpr int MAXRB = 4;              // L*M <= 64
+constexpr int MAXG2 = 2;              // lower-triangular (t, s) tile pairs per wave (<= 10 pairs)
+constexpr int MAXI2 = 4;              // (p tile, row block) items per wave (<= 32 items)
 
 enum { PB_BLUE = 0, PB_OROW, PB_OCOL, PB_DEC, PB_DVX, PB_DEND, PB_N };
 
+// float tile -> operand fragment of type T
 template <typename T>
-__global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
+__device__ __forceinline__ Frag<T> cvt_colk(const float* tile, int pitch, int c0, int k0, int lane) {
+  const Frag<float> f = ld_colk(tile, pitch, c0, k0, lane);
+  return frag_make<T>(f.v);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> cvt_rowk(const float* tile, int pitch, int k0, int c0, int lane) {
+  const Frag<float> f = ld_rowk(tile, pitch, k0, c0, lane);
+  return frag_make<T>(f.v);
+}
+
+template <typename T, int CP, int CN, int CL, int CM>
+__global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
+  constexpr int E16 = 16 / sizeof(T);
+  constexpr bool FIXED = CP && CN && CL && CM;
+  // bf16: S_c is staged in LDS and the next head's data is prefetched into
+  // registers; float32 (twice the bytes) reads S_c straight from global memory
+  // and stages unpadded rows, so that the LDS footprint stays under 160 KiB.
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int PAD = BF ? 8 : 0;
+  constexpr int MAXX = FIXED ? (CL * CM * CP / E16 + CH_NTH - 1) / CH_NTH : 64 * 128 / E16 / CH_NTH;
+  constexpr int MAXS = FIXED ? (CP * CN / E16 + CH_NTH - 1) / CH_NTH : 128 * 128 / E16 / CH_NTH;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int P = (int)a.P, N = (int)a.N, LM = (int)a.LM, L = (int)a.L, M = (int)a.M;
+  const int P = CP ? CP : (int)a.P, N = CN ? CN : (int)a.N, L = CL ? CL : (int)a.L, M = CM ? CM : (int)a.M;
+  const int LM = L * M;
   const int PT = P / 16, NT = N / 16, RB = LM / 16;
-  const int LDC = LM + 4;                          // CB row pitch (float)
-  const int LDP = P + (sizeof(T) == 2 ? 8 : 4);    // x/dy row pitch
-  const int LDN = N + (sizeof(T) == 2 ? 8 : 4);    // dS row pitch
-  float* CB = (float*)smem_raw;                    // [LM][LDC] C.B^T, later the head-summed d_cb
-  float* part = CB + LM * LDC;                     // [2][PB_N][8][64] partial row sums (per wave or per p tile)
-  T* xs = (T*)(part + 2 * PB_N * 8 * 64);          // [LM][LDP] x (Mamba-2) or v (RAW)
-  T* dys = xs + LM * LDP;                          // [LM][LDP] dy
-  T* dSl = dys + LM * LDP;                         // [P][LDN]  dS_{c+1}, row-major
+  const int LDC = LM + 4;     // CB pitch (float)
+  const int LDN = N + PAD;    // B / C pitch
+  const int LDP = P + PAD;    // x / dy pitch
+  float* CBs = (float*)smem_raw;                 // [LM][LDC] C.B^T, later the head-summed d_cb
+  float* pb = CBs + LM * LDC;                    // [PB_N][8][64] partial row sums
+  T* Bs = (T*)(pb + PB_N * 8 * 64);              // [LM][LDN]
+  T* Cs = Bs + LM * LDN;                         // [LM][LDN]
+  T* xs = Cs + LM * LDN;                         // [LM][LDP] x (Mamba-2) or v (RAW)
+  T* dys = xs + LM * LDP;                        // [LM][LDP]
+  T* dSs = dys + LM * LDP;                       // [P*N] dS_{c+1}, native tiles
+  T* Ss = dSs + P * N;                           // [P*N] S_c, native tiles (bf16 only)
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
@@ -269,143 +315,148 @@ __global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
   const i64 c = bid % a.nc, bi = bid / a.nc;
   const i64 t0 = c * L;
   const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
-  const T* Bg = (const T*)a.B;
-  const T* Cg = (const T*)a.C;
   const T* xg = (const T*)a.xv;
   const T* dyg = (const T*)a.dy;
   T* dxg = (T*)a.dxv;
+  const int xrow = P / E16, nrow = N / E16, PN = P * N;
+  auto tile_off = [&](int pt, int nt) { return (pt * NT + nt) * 256; };
 
-  // row r of the chunk's fused L*M length -> (step l, rank m); rows past T are zero
-  auto bc_frag = [&](const T* base, int r, int k0) -> frag4 {  // 4 consecutive n of row r
-    const int l = r / M, m = r % M;
-    if (l >= Lc) {
-      frag4 z = {{0.f, 0.f, 0.f, 0.f}};
-      return z;
+  // ---- B and C rows of the chunk (group g) into LDS ----
+  for (int idx = tid; idx < LM * nrow; idx += CH_NTH) {
+    const int r = idx / nrow, col = (idx % nrow) * E16, l = r / M, m = r % M;
+    u32x4 ub = zero_u4(), uc = zero_u4();
+    if (l < Lc) {
+      ub = load16((const T*)a.B + ix_bc(a, bi, t0 + l, m, g, col));
+      uc = load16((const T*)a.C + ix_bc(a, bi, t0 + l, m, g, col));
     }
-    return load4(base + ix_bc(a, bi, t0 + l, m, g, k0));
-  };
-  auto bc_elem = [&](const T* base, int r, int n) -> float {
-    const int l = r / M, m = r % M;
-    return l < Lc ? ld(base, ix_bc(a, bi, t0 + l, m, g, n)) : 0.0f;
-  };
-
-  // ---- C.B^T for the chunk (K2 recompute), lower-triangular tile pairs ----
-  const int npairs = RB * (RB + 1) / 2;
-  for (int pi = w; pi < RB * RB; pi += 4) {
-    const int rt = pi / RB, rs = pi % RB;
-    f32x4 acc = zero4();
-    if (rs <= rt) {
-      for (int kb = 0; kb < NT; ++kb) {
-        const frag4 fa = bc_frag(Cg, 16 * rt + r16, 16 * kb + 4 * q);
-        const frag4 fb = bc_frag(Bg, 16 * rs + r16, 16 * kb + 4 * q);
-        Mma<T>::run(acc, fa, fb);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) CB[(16 * rt + 4 * q + j) * LDC + 16 * rs + r16] = acc[j];
+    *(u32x4*)(Bs + r * LDN + col) = ub;
+    *(u32x4*)(Cs + r * LDN + col) = uc;
   }
 
-  f32x4 dBacc[MAXRB][MAXNW], dCacc[MAXRB][MAXNW], dcbacc[MAXG];
+  // ---- register prefetch of one head: x/v and dy rows, S_c and dS_{c+1}, dt/da ----
+  u32x4 rx[MAXX], ry[MAXX], rs[MAXS], rd[MAXS];
+  float rz = 0.0f;
+  const i64 hbase = g * a.hpg + hs * a.hph;
+  auto issue = [&](i64 h) {
 #pragma unroll
-  for (int rb = 0; rb < MAXRB; ++rb)
-#pragma unroll
-    for (int k = 0; k < MAXNW; ++k) {
-      dBacc[rb][k] = zero4();
-      dCacc[rb][k] = zero4();
+    for (int it = 0; it < MAXX; ++it) {
+      const int idx = tid + it * CH_NTH;
+      rx[it] = ry[it] = zero_u4();
+      if (idx < LM * xrow) {
+        const int r = idx / xrow, col = (idx % xrow) * E16, l = r / M, m = r % M;
+        if (l < Lc) {
+          rx[it] = load16(xg + ix_xv(a, bi, t0 + l, m, h, col));
+          ry[it] = load16(dyg + ix_xv(a, bi, t0 + l, m, h, col));
+        }
+      }
     }
+    const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+    const T* dSg = (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN;
 #pragma unroll
-  for (int k = 0; k < MAXG; ++k) dcbacc[k] = zero4();
-  int pair_rt[MAXG], pair_rs[MAXG];
+    for (int it = 0; it < MAXS; ++it) {
+      const int idx = tid + it * CH_NTH;
+      rs[it] = rd[it] = zero_u4();
+      if (idx < PN / E16) {
+        if (BF) rs[it] = load16(Sg + idx * E16);
+        rd[it] = load16(dSg + idx * E16);
+      }
+    }
+    rz = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
+  };
+  if (BF) issue(hbase);
+  __syncthreads();  // B, C staged
+
+  // ---- C.B^T (K2 recompute) over the lower-triangular tile pairs; upper pairs zero ----
+  for (int pi = w; pi < RB * RB; pi += CH_NW) {
+    const int rt = pi / RB, rs_ = pi % RB;
+    f32x4 acc = zero4();
+    if (rs_ <= rt)
+      for (int kb = 0; kb < NT; ++kb)
+        mma(acc, ld_colk(Cs, LDN, 16 * rt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * rs_, 16 * kb, lane));
 #pragma unroll
-  for (int k = 0; k < MAXG; ++k) {
-    const int pi = w + 4 * k;
+    for (int j = 0; j < 4; ++j) CBs[(16 * rt + 4 * q + j) * LDC + 16 * rs_ + r16] = acc[j];
+  }
+
+  // per-wave work items
+  const int npairs = RB * (RB + 1) / 2;
+  int pair_rt[MAXG2], pair_rs[MAXG2];
+#pragma unroll
+  for (int k = 0; k < MAXG2; ++k) {
+    const int pi = w + CH_NW * k;
     int rt = 0;
     while (rt < RB && (rt + 1) * (rt + 2) / 2 <= pi) ++rt;
     pair_rt[k] = pi < npairs ? rt : -1;
     pair_rs[k] = pi < npairs ? pi - rt * (rt + 1) / 2 : -1;
   }
+  const int nt_own = w;  // the n tile of this wave (N <= 16 * CH_NW)
+  f32x4 dBacc[MAXRB], dCacc[MAXRB], dcbacc[MAXG2];
+#pragma unroll
+  for (int rb = 0; rb < MAXRB; ++rb) dBacc[rb] = dCacc[rb] = zero4();
+#pragma unroll
+  for (int k = 0; k < MAXG2; ++k) dcbacc[k] = zero4();
 
-  const i64 hbase = g * a.hpg + hs * a.hph;
   for (i64 hh = 0; hh < a.hph; ++hh) {
     const i64 h = hbase + hh;
-    float* pb = part + (hh & 1) * PB_N * 8 * 64;
-    const ChunkScalars cs = chunk_scalars(a, bi, h, t0, Lc, lane);
+    if (!BF) issue(h);
+    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
     const float Ah = a.raw ? 0.0f : a.A[h];
+    // lane shuffles: call them where every lane of the wave is active (a
+    // shuffle under a divergent mask reads zero from inactive source lanes)
     auto cum_of = [&](int l) { return __shfl(cs.cum, l, 64); };
     auto delta_of = [&](int l) { return __shfl(cs.delta, l, 64); };
 
-    __syncthreads();  // previous head is done with xs / dys / dSl (and CB writes on entry)
-    for (int idx = tid; idx < LM * (P / 8); idx += 256) {
-      const int r = idx / (P / 8), p0 = (idx % (P / 8)) * 8, l = r / M, m = r % M;
-      float xv8[8] = {0, 0, 0, 0, 0, 0, 0, 0}, dy8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (l < Lc) {
-        load8(xg + ix_xv(a, bi, t0 + l, m, h, p0), xv8);
-        load8(dyg + ix_xv(a, bi, t0 + l, m, h, p0), dy8);
-      }
+    __syncthreads();  // previous head is done with xs / dys / Ss / dSs (and CB writes on entry)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xs[r * LDP + p0 + e] = (T)xv8[e];
-        dys[r * LDP + p0 + e] = (T)dy8[e];
+    for (int it = 0; it < MAXX; ++it) {
+      const int idx = tid + it * CH_NTH;
+      if (idx < LM * xrow) {
+        const int r = idx / xrow, col = (idx % xrow) * E16;
+        *(u32x4*)(xs + r * LDP + col) = rx[it];
+        *(u32x4*)(dys + r * LDP + col) = ry[it];
       }
     }
+#pragma unroll
+    for (int it = 0; it < MAXS; ++it) {
+      const int idx = tid + it * CH_NTH;
+      if (idx < PN / E16) {
+        if (BF) *(u32x4*)(Ss + idx * E16) = rs[it];
+        *(u32x4*)(dSs + idx * E16) = rd[it];
+      }
+    }
+    if (BF && hh + 1 < a.hph) issue(h + 1);
     __syncthreads();
 
     // ---- BLUE: dC_blue = (dy * exp(cumA)) . S_c ; d_cumA_blue = rowsum(C * dC_blue) ----
-    // ---- K3:   dB_k3 += (exp(end - cumA) v) . dS_{c+1}                            ----
-    // This wave's n tiles of S_c and dS_{c+1} (all p), read in native layout, one
-    // k block at a time; dS_{c+1} is also written row-major to LDS for the
-    // contraction over n below.
-    const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
-    const T* dSg = (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
+    // ---- K3:   dB_k3 += (exp(end - cumA) v) . dS_{c+1} ;  d_end = sum S_c * dS_{c+1} ----
     float dend = 0.0f;
-    {
-      float ecum[MAXRB][4], xscale[MAXRB], bluep[MAXRB][4];
+    if (nt_own < NT) {
+      float xscale[MAXRB];
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
-        const int ra = 16 * rb + r16;  // A-fragment row of this lane
-        xscale[rb] = delta_of(ra / M) * expf(cs.end - cum_of(ra / M));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ecum[rb][j] = expf(cum_of((16 * rb + 4 * q + j) / M));
-          bluep[rb][j] = 0.0f;
-        }
+        const int l = (16 * rb + r16) / M;  // row of this lane's A fragment
+        xscale[rb] = delta_of(l) * expf(cs.end - cum_of(l));
       }
+      f32x4 acc1[MAXRB];
 #pragma unroll
-      for (int k = 0; k < MAXNW; ++k) {
-        const int nt = w + 4 * k;
-        if (nt >= NT) continue;
-        f32x4 acc[MAXRB];
+      for (int rb = 0; rb < MAXRB; ++rb) acc1[rb] = zero4();
+      const T* Scur = BF ? (const T*)Ss : (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+      for (int kb = 0; kb < PT; ++kb) {
+        const Frag<T> fS = ld_ntv(Scur + tile_off(kb, nt_own), lane);
+        const Frag<T> fdS = ld_ntv(dSs + tile_off(kb, nt_own), lane);
+        float vS[4], vdS[4];
+        frag_get(fS, vS);
+        frag_get(fdS, vdS);
 #pragma unroll
-        for (int rb = 0; rb < MAXRB; ++rb) acc[rb] = zero4();
-        for (int kb = 0; kb < PT; ++kb) {
-          const frag4 fS = load4(Sg + native_off(N, kb, nt, lane, 0));
-          const frag4 fdS = load4(dSg + native_off(N, kb, nt, lane, 0));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            dend += fS.v[j] * fdS.v[j];
-            dSl[(16 * kb + 4 * q + j) * LDN + 16 * nt + r16] = (T)fdS.v[j];
-          }
-#pragma unroll
-          for (int rb = 0; rb < MAXRB; ++rb) {
-            if (rb >= RB) break;
-            const int ra = 16 * rb + r16;
-            const frag4 fa = load4(dys + ra * LDP + 16 * kb + 4 * q);
-            Mma<T>::run(acc[rb], fa, fS);
-            frag4 fx = load4(xs + ra * LDP + 16 * kb + 4 * q);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fx.v[j] *= xscale[rb];
-            Mma<T>::run(dBacc[rb][k], fx, fdS);
-          }
-        }
+        for (int j = 0; j < 4; ++j) dend += vS[j] * vdS[j];
 #pragma unroll
         for (int rb = 0; rb < MAXRB; ++rb) {
           if (rb >= RB) break;
+          mma(acc1[rb], ld_colk(dys, LDP, 16 * rb, 16 * kb, lane), fS);
+          float vx[4];
+          frag_get(ld_colk(xs, LDP, 16 * rb, 16 * kb, lane), vx);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float val = acc[rb][j] * ecum[rb][j];
-            dCacc[rb][k][j] += val;
-            bluep[rb][j] += bc_elem(Cg, 16 * rb + 4 * q + j, 16 * nt + r16) * val;
-          }
+          for (int j = 0; j < 4; ++j) vx[j] *= xscale[rb];
+          mma(dBacc[rb], frag_make<T>(vx), fdS);
         }
       }
 #pragma unroll
@@ -413,13 +464,16 @@ __global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
         if (rb >= RB) break;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float s = sum16(bluep[rb][j]);
-          if (r16 == 0) pb[(PB_BLUE * 8 + w) * 64 + 16 * rb + 4 * q + j] = s;
+          const int r = 16 * rb + 4 * q + j;
+          const float val = acc1[rb][j] * expf(cum_of(r / M));
+          dCacc[rb][j] += val;
+          const float s = sum16((float)Cs[r * LDN + 16 * nt_own + r16] * val);
+          if (r16 == 0) pb[(PB_BLUE * 8 + nt_own) * 64 + r] = s;
         }
       }
     }
 
-    // ---- ORANGE: G1 = dy . x^T on lower-triangular tiles; d_cb, row/col sums ----
+    // ---- ORANGE: G1 = dy . x^T on lower-triangular tile pairs; d_cb, row/col sums ----
     {
       float orow[MAXRB][4], ocol[MAXRB];
 #pragma unroll
@@ -429,29 +483,26 @@ __global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
         for (int j = 0; j < 4; ++j) orow[rb][j] = 0.0f;
       }
 #pragma unroll
-      for (int k = 0; k < MAXG; ++k) {
-        const int rt = pair_rt[k], rs = pair_rs[k];
+      for (int k = 0; k < MAXG2; ++k) {
+        const int rt = pair_rt[k], rs_ = pair_rs[k];
         if (rt < 0) continue;
         f32x4 acc = zero4();
-        for (int kb = 0; kb < PT; ++kb) {
-          const frag4 fa = load4(dys + (16 * rt + r16) * LDP + 16 * kb + 4 * q);
-          const frag4 fb = load4(xs + (16 * rs + r16) * LDP + 16 * kb + 4 * q);
-          Mma<T>::run(acc, fa, fb);
-        }
-        const int s = 16 * rs + r16, ls = s / M;
+        for (int kb = 0; kb < PT; ++kb)
+          mma(acc, ld_colk(dys, LDP, 16 * rt, 16 * kb, lane), ld_colk(xs, LDP, 16 * rs_, 16 * kb, lane));
+        const int s_ = 16 * rs_ + r16, ls = s_ / M;
         const float cs_s = cum_of(ls), dls = delta_of(ls);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * rt + 4 * q + j, lt = t / M;
-          const float ct = cum_of(lt);
+          const float ct = cum_of(lt);  // every lane takes part in the shuffle
           const float dec = (ls <= lt && lt < Lc) ? expf(ct - cs_s) : 0.0f;
           const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
           dcbacc[k][j] += dcb;
-          const float dd = dcb * CB[t * LDC + s];
+          const float dd = dcb * CBs[t * LDC + s_];
 #pragma unroll
           for (int rb = 0; rb < MAXRB; ++rb) {
             if (rb == rt) orow[rb][j] += dd;
-            if (rb == rs) ocol[rb] += dd;
+            if (rb == rs_) ocol[rb] += dd;
           }
         }
       }
@@ -467,96 +518,69 @@ __global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
         if (q == 0) pb[(PB_OCOL * 8 + w) * 64 + 16 * rb + r16] = s2;
       }
     }
-    dend = wave_sum(dend);
-    if (lane == 0) pb[(PB_DEND * 8 + w) * 64] = dend;
-    __syncthreads();  // dSl complete
 
     // ---- K3: d_dv = B . dS^T ; ORANGE: d_v_or = (CB * decay)^T . dy ; dx ----
-    // This wave's p tiles, all row blocks.  Partial row sums over p go to one
-    // LDS slot per p tile.
 #pragma unroll
-    for (int k2 = 0; k2 < MAXPW; ++k2) {
-      const int pt = w + 4 * k2;
-      if (pt >= PT) continue;
-      f32x4 acc3[MAXRB], acc5[MAXRB];
-#pragma unroll
-      for (int rb = 0; rb < MAXRB; ++rb) acc3[rb] = acc5[rb] = zero4();
-#pragma unroll 1
-      for (int kb = 0; kb < NT; ++kb) {
-        const frag4 fb = load4(dSl + (16 * pt + r16) * LDN + 16 * kb + 4 * q);
-#pragma unroll
-        for (int rb = 0; rb < MAXRB; ++rb) {
-          if (rb >= RB) break;
-          Mma<T>::run(acc3[rb], bc_frag(Bg, 16 * rb + r16, 16 * kb + 4 * q), fb);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < MAXRB; ++kb) {  // k block of t; rows s of block rb <= kb
-        if (kb >= RB) break;
-        frag4 fd;
-        float ct[4];
+    for (int k2 = 0; k2 < MAXI2; ++k2) {
+      const int it = w + CH_NW * k2;
+      if (it >= PT * RB) continue;
+      const int pt = it / RB, rb = it % RB;
+      f32x4 acc3 = zero4(), acc5 = zero4();
+      for (int kb = 0; kb < NT; ++kb)
+        mma(acc3, ld_colk(Bs, LDN, 16 * rb, 16 * kb, lane), ld_ntv_t(dSs + tile_off(pt, kb), lane));
+      const int s_ = 16 * rb + r16, ls = s_ / M;
+      const float cs_s = cum_of(ls);
+      for (int kb = rb; kb < RB; ++kb) {
+        float fw[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * kb + 4 * q + j;
-          fd.v[j] = (float)dys[t * LDP + 16 * pt + r16];
-          ct[j] = cum_of(t / M);
+          const int t = 16 * kb + 4 * q + j, lt = t / M;
+          const float ct = cum_of(lt);  // every lane takes part in the shuffle
+          fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * expf(ct - cs_s) : 0.0f;
         }
-#pragma unroll
-        for (int rb = 0; rb < MAXRB; ++rb) {
-          if (rb > kb) break;
-          const int s = 16 * rb + r16, ls = s / M;
-          const float cs_s = cum_of(ls);
-          frag4 fw;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int t = 16 * kb + 4 * q + j, lt = t / M;
-            fw.v[j] = (ls <= lt && lt < Lc) ? CB[t * LDC + s] * expf(ct[j] - cs_s) : 0.0f;
-          }
-          Mma<T>::run(acc5[rb], fw, fd);
-        }
+        mma(acc5, frag_make<T>(fw), ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane));
       }
 #pragma unroll
-      for (int rb = 0; rb < MAXRB; ++rb) {
-        if (rb >= RB) break;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, p = 16 * pt + r16;
-          const float dl = delta_of(l);
-          const float edec = expf(cs.end - cum_of(l));
-          const float xval = (float)xs[r * LDP + p];
-          const float dv = acc3[rb][j] * edec + acc5[rb][j];  // d_v = d_v_k3 + d_v_orange
-          if (l < Lc) st(dxg, ix_xv(a, bi, t0 + l, m, h, p), a.raw ? dv : dv * dl);
-          const float s1 = sum16(acc3[rb][j] * dl * xval);     // d_decay = sum_p d_decayed_v . v
-          const float s2 = sum16(dv * xval);
-          if (r16 == 0) {
-            pb[(PB_DEC * 8 + pt) * 64 + r] = s1;
-            pb[(PB_DVX * 8 + pt) * 64 + r] = s2;
-          }
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, p = 16 * pt + r16;
+        const float dl = delta_of(l);
+        const float edec = expf(cs.end - cum_of(l));
+        const float xval = (float)xs[r * LDP + p];
+        const float dv = acc3[j] * edec + acc5[j];  // d_v = d_v_k3 + d_v_orange
+        if (l < Lc) st(dxg, ix_xv(a, bi, t0 + l, m, h, p), a.raw ? dv : dv * dl);
+        const float s1 = sum16(acc3[j] * dl * xval);  // d_decay = sum_p d_decayed_v . v
+        const float s2 = sum16(dv * xval);
+        if (r16 == 0) {
+          pb[(PB_DEC * 8 + pt) * 64 + r] = s1;
+          pb[(PB_DVX * 8 + pt) * 64 + r] = s2;
         }
       }
     }
+    dend = wave_sum(dend);
+    if (lane == 0) pb[(PB_DEND * 8 + w) * 64] = dend;
     __syncthreads();  // partial row sums complete
 
     // ---- d_cumA from its four sources, K1 suffix sum, chain to d_dt (wave 0) ----
     if (w == 0) {
       float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
+      const float c_row = cum_of((lane / M) & 63);  // every lane takes part in the shuffle
       if (lane < LM) {
         float blue = 0, orow = 0, ocol = 0, dec = 0;
-        for (int ww = 0; ww < 4; ++ww) {
-          blue += pb[(PB_BLUE * 8 + ww) * 64 + lane];
-          orow += pb[(PB_OROW * 8 + ww) * 64 + lane];
-          ocol += pb[(PB_OCOL * 8 + ww) * 64 + lane];
+        for (int k = 0; k < NT; ++k) blue += pb[(PB_BLUE * 8 + k) * 64 + lane];
+        for (int k = 0; k < CH_NW; ++k) {
+          orow += pb[(PB_OROW * 8 + k) * 64 + lane];
+          ocol += pb[(PB_OCOL * 8 + k) * 64 + lane];
         }
-        for (int pt = 0; pt < PT; ++pt) {
-          dec += pb[(PB_DEC * 8 + pt) * 64 + lane];
-          dvx += pb[(PB_DVX * 8 + pt) * 64 + lane];
+        for (int k = 0; k < PT; ++k) {
+          dec += pb[(PB_DEC * 8 + k) * 64 + lane];
+          dvx += pb[(PB_DVX * 8 + k) * 64 + lane];
         }
-        qv = dec * expf(cs.end - cum_of(lane / M));
+        qv = dec * expf(cs.end - c_row);
         dc = blue + orow - ocol - qv;
       }
       const float qsum = wave_sum(qv);
       float dendt = 0.0f;
-      for (int ww = 0; ww < 4; ++ww) dendt += pb[(PB_DEND * 8 + ww) * 64];
+      for (int k = 0; k < CH_NW; ++k) dendt += pb[(PB_DEND * 8 + k) * 64];
       dendt *= expf(cs.end);
       // reduce the fused rows over the rank m: step l collects rows l*M .. l*M+M-1
       float dcl = 0.0f, dvxl = 0.0f;
@@ -580,51 +604,34 @@ __global__ void __launch_bounds__(256) ssd_chunk_bwd_kernel(SsdArgs a) {
   // ---- K2 backward on the head-summed d_cb: dC_k2 = d_cb . B, dB_k2 = d_cb^T . C ----
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < MAXG; ++k) {
-    const int rt = pair_rt[k], rs = pair_rs[k];
+  for (int k = 0; k < MAXG2; ++k) {
+    const int rt = pair_rt[k], rs_ = pair_rs[k];
     if (rt < 0) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) CB[(16 * rt + 4 * q + j) * LDC + 16 * rs + r16] = dcbacc[k][j];
+    for (int j = 0; j < 4; ++j) CBs[(16 * rt + 4 * q + j) * LDC + 16 * rs_ + r16] = dcbacc[k][j];
   }
   __syncthreads();
-  float* partB = a.part;
-  float* partC = a.part + a.hsplit * a.b * a.T * a.M * a.G * a.N;
+  if (nt_own < NT) {
+    const i64 stride = a.b * a.T * a.M * a.G * a.N;
 #pragma unroll
-  for (int rb = 0; rb < MAXRB; ++rb) {
-    if (rb >= RB) break;
-#pragma unroll
-    for (int k = 0; k < MAXNW; ++k) {
-      const int nt = w + 4 * k;
-      if (nt >= NT) continue;
-      f32x4 accC = dCacc[rb][k], accB = dBacc[rb][k];
-      for (int kb = 0; kb <= rb; ++kb) {
-        const frag4 fa = load4(CB + (16 * rb + r16) * LDC + 16 * kb + 4 * q);
-        frag4 fb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb.v[j] = bc_elem(Bg, 16 * kb + 4 * q + j, 16 * nt + r16);
-        Mma<T>::run(accC, fa, fb);
-      }
-      for (int kb = rb; kb < RB; ++kb) {
-        frag4 fa, fb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fa.v[j] = CB[(16 * kb + 4 * q + j) * LDC + 16 * rb + r16];
-          fb.v[j] = bc_elem(Cg, 16 * kb + 4 * q + j, 16 * nt + r16);
-        }
-        Mma<T>::run(accB, fa, fb);
-      }
+    for (int rb = 0; rb < MAXRB; ++rb) {
+      if (rb >= RB) break;
+      f32x4 accC = dCacc[rb], accB = dBacc[rb];
+      for (int kb = 0; kb <= rb; ++kb)
+        mma(accC, cvt_colk<T>(CBs, LDC, 16 * rb, 16 * kb, lane), ld_rowk(Bs, LDN, 16 * kb, 16 * nt_own, lane));
+      for (int kb = rb; kb < RB; ++kb)
+        mma(accB, cvt_rowk<T>(CBs, LDC, 16 * kb, 16 * rb, lane), ld_rowk(Cs, LDN, 16 * kb, 16 * nt_own, lane));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, n = 16 * nt + r16;
+        const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, n = 16 * nt_own + r16;
         if (l >= Lc) continue;
         const i64 o = ix_bc(a, bi, t0 + l, m, g, n);
         if (a.hsplit == 1) {
           st((T*)a.dB, o, accB[j]);
           st((T*)a.dC, o, accC[j]);
         } else {
-          const i64 stride = a.b * a.T * a.M * a.G * a.N;
-          partB[hs * stride + o] = accB[j];
-          partC[hs * stride + o] = accC[j];
+          a.part[hs * stride + o] = accB[j];
+          a.part[(a.hsplit + hs) * stride + o] = accC[j];
         }
       }
     }
@@ -663,10 +670,18 @@ static i64 pick_hsplit(const ssmvjp_ssd_desc& d, i64 nc) {
   return hs;
 }
 
+static size_t grads_lds_bytes(const ssmvjp_ssd_desc& d) {
+  const bool bf = d.dtype == SSMVJP_BF16;
+  const size_t e = bf ? 2 : 4, pad = bf ? 8 : 0, LM = (size_t)(d.chunk_len * d.mimo_rank);
+  return 4 * (LM * (LM + 4) + PB_N * 8 * 64) +
+         e * (2 * LM * (d.dstate + pad) + 2 * LM * (d.headdim + pad) + (bf ? 2 : 1) * (size_t)(d.headdim * d.dstate));
+}
+
 bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
-  if (d.headdim % 16 || d.dstate % 16 || d.headdim > 128 || d.dstate > MAXNW * 4 * 16) return false;
+  if (d.headdim % 16 || d.dstate % 16 || d.headdim > 128 || d.dstate > 16 * CH_NW) return false;
   const i64 LM = d.chunk_len * d.mimo_rank;
   if (LM % 16 || LM > MAXRB * 16) return false;
+  if (grads_lds_bytes(d) > 160 * 1024) return false;
   return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_MAXT * 4;
 }
 
@@ -707,22 +722,43 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
 }
 
 template <typename T>
+static size_t states_lds(const SsdArgs& a, int NB) {
+  const int PAD = 16 / sizeof(T);
+  return sizeof(T) * (size_t)a.LM * ((a.P + PAD) + (NB + PAD));
+}
+
+template <typename T>
+static size_t grads_lds(const SsdArgs& a) {
+  const bool bf = sizeof(T) == 2;
+  const int PAD = bf ? 8 : 0;
+  return sizeof(float) * ((size_t)a.LM * (a.LM + 4) + PB_N * 8 * 64) +
+         sizeof(T) * (2 * (size_t)a.LM * (a.N + PAD) + 2 * (size_t)a.LM * (a.P + PAD) + (bf ? 2 : 1) * (size_t)a.P * a.N);
+}
+
+// the Mamba-2 chunked workload shape gets compile-time sizes
+static bool workload_shape(const SsdArgs& a) { return a.P == 64 && a.N == 128 && a.L == 64 && a.M == 1; }
+
+template <typename T>
 static void launch_states_t(const SsdArgs& a, hipStream_t stream, int NB) {
-  const int LDK = (int)a.LM + (sizeof(T) == 2 ? 8 : 4);
-  const size_t lds1 = 68 * sizeof(float) + sizeof(T) * (size_t)LDK * (a.P + NB);
   const i64 grid1 = a.b * a.H * 2 * (a.N / NB);
-  hipLaunchKernelGGL(ssd_state_scan_kernel<T>, dim3((unsigned)grid1), dim3(256), lds1, stream, a, NB);
+  if (workload_shape(a) && NB == 128)
+    hipLaunchKernelGGL((ssd_state_scan_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid1), dim3(SCAN_NTH),
+                       states_lds<T>(a, NB), stream, a, NB);
+  else
+    hipLaunchKernelGGL((ssd_state_scan_kernel<T, 0, 0, 0, 0>), dim3((unsigned)grid1), dim3(SCAN_NTH),
+                       states_lds<T>(a, NB), stream, a, NB);
 }
 
 template <typename T>
 static void launch_grads_t(const SsdArgs& a, hipStream_t stream) {
   if (a.T == 0) return;
-  const int LDP = (int)a.P + (sizeof(T) == 2 ? 8 : 4);
-  const int LDN = (int)a.N + (sizeof(T) == 2 ? 8 : 4);
-  const size_t lds2 = sizeof(float) * ((size_t)a.LM * (a.LM + 4) + 2 * PB_N * 8 * 64) +
-                      sizeof(T) * (2 * (size_t)a.LM * LDP + (size_t)a.P * LDN);
   const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
-  hipLaunchKernelGGL(ssd_chunk_bwd_kernel<T>, dim3((unsigned)grid2), dim3(256), lds2, stream, a);
+  if (workload_shape(a))
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid2), dim3(CH_NTH),
+                       grads_lds<T>(a), stream, a);
+  else
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 0, 0, 0, 0>), dim3((unsigned)grid2), dim3(CH_NTH), grads_lds<T>(a),
+                       stream, a);
   if (a.hsplit > 1) {
     const i64 n = a.b * a.T * a.M * a.G * a.N;
     hipLaunchKernelGGL(ssd_head_sum_kernel<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, a.part, n,

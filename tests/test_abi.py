@@ -102,6 +102,8 @@ def _ssd(**kw):
     (dict(dstate=40), bd.EUNSUPPORTED),
     (dict(dstate=256), bd.EUNSUPPORTED),
     (dict(headdim=112, dstate=80), bd.EUNSUPPORTED),
+    (dict(headdim=128, dstate=128), bd.EUNSUPPORTED),
+    (dict(headdim=128, dstate=64), bd.OK),
     (dict(chunk_len=72), bd.EUNSUPPORTED),
 ])
 def test_ssd_descriptor_validation(kw, status):

@@ -1,5 +1,6 @@
 """Pins for the KDA gated-delta-rule oracle (oracle.kda_fwd / kda_bwd).
 
+  * a hand-derived two-step worked example (tests/golden/kda_scalar_T2.txt);
   * central finite differences of the float64 forward for all five gradients
     and the initial-state gradient, with a non-zero final-state seed;
   * torch.autograd of an independently written torch forward (F1..F6);
@@ -113,3 +114,37 @@ def test_mutations_are_caught(mutation):
     bad = _bwd(inp, mutation)
     errs = {g: rel_maxabs_probed(bad[g], fd[k]) for k, g in KDA_GRADS}
     assert max(errs.values()) > 100 * FD_GATE, errs
+
+
+def test_golden_hand_derived_example():
+    from test_oracle_mamba import _eval_expr
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "kda_scalar_T2.txt")
+    gi, go = {}, {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kind, name, idx, expr = line.split(None, 3)
+        (gi if kind == "input" else go).setdefault(name, {})[idx] = _eval_expr(expr)
+
+    def seq(d, name, shape):
+        return np.array([d[name]["0"], d[name]["1"]]).reshape(shape)
+    inp = dict(q=seq(gi, "q", (1, 2, 1, 1)), k=seq(gi, "k", (1, 2, 1, 1)), v=seq(gi, "v", (1, 2, 1, 1)),
+               beta=seq(gi, "beta", (1, 2, 1)), g=seq(gi, "g", (1, 2, 1, 1)), S0=np.full((1, 1, 1, 1), gi["S0"]["-"]),
+               do=seq(gi, "do", (1, 2, 1, 1)), dS_final=np.full((1, 1, 1, 1), gi["dS_final"]["-"]),
+               scale=gi["scale"]["-"])
+    o, Sf = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["S0"], scale=inp["scale"])
+    got = _bwd(inp)
+    checked = 0
+    for t in ("0", "1"):
+        ti = int(t)
+        for name, val in (("o", o[0, ti, 0, 0]), ("dq", got["dq"][0, ti, 0, 0]), ("dk", got["dk"][0, ti, 0, 0]),
+                          ("dv", got["dv"][0, ti, 0, 0]), ("dg", got["dg"][0, ti, 0, 0]),
+                          ("dbeta", got["dbeta"][0, ti, 0])):
+            assert val == pytest.approx(go[name][t], abs=1e-14), (name, t)
+            checked += 1
+    assert Sf[0, 0, 0, 0] == pytest.approx(go["S_final"]["-"], abs=1e-14)
+    assert got["dS0"][0, 0, 0, 0] == pytest.approx(go["dS0"]["-"], abs=1e-14)
+    assert checked == 12
