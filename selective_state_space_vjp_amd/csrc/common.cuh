@@ -29,29 +29,35 @@ __device__ __forceinline__ float softplus_f(float z) { return z > 20.0f ? z : lo
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions (butterfly, fixed order: every lane ends with the same bits)
+// wave64 reductions.  All lanes end with the sum; each lane's summation order
+// is fixed, so results are identical from run to run.
+//   sum16: over the 16 lanes of a DPP row (lanes with the same lane/16), with
+//          four row rotations folded into v_add_f32_dpp;
+//   sum4q: over the 4 lanes with the same lane%16, with the gfx950
+//          v_permlane16_swap / v_permlane32_swap exchanges (no LDS traffic);
+//   wave_sum = sum4q(sum16(v)).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-
-// sum over the 16 lanes that share (lane / 16): xor over bits 0..3
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+  v += dpp_f<0x128>(v);  // row_ror:8
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x122>(v);  // row_ror:2
+  v += dpp_f<0x121>(v);  // row_ror:1
   return v;
 }
-
-// sum over the 4 lanes that share (lane % 16): xor over bits 4..5
 __device__ __forceinline__ float sum4q(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  v = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
 }
+__device__ __forceinline__ float wave_sum(float v) { return sum4q(sum16(v)); }
+
+// exp(x) through the hardware exp2 (v_exp_f32, relative error a few 1e-8)
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // inclusive prefix sum over the 64 lanes (Hillis-Steele, fixed order)
 __device__ __forceinline__ float wave_incl_scan(float v, int lane) {

@@ -215,8 +215,8 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_a
     const i64 c = dir == 0 ? step : a.nc - 1 - step;
     const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
     const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
-    const float sc = dir == 0 ? cs.delta * expf(cs.end - cs.cum) : expf(cs.cum);
-    const float e_end = expf(cs.end);
+    const float sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
+    const float e_end = exp_hw(cs.end);
     __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
@@ -297,8 +297,11 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   const int LDN = N + PAD;    // B / C pitch
   const int LDP = P + PAD;    // x / dy pitch
   float* CBs = (float*)smem_raw;                 // [LM][LDC] C.B^T, later the head-summed d_cb
-  float* pb = CBs + LM * LDC;                    // [PB_N][8][64] partial row sums
-  T* Bs = (T*)(pb + PB_N * 8 * 64);              // [LM][LDN]
+  // partial row sums [PB_N][8][64]; bf16 keeps two sets so that a head's
+  // d_cumA assembly can run one head later, overlapped with the next head
+  constexpr int NPB = BF ? 2 : 1;
+  float* pbase = CBs + LM * LDC;
+  T* Bs = (T*)(pbase + NPB * PB_N * 8 * 64);     // [LM][LDN]
   T* Cs = Bs + LM * LDN;                         // [LM][LDN]
   T* xs = Cs + LM * LDN;                         // [LM][LDP] x (Mamba-2) or v (RAW)
   T* dys = xs + LM * LDP;                        // [LM][LDP]
@@ -315,9 +318,16 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   const i64 c = bid % a.nc, bi = bid / a.nc;
   const i64 t0 = c * L;
   const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
-  const T* xg = (const T*)a.xv;
-  const T* dyg = (const T*)a.dy;
-  T* dxg = (T*)a.dxv;
+  // per-chunk base pointers; offsets inside a chunk are 32-bit
+  const int xrs = (int)(a.H * P), brs = (int)(a.G * N);  // fused-row strides of x/dy/dx and B/C/dB/dC
+  const i64 xoff0 = (bi * a.T + t0) * M * a.H * P, boff0 = (bi * a.T + t0) * M * a.G * N + g * N;
+  const T* xg = (const T*)a.xv + xoff0;
+  const T* dyg = (const T*)a.dy + xoff0;
+  T* dxg = (T*)a.dxv + xoff0;
+  const T* Bg = (const T*)a.B + boff0;
+  const T* Cg = (const T*)a.C + boff0;
+  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
+  float* ddtg = a.d_dtda + (bi * a.T + t0) * a.H;
   const int xrow = P / E16, nrow = N / E16, PN = P * N;
   auto tile_off = [&](int pt, int nt) { return (pt * NT + nt) * 256; };
 
@@ -325,9 +335,10 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   for (int idx = tid; idx < LM * nrow; idx += CH_NTH) {
     const int r = idx / nrow, col = (idx % nrow) * E16, l = r / M, m = r % M;
     u32x4 ub = zero_u4(), uc = zero_u4();
+    (void)m;
     if (l < Lc) {
-      ub = load16((const T*)a.B + ix_bc(a, bi, t0 + l, m, g, col));
-      uc = load16((const T*)a.C + ix_bc(a, bi, t0 + l, m, g, col));
+      ub = load16(Bg + r * brs + col);
+      uc = load16(Cg + r * brs + col);
     }
     *(u32x4*)(Bs + r * LDN + col) = ub;
     *(u32x4*)(Cs + r * LDN + col) = uc;
@@ -343,10 +354,10 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
       const int idx = tid + it * CH_NTH;
       rx[it] = ry[it] = zero_u4();
       if (idx < LM * xrow) {
-        const int r = idx / xrow, col = (idx % xrow) * E16, l = r / M, m = r % M;
+        const int r = idx / xrow, col = (idx % xrow) * E16, l = r / M;
         if (l < Lc) {
-          rx[it] = load16(xg + ix_xv(a, bi, t0 + l, m, h, col));
-          ry[it] = load16(dyg + ix_xv(a, bi, t0 + l, m, h, col));
+          rx[it] = load16(xg + r * xrs + (int)h * P + col);
+          ry[it] = load16(dyg + r * xrs + (int)h * P + col);
         }
       }
     }
@@ -361,7 +372,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         rd[it] = load16(dSg + idx * E16);
       }
     }
-    rz = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
+    rz = lane < Lc ? dtg[lane * (int)a.H + (int)h] : 0.0f;
   };
   if (BF) issue(hbase);
   __syncthreads();  // B, C staged
@@ -395,9 +406,52 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 #pragma unroll
   for (int k = 0; k < MAXG2; ++k) dcbacc[k] = zero4();
 
+  // d_cumA from its four sources, the K1 suffix sum and the chain to d_dt for
+  // one head, from the partial row sums in pb; run by a single wave.
+  auto epilogue = [&](i64 h, const ChunkScalars& cs, float Ah, const float* pb) {
+    auto cum_of = [&](int l) { return __shfl(cs.cum, l, 64); };
+    float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
+    const float c_row = cum_of((lane / M) & 63);  // every lane takes part in the shuffle
+    if (lane < LM) {
+      float blue = 0, orow = 0, ocol = 0, dec = 0;
+      for (int k = 0; k < NT; ++k) blue += pb[(PB_BLUE * 8 + k) * 64 + lane];
+      for (int k = 0; k < CH_NW; ++k) {
+        orow += pb[(PB_OROW * 8 + k) * 64 + lane];
+        ocol += pb[(PB_OCOL * 8 + k) * 64 + lane];
+      }
+      for (int k = 0; k < PT; ++k) {
+        dec += pb[(PB_DEC * 8 + k) * 64 + lane];
+        dvx += pb[(PB_DVX * 8 + k) * 64 + lane];
+      }
+      qv = dec * exp_hw(cs.end - c_row);
+      dc = blue + orow - ocol - qv;
+    }
+    const float qsum = wave_sum(qv);
+    float dendt = 0.0f;
+    for (int k = 0; k < CH_NW; ++k) dendt += pb[(PB_DEND * 8 + k) * 64];
+    dendt *= exp_hw(cs.end);
+    // reduce the fused rows over the rank m: step l collects rows l*M .. l*M+M-1
+    float dcl = 0.0f, dvxl = 0.0f;
+    for (int m = 0; m < M; ++m) {
+      const int src = (lane * M + m) & 63;
+      const float v1 = __shfl(dc, src, 64), v2 = __shfl(dvx, src, 64);
+      if (lane < L) {
+        dcl += v1;
+        dvxl += v2;
+      }
+    }
+    if (lane == Lc - 1) dcl += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
+    const float dda = wave_incl_suffix(lane < Lc ? dcl : 0.0f, lane);
+    if (lane < Lc) ddtg[lane * (int)a.H + (int)h] = a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
+  };
+  i64 prev_h = 0;
+  ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
+  float prev_Ah = 0.0f;
+
   for (i64 hh = 0; hh < a.hph; ++hh) {
     const i64 h = hbase + hh;
     if (!BF) issue(h);
+    float* pb = pbase + (BF ? (hh & 1) * PB_N * 8 * 64 : 0);
     const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
     const float Ah = a.raw ? 0.0f : a.A[h];
     // lane shuffles: call them where every lane of the wave is active (a
@@ -425,6 +479,10 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     }
     if (BF && hh + 1 < a.hph) issue(h + 1);
     __syncthreads();
+    // the previous head's partial sums are complete: assemble its d_cumA on a
+    // rotating wave while the other waves start on this head
+    if (BF && hh > 0 && w == (int)((hh - 1) % CH_NW))
+      epilogue(prev_h, prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
 
     // ---- BLUE: dC_blue = (dy * exp(cumA)) . S_c ; d_cumA_blue = rowsum(C * dC_blue) ----
     // ---- K3:   dB_k3 += (exp(end - cumA) v) . dS_{c+1} ;  d_end = sum S_c * dS_{c+1} ----
@@ -434,7 +492,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
         const int l = (16 * rb + r16) / M;  // row of this lane's A fragment
-        xscale[rb] = delta_of(l) * expf(cs.end - cum_of(l));
+        xscale[rb] = delta_of(l) * exp_hw(cs.end - cum_of(l));
       }
       f32x4 acc1[MAXRB];
 #pragma unroll
@@ -465,7 +523,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * rb + 4 * q + j;
-          const float val = acc1[rb][j] * expf(cum_of(r / M));
+          const float val = acc1[rb][j] * exp_hw(cum_of(r / M));
           dCacc[rb][j] += val;
           const float s = sum16((float)Cs[r * LDN + 16 * nt_own + r16] * val);
           if (r16 == 0) pb[(PB_BLUE * 8 + nt_own) * 64 + r] = s;
@@ -495,7 +553,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * rt + 4 * q + j, lt = t / M;
           const float ct = cum_of(lt);  // every lane takes part in the shuffle
-          const float dec = (ls <= lt && lt < Lc) ? expf(ct - cs_s) : 0.0f;
+          const float dec = (ls <= lt && lt < Lc) ? exp_hw(ct - cs_s) : 0.0f;
           const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
           dcbacc[k][j] += dcb;
           const float dd = dcb * CBs[t * LDC + s_];
@@ -536,18 +594,18 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * kb + 4 * q + j, lt = t / M;
           const float ct = cum_of(lt);  // every lane takes part in the shuffle
-          fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * expf(ct - cs_s) : 0.0f;
+          fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * exp_hw(ct - cs_s) : 0.0f;
         }
         mma(acc5, frag_make<T>(fw), ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, p = 16 * pt + r16;
+        const int r = 16 * rb + 4 * q + j, l = r / M, p = 16 * pt + r16;
         const float dl = delta_of(l);
-        const float edec = expf(cs.end - cum_of(l));
+        const float edec = exp_hw(cs.end - cum_of(l));
         const float xval = (float)xs[r * LDP + p];
         const float dv = acc3[j] * edec + acc5[j];  // d_v = d_v_k3 + d_v_orange
-        if (l < Lc) st(dxg, ix_xv(a, bi, t0 + l, m, h, p), a.raw ? dv : dv * dl);
+        if (l < Lc) st(dxg, r * xrs + (int)h * P + p, a.raw ? dv : dv * dl);
         const float s1 = sum16(acc3[j] * dl * xval);  // d_decay = sum_p d_decayed_v . v
         const float s2 = sum16(dv * xval);
         if (r16 == 0) {
@@ -560,45 +618,19 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     if (lane == 0) pb[(PB_DEND * 8 + w) * 64] = dend;
     __syncthreads();  // partial row sums complete
 
-    // ---- d_cumA from its four sources, K1 suffix sum, chain to d_dt (wave 0) ----
-    if (w == 0) {
-      float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
-      const float c_row = cum_of((lane / M) & 63);  // every lane takes part in the shuffle
-      if (lane < LM) {
-        float blue = 0, orow = 0, ocol = 0, dec = 0;
-        for (int k = 0; k < NT; ++k) blue += pb[(PB_BLUE * 8 + k) * 64 + lane];
-        for (int k = 0; k < CH_NW; ++k) {
-          orow += pb[(PB_OROW * 8 + k) * 64 + lane];
-          ocol += pb[(PB_OCOL * 8 + k) * 64 + lane];
-        }
-        for (int k = 0; k < PT; ++k) {
-          dec += pb[(PB_DEC * 8 + k) * 64 + lane];
-          dvx += pb[(PB_DVX * 8 + k) * 64 + lane];
-        }
-        qv = dec * expf(cs.end - c_row);
-        dc = blue + orow - ocol - qv;
-      }
-      const float qsum = wave_sum(qv);
-      float dendt = 0.0f;
-      for (int k = 0; k < CH_NW; ++k) dendt += pb[(PB_DEND * 8 + k) * 64];
-      dendt *= expf(cs.end);
-      // reduce the fused rows over the rank m: step l collects rows l*M .. l*M+M-1
-      float dcl = 0.0f, dvxl = 0.0f;
-      for (int m = 0; m < M; ++m) {
-        const int src = (lane * M + m) & 63;
-        const float v1 = __shfl(dc, src, 64), v2 = __shfl(dvx, src, 64);
-        if (lane < L) {
-          dcl += v1;
-          dvxl += v2;
-        }
-      }
-      if (lane == Lc - 1) dcl += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
-      const float dda = wave_incl_suffix(lane < Lc ? dcl : 0.0f, lane);
-      if (lane < Lc) {
-        const i64 o = (bi * a.T + t0 + lane) * a.H + h;
-        a.d_dtda[o] = a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
-      }
+    // ---- d_cumA assembly: this head now (float32) or one head later (bf16) ----
+    if (!BF) {
+      __syncthreads();  // partial row sums complete
+      if (w == 0) epilogue(h, cs, Ah, pbase);
+    } else {
+      prev_h = h;
+      prev_cs = cs;
+      prev_Ah = Ah;
     }
+  }
+  if (BF && a.hph > 0) {
+    __syncthreads();
+    if (w == (int)((a.hph - 1) % CH_NW)) epilogue(prev_h, prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_N * 8 * 64);
   }
 
   // ---- K2 backward on the head-summed d_cb: dC_k2 = d_cb . B, dB_k2 = d_cb^T . C ----
@@ -623,15 +655,15 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         mma(accB, cvt_rowk<T>(CBs, LDC, 16 * kb, 16 * rb, lane), ld_rowk(Cs, LDN, 16 * kb, 16 * nt_own, lane));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rb + 4 * q + j, l = r / M, m = r % M, n = 16 * nt_own + r16;
+        const int r = 16 * rb + 4 * q + j, l = r / M, n = 16 * nt_own + r16;
         if (l >= Lc) continue;
-        const i64 o = ix_bc(a, bi, t0 + l, m, g, n);
+        const int o = r * brs + n;  // offset from boff0
         if (a.hsplit == 1) {
-          st((T*)a.dB, o, accB[j]);
-          st((T*)a.dC, o, accC[j]);
+          st((T*)a.dB + boff0, o, accB[j]);
+          st((T*)a.dC + boff0, o, accC[j]);
         } else {
-          a.part[hs * stride + o] = accB[j];
-          a.part[(a.hsplit + hs) * stride + o] = accC[j];
+          a.part[hs * stride + boff0 + o] = accB[j];
+          a.part[(a.hsplit + hs) * stride + boff0 + o] = accC[j];
         }
       }
     }
@@ -673,7 +705,7 @@ static i64 pick_hsplit(const ssmvjp_ssd_desc& d, i64 nc) {
 static size_t grads_lds_bytes(const ssmvjp_ssd_desc& d) {
   const bool bf = d.dtype == SSMVJP_BF16;
   const size_t e = bf ? 2 : 4, pad = bf ? 8 : 0, LM = (size_t)(d.chunk_len * d.mimo_rank);
-  return 4 * (LM * (LM + 4) + PB_N * 8 * 64) +
+  return 4 * (LM * (LM + 4) + (bf ? 2 : 1) * PB_N * 8 * 64) +
          e * (2 * LM * (d.dstate + pad) + 2 * LM * (d.headdim + pad) + (bf ? 2 : 1) * (size_t)(d.headdim * d.dstate));
 }
 
@@ -682,6 +714,7 @@ bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
   const i64 LM = d.chunk_len * d.mimo_rank;
   if (LM % 16 || LM > MAXRB * 16) return false;
   if (grads_lds_bytes(d) > 160 * 1024) return false;
+  if (LM * d.nheads * d.headdim >= (1ll << 31) || LM * d.ngroups * d.dstate >= (1ll << 31)) return false;
   return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_MAXT * 4;
 }
 
@@ -731,7 +764,7 @@ template <typename T>
 static size_t grads_lds(const SsdArgs& a) {
   const bool bf = sizeof(T) == 2;
   const int PAD = bf ? 8 : 0;
-  return sizeof(float) * ((size_t)a.LM * (a.LM + 4) + PB_N * 8 * 64) +
+  return sizeof(float) * ((size_t)a.LM * (a.LM + 4) + (bf ? 2 : 1) * PB_N * 8 * 64) +
          sizeof(T) * (2 * (size_t)a.LM * (a.N + PAD) + 2 * (size_t)a.LM * (a.P + PAD) + (bf ? 2 : 1) * (size_t)a.P * a.N);
 }
 
