@@ -484,22 +484,29 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     if (BF && hh > 0 && w == (int)((hh - 1) % CH_NW))
       epilogue(prev_h, prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
 
-    // ---- BLUE: dC_blue = (dy * exp(cumA)) . S_c ; d_cumA_blue = rowsum(C * dC_blue) ----
-    // ---- K3:   dB_k3 += (exp(end - cumA) v) . dS_{c+1} ;  d_end = sum S_c * dS_{c+1} ----
+    // The [L x N] and [L x P] products are computed transposed (rows n or p,
+    // columns the chunk's rows r = l*M + m), so per-row factors are per-lane
+    // constants, reductions over n or p are in-lane plus sum4q, and results
+    // leave as 4 consecutive n or p per lane (vector stores).
+
+    // ---- BLUE: dC_blue^T = S_c^T . (dy * exp(cumA))^T ; d_cumA_blue = colsum(C^T * dC_blue^T) ----
+    // ---- K3:   dB_k3^T  += dS_{c+1}^T . (exp(end - cumA) v)^T ;  d_end = sum S_c * dS_{c+1} ----
     float dend = 0.0f;
     if (nt_own < NT) {
-      float xscale[MAXRB];
+      const T* Scur = BF ? (const T*)Ss : (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+      float ecol[MAXRB], xcol[MAXRB];
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
-        const int l = (16 * rb + r16) / M;  // row of this lane's A fragment
-        xscale[rb] = delta_of(l) * exp_hw(cs.end - cum_of(l));
+        const int l = (16 * rb + r16) / M;  // this lane's column r
+        const float cl = cum_of(l);
+        ecol[rb] = exp_hw(cl);
+        xcol[rb] = delta_of(l) * exp_hw(cs.end - cl);
       }
-      f32x4 acc1[MAXRB];
+      f32x4 acc1[MAXRB], acc2[MAXRB];
 #pragma unroll
-      for (int rb = 0; rb < MAXRB; ++rb) acc1[rb] = zero4();
-      const T* Scur = BF ? (const T*)Ss : (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+      for (int rb = 0; rb < MAXRB; ++rb) acc1[rb] = acc2[rb] = zero4();
       for (int kb = 0; kb < PT; ++kb) {
-        const Frag<T> fS = ld_ntv(Scur + tile_off(kb, nt_own), lane);
+        const Frag<T> fS = ld_ntv(Scur + tile_off(kb, nt_own), lane);    // A: rows n, k = p
         const Frag<T> fdS = ld_ntv(dSs + tile_off(kb, nt_own), lane);
         float vS[4], vdS[4];
         frag_get(fS, vS);
@@ -509,39 +516,37 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int rb = 0; rb < MAXRB; ++rb) {
           if (rb >= RB) break;
-          mma(acc1[rb], ld_colk(dys, LDP, 16 * rb, 16 * kb, lane), fS);
-          float vx[4];
-          frag_get(ld_colk(xs, LDP, 16 * rb, 16 * kb, lane), vx);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vx[j] *= xscale[rb];
-          mma(dBacc[rb], frag_make<T>(vx), fdS);
+          mma(acc1[rb], fS, ld_colk(dys, LDP, 16 * rb, 16 * kb, lane));  // B: k = p, columns r
+          mma(acc2[rb], fdS, ld_colk(xs, LDP, 16 * rb, 16 * kb, lane));
         }
       }
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
         if (rb >= RB) break;
+        const int r = 16 * rb + r16;
+        float cv[4];
+        frag_get(ld_colk(Cs, LDN, 16 * rb, 16 * nt_own, lane), cv);  // C[r][n .. n+3], n = 16 nt + 4q
+        float bsum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = 16 * rb + 4 * q + j;
-          const float val = acc1[rb][j] * exp_hw(cum_of(r / M));
+          const float val = acc1[rb][j] * ecol[rb];
           dCacc[rb][j] += val;
-          const float s = sum16((float)Cs[r * LDN + 16 * nt_own + r16] * val);
-          if (r16 == 0) pb[(PB_BLUE * 8 + nt_own) * 64 + r] = s;
+          bsum += cv[j] * val;
+          dBacc[rb][j] += acc2[rb][j] * xcol[rb];
         }
+        bsum = sum4q(bsum);
+        if (q == 0) pb[(PB_BLUE * 8 + nt_own) * 64 + r] = bsum;
       }
     }
 
     // ---- ORANGE: G1 = dy . x^T on lower-triangular tile pairs; d_cb, row/col sums ----
     {
-      float orow[MAXRB][4], ocol[MAXRB];
-#pragma unroll
-      for (int rb = 0; rb < MAXRB; ++rb) {
-        ocol[rb] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) orow[rb][j] = 0.0f;
-      }
+      float orow[MAXG2][4], ocol[MAXG2];
 #pragma unroll
       for (int k = 0; k < MAXG2; ++k) {
+        ocol[k] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) orow[k][j] = 0.0f;
         const int rt = pair_rt[k], rs_ = pair_rs[k];
         if (rt < 0) continue;
         f32x4 acc = zero4();
@@ -557,36 +562,52 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
           const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
           dcbacc[k][j] += dcb;
           const float dd = dcb * CBs[t * LDC + s_];
-#pragma unroll
-          for (int rb = 0; rb < MAXRB; ++rb) {
-            if (rb == rt) orow[rb][j] += dd;
-            if (rb == rs_) ocol[rb] += dd;
-          }
+          orow[k][j] += dd;
+          ocol[k] += dd;
         }
       }
+      // this wave's slots: row sums for its items' row blocks, column sums for
+      // its items' column blocks, zero elsewhere
 #pragma unroll
       for (int rb = 0; rb < MAXRB; ++rb) {
         if (rb >= RB) break;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum = 0.0f;
+        bool rtouch = false, ctouch = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = sum16(orow[rb][j]);
-          if (r16 == 0) pb[(PB_OROW * 8 + w) * 64 + 16 * rb + 4 * q + j] = s;
+        for (int k = 0; k < MAXG2; ++k) {
+          if (pair_rt[k] == rb) {
+            rtouch = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rsum[j] += orow[k][j];
+          }
+          if (pair_rs[k] == rb) {
+            ctouch = true;
+            csum += ocol[k];
+          }
         }
-        const float s2 = sum4q(ocol[rb]);
-        if (q == 0) pb[(PB_OCOL * 8 + w) * 64 + 16 * rb + r16] = s2;
+        if (rtouch) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rsum[j] = sum16(rsum[j]);
+        }
+        if (r16 == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pb[(PB_OROW * 8 + w) * 64 + 16 * rb + 4 * q + j] = rsum[j];
+        }
+        if (ctouch) csum = sum4q(csum);
+        if (q == 0) pb[(PB_OCOL * 8 + w) * 64 + 16 * rb + r16] = csum;
       }
     }
 
-    // ---- K3: d_dv = B . dS^T ; ORANGE: d_v_or = (CB * decay)^T . dy ; dx ----
+    // ---- K3: d_dv^T = dS_{c+1} . B^T ; ORANGE: d_v_or^T = dy^T . (CB * decay) ; dx ----
 #pragma unroll
     for (int k2 = 0; k2 < MAXI2; ++k2) {
       const int it = w + CH_NW * k2;
       if (it >= PT * RB) continue;
       const int pt = it / RB, rb = it % RB;
       f32x4 acc3 = zero4(), acc5 = zero4();
-      for (int kb = 0; kb < NT; ++kb)
-        mma(acc3, ld_colk(Bs, LDN, 16 * rb, 16 * kb, lane), ld_ntv_t(dSs + tile_off(pt, kb), lane));
-      const int s_ = 16 * rb + r16, ls = s_ / M;
+      for (int kb = 0; kb < NT; ++kb)  // A: rows p, k = n (transposed native read); B: k = n, columns r
+        mma(acc3, ld_ntv_t(dSs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * rb, 16 * kb, lane));
+      const int s_ = 16 * rb + r16, ls = s_ / M;  // this lane's column
       const float cs_s = cum_of(ls);
       for (int kb = rb; kb < RB; ++kb) {
         float fw[4];
@@ -596,22 +617,28 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
           const float ct = cum_of(lt);  // every lane takes part in the shuffle
           fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * exp_hw(ct - cs_s) : 0.0f;
         }
-        mma(acc5, frag_make<T>(fw), ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane));
+        // A: rows p, k = t (transpose read of dy rows); B: k = t, columns s
+        mma(acc5, ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane), frag_make<T>(fw));
       }
+      const int r = s_, l = ls;
+      const float dl = delta_of(l);
+      const float edec = exp_hw(cs.end - cs_s);
+      float xv[4];
+      frag_get(ld_colk(xs, LDP, 16 * rb, 16 * pt, lane), xv);  // x[r][p .. p+3], p = 16 pt + 4q
+      float dvo[4], s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rb + 4 * q + j, l = r / M, p = 16 * pt + r16;
-        const float dl = delta_of(l);
-        const float edec = exp_hw(cs.end - cum_of(l));
-        const float xval = (float)xs[r * LDP + p];
         const float dv = acc3[j] * edec + acc5[j];  // d_v = d_v_k3 + d_v_orange
-        if (l < Lc) st(dxg, r * xrs + (int)h * P + p, a.raw ? dv : dv * dl);
-        const float s1 = sum16(acc3[j] * dl * xval);  // d_decay = sum_p d_decayed_v . v
-        const float s2 = sum16(dv * xval);
-        if (r16 == 0) {
-          pb[(PB_DEC * 8 + pt) * 64 + r] = s1;
-          pb[(PB_DVX * 8 + pt) * 64 + r] = s2;
-        }
+        dvo[j] = a.raw ? dv : dv * dl;
+        s1 += acc3[j] * xv[j];                      // d_decay / delta = sum_p d_decayed_v . x
+        s2 += dv * xv[j];
+      }
+      if (l < Lc) store4(dxg + r * xrs + (int)h * P + 16 * pt + 4 * q, f32x4{dvo[0], dvo[1], dvo[2], dvo[3]});
+      s1 = sum4q(s1) * dl;
+      s2 = sum4q(s2);
+      if (q == 0) {
+        pb[(PB_DEC * 8 + pt) * 64 + r] = s1;
+        pb[(PB_DVX * 8 + pt) * 64 + r] = s2;
       }
     }
     dend = wave_sum(dend);
@@ -648,23 +675,21 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int rb = 0; rb < MAXRB; ++rb) {
       if (rb >= RB) break;
+      // transposed: rows n, columns r
       f32x4 accC = dCacc[rb], accB = dBacc[rb];
-      for (int kb = 0; kb <= rb; ++kb)
-        mma(accC, cvt_colk<T>(CBs, LDC, 16 * rb, 16 * kb, lane), ld_rowk(Bs, LDN, 16 * kb, 16 * nt_own, lane));
-      for (int kb = rb; kb < RB; ++kb)
-        mma(accB, cvt_rowk<T>(CBs, LDC, 16 * kb, 16 * rb, lane), ld_rowk(Cs, LDN, 16 * kb, 16 * nt_own, lane));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * rb + 4 * q + j, l = r / M, n = 16 * nt_own + r16;
-        if (l >= Lc) continue;
-        const int o = r * brs + n;  // offset from boff0
-        if (a.hsplit == 1) {
-          st((T*)a.dB + boff0, o, accB[j]);
-          st((T*)a.dC + boff0, o, accC[j]);
-        } else {
-          a.part[hs * stride + boff0 + o] = accB[j];
-          a.part[(a.hsplit + hs) * stride + boff0 + o] = accC[j];
-        }
+      for (int kb = 0; kb <= rb; ++kb)  // dC_k2^T = B^T . d_cb^T
+        mma(accC, ld_rowk(Bs, LDN, 16 * kb, 16 * nt_own, lane), cvt_colk<T>(CBs, LDC, 16 * rb, 16 * kb, lane));
+      for (int kb = rb; kb < RB; ++kb)  // dB_k2^T = C^T . d_cb
+        mma(accB, ld_rowk(Cs, LDN, 16 * kb, 16 * nt_own, lane), cvt_rowk<T>(CBs, LDC, 16 * kb, 16 * rb, lane));
+      const int r = 16 * rb + r16, l = r / M;
+      if (l >= Lc) continue;
+      const int o = r * brs + 16 * nt_own + 4 * q;  // dB[r][n .. n+3], offset from boff0
+      if (a.hsplit == 1) {
+        store4((T*)a.dB + boff0 + o, accB);
+        store4((T*)a.dC + boff0 + o, accC);
+      } else {
+        store4(a.part + hs * stride + boff0 + o, accB);
+        store4(a.part + (a.hsplit + hs) * stride + boff0 + o, accC);
       }
     }
   }
