@@ -307,6 +307,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   T* dys = xs + LM * LDP;                        // [LM][LDP]
   T* dSs = dys + LM * LDP;                       // [P*N] dS_{c+1}, native tiles
   T* Ss = dSs + P * N;                           // [P*N] S_c, native tiles (bf16 only)
+  T* Wt = Ss + P * N;                            // [10][256] masked CB * decay per (t, s) tile pair (bf16 only)
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
@@ -484,6 +485,70 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     if (BF && hh > 0 && w == (int)((hh - 1) % CH_NW))
       epilogue(prev_h, prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
 
+    // ---- ORANGE: G1 = dy . x^T on lower-triangular tile pairs; d_cb, row/col sums ----
+    {
+      float orow[MAXG2][4], ocol[MAXG2];
+#pragma unroll
+      for (int k = 0; k < MAXG2; ++k) {
+        ocol[k] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) orow[k][j] = 0.0f;
+        const int rt = pair_rt[k], rs_ = pair_rs[k];
+        if (rt < 0) continue;
+        f32x4 acc = zero4();
+        float wv[4];
+        for (int kb = 0; kb < PT; ++kb)
+          mma(acc, ld_colk(dys, LDP, 16 * rt, 16 * kb, lane), ld_colk(xs, LDP, 16 * rs_, 16 * kb, lane));
+        const int s_ = 16 * rs_ + r16, ls = s_ / M;
+        const float cs_s = cum_of(ls), dls = delta_of(ls);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * rt + 4 * q + j, lt = t / M;
+          const float ct = cum_of(lt);  // every lane takes part in the shuffle
+          const float dec = (ls <= lt && lt < Lc) ? exp_hw(ct - cs_s) : 0.0f;
+          const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
+          dcbacc[k][j] += dcb;
+          const float cb = CBs[t * LDC + s_];
+          const float dd = dcb * cb;
+          orow[k][j] += dd;
+          ocol[k] += dd;
+          wv[j] = cb * dec;  // w = CB * decay at (t, s): the d_v_orange operand
+        }
+        // w in native tile order is the B operand (k = t, columns s) of d_v_or^T
+        if (BF) store4(Wt + (rt * (rt + 1) / 2 + rs_) * 256 + 4 * lane, f32x4{wv[0], wv[1], wv[2], wv[3]});
+      }
+      // this wave's slots: row sums for its items' row blocks, column sums for
+      // its items' column blocks, zero elsewhere
+#pragma unroll
+      for (int rb = 0; rb < MAXRB; ++rb) {
+        if (rb >= RB) break;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum = 0.0f;
+        bool rtouch = false, ctouch = false;
+#pragma unroll
+        for (int k = 0; k < MAXG2; ++k) {
+          if (pair_rt[k] == rb) {
+            rtouch = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rsum[j] += orow[k][j];
+          }
+          if (pair_rs[k] == rb) {
+            ctouch = true;
+            csum += ocol[k];
+          }
+        }
+        if (rtouch) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rsum[j] = sum16(rsum[j]);
+        }
+        if (r16 == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pb[(PB_OROW * 8 + w) * 64 + 16 * rb + 4 * q + j] = rsum[j];
+        }
+        if (ctouch) csum = sum4q(csum);
+        if (q == 0) pb[(PB_OCOL * 8 + w) * 64 + 16 * rb + r16] = csum;
+      }
+    }
+
     // The [L x N] and [L x P] products are computed transposed (rows n or p,
     // columns the chunk's rows r = l*M + m), so per-row factors are per-lane
     // constants, reductions over n or p are in-lane plus sum4q, and results
@@ -539,64 +604,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
       }
     }
 
-    // ---- ORANGE: G1 = dy . x^T on lower-triangular tile pairs; d_cb, row/col sums ----
-    {
-      float orow[MAXG2][4], ocol[MAXG2];
-#pragma unroll
-      for (int k = 0; k < MAXG2; ++k) {
-        ocol[k] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) orow[k][j] = 0.0f;
-        const int rt = pair_rt[k], rs_ = pair_rs[k];
-        if (rt < 0) continue;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < PT; ++kb)
-          mma(acc, ld_colk(dys, LDP, 16 * rt, 16 * kb, lane), ld_colk(xs, LDP, 16 * rs_, 16 * kb, lane));
-        const int s_ = 16 * rs_ + r16, ls = s_ / M;
-        const float cs_s = cum_of(ls), dls = delta_of(ls);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * rt + 4 * q + j, lt = t / M;
-          const float ct = cum_of(lt);  // every lane takes part in the shuffle
-          const float dec = (ls <= lt && lt < Lc) ? exp_hw(ct - cs_s) : 0.0f;
-          const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
-          dcbacc[k][j] += dcb;
-          const float dd = dcb * CBs[t * LDC + s_];
-          orow[k][j] += dd;
-          ocol[k] += dd;
-        }
-      }
-      // this wave's slots: row sums for its items' row blocks, column sums for
-      // its items' column blocks, zero elsewhere
-#pragma unroll
-      for (int rb = 0; rb < MAXRB; ++rb) {
-        if (rb >= RB) break;
-        float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum = 0.0f;
-        bool rtouch = false, ctouch = false;
-#pragma unroll
-        for (int k = 0; k < MAXG2; ++k) {
-          if (pair_rt[k] == rb) {
-            rtouch = true;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) rsum[j] += orow[k][j];
-          }
-          if (pair_rs[k] == rb) {
-            ctouch = true;
-            csum += ocol[k];
-          }
-        }
-        if (rtouch) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) rsum[j] = sum16(rsum[j]);
-        }
-        if (r16 == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pb[(PB_OROW * 8 + w) * 64 + 16 * rb + 4 * q + j] = rsum[j];
-        }
-        if (ctouch) csum = sum4q(csum);
-        if (q == 0) pb[(PB_OCOL * 8 + w) * 64 + 16 * rb + r16] = csum;
-      }
-    }
+    if (BF) __syncthreads();  // w tiles complete
 
     // ---- K3: d_dv^T = dS_{c+1} . B^T ; ORANGE: d_v_or^T = dy^T . (CB * decay) ; dx ----
 #pragma unroll
@@ -609,16 +617,19 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         mma(acc3, ld_ntv_t(dSs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * rb, 16 * kb, lane));
       const int s_ = 16 * rb + r16, ls = s_ / M;  // this lane's column
       const float cs_s = cum_of(ls);
-      for (int kb = rb; kb < RB; ++kb) {
-        float fw[4];
+      for (int kb = rb; kb < RB; ++kb) {  // A: rows p, k = t (transpose read of dy rows); B: k = t, columns s
+        if constexpr (BF) {
+          mma(acc5, ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane), ld_ntv(Wt + (kb * (kb + 1) / 2 + rb) * 256, lane));
+        } else {  // float32: no LDS room for the shared w tiles; recompute them
+          float fw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * kb + 4 * q + j, lt = t / M;
-          const float ct = cum_of(lt);  // every lane takes part in the shuffle
-          fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * exp_hw(ct - cs_s) : 0.0f;
+          for (int j = 0; j < 4; ++j) {
+            const int t = 16 * kb + 4 * q + j, lt = t / M;
+            const float ct = cum_of(lt);  // every lane takes part in the shuffle
+            fw[j] = (ls <= lt && lt < Lc) ? CBs[t * LDC + s_] * exp_hw(ct - cs_s) : 0.0f;
+          }
+          mma(acc5, ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane), frag_make<T>(fw));
         }
-        // A: rows p, k = t (transpose read of dy rows); B: k = t, columns s
-        mma(acc5, ld_rowk(dys, LDP, 16 * kb, 16 * pt, lane), frag_make<T>(fw));
       }
       const int r = s_, l = ls;
       const float dl = delta_of(l);
@@ -713,7 +724,7 @@ __global__ void ssd_head_sum_kernel(const float* __restrict__ part, i64 n, i64 h
 // host side
 // ===========================================================================
 static int scan_nb(const ssmvjp_ssd_desc& d) {
-  // n-block per scan workgroup: at most SCAN_MAXT * 4 state tiles per workgroup
+  // n block per scan workgroup: at most SCAN_MAXT * 4 state tiles per workgroup
   i64 nb = d.dstate;
   while ((d.headdim / 16) * (nb / 16) > SCAN_MAXT * 4 && nb % 32 == 0) nb /= 2;
   return (int)nb;
@@ -731,7 +742,8 @@ static size_t grads_lds_bytes(const ssmvjp_ssd_desc& d) {
   const bool bf = d.dtype == SSMVJP_BF16;
   const size_t e = bf ? 2 : 4, pad = bf ? 8 : 0, LM = (size_t)(d.chunk_len * d.mimo_rank);
   return 4 * (LM * (LM + 4) + (bf ? 2 : 1) * PB_N * 8 * 64) +
-         e * (2 * LM * (d.dstate + pad) + 2 * LM * (d.headdim + pad) + (bf ? 2 : 1) * (size_t)(d.headdim * d.dstate));
+         e * (2 * LM * (d.dstate + pad) + 2 * LM * (d.headdim + pad) + (bf ? 2 : 1) * (size_t)(d.headdim * d.dstate) +
+              (bf ? 10 * 256 : 0));
 }
 
 bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
@@ -790,7 +802,8 @@ static size_t grads_lds(const SsdArgs& a) {
   const bool bf = sizeof(T) == 2;
   const int PAD = bf ? 8 : 0;
   return sizeof(float) * ((size_t)a.LM * (a.LM + 4) + (bf ? 2 : 1) * PB_N * 8 * 64) +
-         sizeof(T) * (2 * (size_t)a.LM * (a.N + PAD) + 2 * (size_t)a.LM * (a.P + PAD) + (bf ? 2 : 1) * (size_t)a.P * a.N);
+         sizeof(T) * (2 * (size_t)a.LM * (a.N + PAD) + 2 * (size_t)a.LM * (a.P + PAD) + (bf ? 2 : 1) * (size_t)a.P * a.N +
+                      (bf ? 10 * 256 : 0));
 }
 
 // the Mamba-2 chunked workload shape gets compile-time sizes
