@@ -59,24 +59,30 @@ __device__ __forceinline__ float wave_sum(float v) { return sum4q(sum16(v)); }
 // exp(x) through the hardware exp2 (v_exp_f32, relative error a few 1e-8)
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// inclusive prefix sum over the 64 lanes (Hillis-Steele, fixed order)
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+// inclusive prefix sum over the 64 lanes, all in DPP: Hillis-Steele inside
+// each 16-lane row (row_shr 1, 2, 4, 8 with zero fill), then the row totals
+// carried across rows with row_bcast:15 (rows 1 and 3) and row_bcast:31
+// (rows 2 and 3).  Fixed order, no LDS traffic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+__device__ __forceinline__ float wave_incl_scan(float v, int /*lane*/) {
+  v += dpp_zero<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_zero<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_zero<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_zero<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
-// inclusive suffix sum over the 64 lanes: lane l gets sum_{k >= l} v_k
+// inclusive suffix sum over the 64 lanes: lane l gets sum_{k >= l} v_k,
+// formed as total - (inclusive prefix - v) (the K1 backward's own form).
 __device__ __forceinline__ float wave_incl_suffix(float v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float o = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += o;
-  }
-  return v;
+  const float incl = wave_incl_scan(v, lane);
+  const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+  return total - (incl - v);
 }
 
 // ---------------------------------------------------------------------------

@@ -135,14 +135,22 @@ __device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z,
 // ===========================================================================
 // kernel 1: forward and reverse state scans over chunks
 // ===========================================================================
-constexpr int SCAN_NTH = 256;
-constexpr int SCAN_MAXT = 8;  // state tiles per wave
+constexpr int SCAN_NW = 8;                   // waves per workgroup
+constexpr int SCAN_NTH = 64 * SCAN_NW;
+constexpr int SCAN_TILES = 32;               // state tiles per workgroup (at most)
+constexpr int SCAN_MAXT = SCAN_TILES / SCAN_NW;  // state tiles per wave
 
 // Shape parameters CP, CNB (n block), CL, CM: a non-zero value fixes P, the n
 // block, the chunk length or the rank at compile time (the workload shape gets
 // its own instantiation); zero reads it from the arguments.
+//
+// Pipeline: the operand rows of chunk c+2 are in flight in registers while
+// chunk c is staged into one of two LDS buffers and chunk c+1's registers wait;
+// with two LDS buffers a single barrier per chunk separates the staging of a
+// buffer from its fragment reads (the reads of that buffer two chunks back
+// ended before the previous chunk's barrier).
 template <typename T, int CP, int CNB, int CL, int CM>
-__global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_arg) {
+__global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int nb_arg) {
   constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr bool FIXED = CP && CNB && CL && CM;
   constexpr int MAXC_O = FIXED ? (CL * CM * CP / E16 + SCAN_NTH - 1) / SCAN_NTH : 64 * 128 / E16 / SCAN_NTH;
@@ -154,8 +162,8 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_a
   const int NB = CNB ? CNB : nb_arg, LM = L * M;
   const int PT = P / 16, NTB = NB / 16, RB = LM / 16;
   const int PPO = P + PAD, PPB = NB + PAD;  // row pitches (elements) of the staged tiles
-  T* opS = (T*)smem_raw;                    // [LM][PPO]  v or dy rows, scaled per step
-  T* bcS = opS + LM * PPO;                  // [LM][PPB]  B or C rows (this n block)
+  const int BUF = LM * (PPO + PPB);         // elements per LDS buffer
+  // buffer k: [LM][PPO] v or dy rows scaled per step, then [LM][PPB] B or C rows (this n block)
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
@@ -172,11 +180,11 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_a
   T* out = (T*)(dir == 0 ? a.S : a.dS);
   const float* init = dir == 0 ? a.s0 : a.dsf;
 
-  const int ntiles = PT * NTB;  // tiles of this wave: ti = pt * NTB + nt, ti % 4 == w
+  const int ntiles = PT * NTB;  // tiles of this wave: ti = pt * NTB + nt, ti % SCAN_NW == w
   f32x4 st[SCAN_MAXT];
 #pragma unroll
   for (int k = 0; k < SCAN_MAXT; ++k) {
-    const int ti = w + 4 * k;
+    const int ti = w + SCAN_NW * k;
     st[k] = zero4();
     if (ti < ntiles && init) {
       const int pt = ti / NTB, nt = ti % NTB;
@@ -187,51 +195,55 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_a
   }
 
   // register prefetch of one chunk: operand rows, B/C rows, the step values
+  struct Pre {
+    u32x4 o[MAXC], b[MAXC];
+    float z;
+  };
   const int oc_row = P / E16, bc_row = NB / E16;
-  u32x4 ro[MAXC], rb[MAXC];
-  float rz = 0.0f;
-  auto issue = [&](i64 c) {
+  auto chunk_of = [&](i64 step) { return dir == 0 ? step : a.nc - 1 - step; };
+  auto issue = [&](Pre& pr, i64 c) {
     const i64 t0 = c * L;
     const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
-      ro[it] = zero_u4();
-      rb[it] = zero_u4();
+      pr.o[it] = zero_u4();
+      pr.b[it] = zero_u4();
       if (idx < LM * oc_row) {
         const int r = idx / oc_row, col = (idx % oc_row) * E16, l = r / M, m = r % M;
-        if (l < Lc) ro[it] = load16(op + ix_xv(a, bi, t0 + l, m, h, col));
+        if (l < Lc) pr.o[it] = load16(op + ix_xv(a, bi, t0 + l, m, h, col));
       }
       if (idx < LM * bc_row) {
         const int r = idx / bc_row, col = (idx % bc_row) * E16, l = r / M, m = r % M;
-        if (l < Lc) rb[it] = load16(bc + ix_bc(a, bi, t0 + l, m, g, n0 + col));
+        if (l < Lc) pr.b[it] = load16(bc + ix_bc(a, bi, t0 + l, m, g, n0 + col));
       }
     }
-    rz = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
+    pr.z = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
   };
-
-  if (a.nc > 0) issue(dir == 0 ? 0 : a.nc - 1);  // T = 0 has no chunk to prefetch
-  for (i64 step = 0; step < a.nc; ++step) {
-    const i64 c = dir == 0 ? step : a.nc - 1 - step;
+  // one chunk: step scalars, staging into LDS buffer sb, refill of pr with
+  // chunk step + 2, one barrier, then the state tiles
+  auto process = [&](Pre& pr, i64 step, T* sb) {
+    const i64 c = chunk_of(step);
     const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
-    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
+    const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, h, lane);
     const float sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
     const float e_end = exp_hw(cs.end);
-    __syncthreads();  // the previous chunk's fragment reads are done
+    T* opS = sb;
+    T* bcS = sb + LM * PPO;
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
       const int r = idx / oc_row;
       const float s_r = __shfl(sc, (r / M) & 63, 64);
-      if (idx < LM * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(ro[it], s_r, (const T*)0);
-      if (idx < LM * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = rb[it];
+      if (idx < LM * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(pr.o[it], s_r, (const T*)0);
+      if (idx < LM * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = pr.b[it];
     }
-    if (step + 1 < a.nc) issue(dir == 0 ? c + 1 : c - 1);
+    if (step + 2 < a.nc) issue(pr, chunk_of(step + 2));
     __syncthreads();
     T* outc = out + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
 #pragma unroll
     for (int k = 0; k < SCAN_MAXT; ++k) {
-      const int ti = w + 4 * k;
+      const int ti = w + SCAN_NW * k;
       if (ti >= ntiles) continue;
       const int pt = ti / NTB, nt = ti % NTB;
       store4(outc + native_off(N, pt, n0 / 16 + nt, lane, 0), st[k]);
@@ -241,11 +253,21 @@ __global__ void __launch_bounds__(256) ssd_state_scan_kernel(SsdArgs a, int nb_a
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[k][j] = e_end * st[k][j] + acc[j];
     }
+  };
+
+  T* sb0 = (T*)smem_raw;
+  T* sb1 = sb0 + BUF;
+  Pre p0, p1;
+  if (a.nc > 0) issue(p0, chunk_of(0));  // T = 0 has no chunk to prefetch
+  if (a.nc > 1) issue(p1, chunk_of(1));
+  for (i64 step = 0; step < a.nc; step += 2) {
+    process(p0, step, sb0);
+    if (step + 1 < a.nc) process(p1, step + 1, sb1);
   }
   if (dir == 1) {
 #pragma unroll
     for (int k = 0; k < SCAN_MAXT; ++k) {
-      const int ti = w + 4 * k;
+      const int ti = w + SCAN_NW * k;
       if (ti >= ntiles) continue;
       const int pt = ti / NTB, nt = ti % NTB;
 #pragma unroll
@@ -724,9 +746,9 @@ __global__ void ssd_head_sum_kernel(const float* __restrict__ part, i64 n, i64 h
 // host side
 // ===========================================================================
 static int scan_nb(const ssmvjp_ssd_desc& d) {
-  // n block per scan workgroup: at most SCAN_MAXT * 4 state tiles per workgroup
+  // n block per scan workgroup: at most SCAN_TILES state tiles per workgroup
   i64 nb = d.dstate;
-  while ((d.headdim / 16) * (nb / 16) > SCAN_MAXT * 4 && nb % 32 == 0) nb /= 2;
+  while ((d.headdim / 16) * (nb / 16) > SCAN_TILES && nb % 32 == 0) nb /= 2;
   return (int)nb;
 }
 
@@ -752,7 +774,7 @@ bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
   if (LM % 16 || LM > MAXRB * 16) return false;
   if (grads_lds_bytes(d) > 160 * 1024) return false;
   if (LM * d.nheads * d.headdim >= (1ll << 31) || LM * d.ngroups * d.dstate >= (1ll << 31)) return false;
-  return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_MAXT * 4;
+  return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_TILES;
 }
 
 SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
@@ -794,7 +816,7 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
 template <typename T>
 static size_t states_lds(const SsdArgs& a, int NB) {
   const int PAD = 16 / sizeof(T);
-  return sizeof(T) * (size_t)a.LM * ((a.P + PAD) + (NB + PAD));
+  return 2 * sizeof(T) * (size_t)a.LM * ((a.P + PAD) + (NB + PAD));  // two buffers
 }
 
 template <typename T>
