@@ -23,6 +23,31 @@ __device__ __forceinline__ void st(float* p, i64 i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(bf16* p, i64 i, float v) { p[i] = (bf16)v; }
 
 // ---------------------------------------------------------------------------
+// Range-checked global loads through a raw buffer resource.  A load whose
+// 32-bit byte offset (plus its size) lies past the resource size returns zeros
+// (the hardware range check), so rows past the end of a sequence need neither a
+// branch nor a lane mask, and the loads issue on straight-line code, where the
+// compiler can count outstanding loads exactly instead of draining them.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t brsrc;
+constexpr unsigned BUF_OOB = 0x80000000u;  // past the size of every resource made here (< 2^31 bytes)
+__device__ __forceinline__ brsrc make_rsrc(const void* base, unsigned bytes) {
+  // dword 3: 32-bit data format, the raw (untyped) form of the gfx9 resource
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(brsrc r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float bload_f32(brsrc r, unsigned off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+// stores through a resource: a store past the resource size is dropped
+__device__ __forceinline__ void bstore_f32(brsrc r, unsigned off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // step size: delta = softplus(z) (z > 20 -> z), its derivative sigmoid(z)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float softplus_f(float z) { return z > 20.0f ? z : log1pf(expf(z)); }

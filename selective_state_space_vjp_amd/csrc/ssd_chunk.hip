@@ -81,8 +81,20 @@ __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
   *(bf16x4*)p = u;
 }
 
+// four float results stored as 4 consecutive elements of T through a resource
+// (dropped past the resource size)
+__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const float*) {
+  u32x4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const bf16*) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 u = {(unsigned)(unsigned short)bf16_bits(v[0]) | ((unsigned)(unsigned short)bf16_bits(v[1]) << 16),
+             (unsigned)(unsigned short)bf16_bits(v[2]) | ((unsigned)(unsigned short)bf16_bits(v[3]) << 16)};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
+}
+
 // 16-byte global <-> register chunks for staging (8 bf16 or 4 float)
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 zero_u4() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;
@@ -107,7 +119,7 @@ __device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
 
 // Per-chunk step sizes for one head, one lane per step l < L (lanes >= L and
 // steps past T get zeros, which keeps cumA flat over a short last chunk).
-// z is this lane's dt (Mamba-2) or da (RAW) value.
+// z is this lane's dt (Mamba-2) or da (RAW) value, Ah the head's A (Mamba-2).
 struct ChunkScalars {
   float delta;  // softplus(dt) (Mamba-2) or 1 (RAW)
   float sig;    // sigmoid(dt) (Mamba-2)
@@ -115,7 +127,7 @@ struct ChunkScalars {
   float end;    // cumsum at the last step of the chunk (same in every lane)
 };
 
-__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z, bool valid, i64 h, int lane) {
+__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z, bool valid, float Ah, int lane) {
   ChunkScalars s;
   float da;
   if (a.raw) {
@@ -125,7 +137,7 @@ __device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z,
   } else {
     s.delta = valid ? softplus_f(z) : 0.0f;
     s.sig = sigmoid_f(z);
-    da = s.delta * a.A[h];
+    da = s.delta * Ah;
   }
   s.cum = wave_incl_scan(valid ? da : 0.0f, lane);
   s.end = __shfl(s.cum, 63, 64);
@@ -167,6 +179,7 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
+  __builtin_assume(w >= 0 && w < SCAN_NW);  // lets the tile loop compile without branches
   const int nblk = N / NB;
   i64 bid = blockIdx.x;
   const int nbi = (int)(bid % nblk);
@@ -194,38 +207,40 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
     }
   }
 
-  // register prefetch of one chunk: operand rows, B/C rows, the step values
+  // register prefetch of one chunk: the step values, operand rows, B/C rows.
+  // Branch-free buffer loads: rows past the end of the sequence read zeros.
   struct Pre {
-    u32x4 o[MAXC], b[MAXC];
     float z;
+    u32x4 o[MAXC], b[MAXC];
   };
   const int oc_row = P / E16, bc_row = NB / E16;
+  const unsigned esz = sizeof(T);
+  const float Ah = a.raw ? 0.0f : a.A[h];
   auto chunk_of = [&](i64 step) { return dir == 0 ? step : a.nc - 1 - step; };
   auto issue = [&](Pre& pr, i64 c) {
     const i64 t0 = c * L;
     const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
+    const int rows = Lc * M;  // valid fused rows (>= 1)
+    const brsrc rz = make_rsrc(a.dtda + (bi * a.T + t0) * a.H + h, (unsigned)(((Lc - 1) * a.H + 1) * 4));
+    pr.z = bload_f32(rz, (unsigned)(lane * a.H * 4));
+    const brsrc ro = make_rsrc(op + ix_xv(a, bi, t0, 0, h, 0), (unsigned)(((rows - 1) * a.H * P + P) * esz));
+    const brsrc rb = make_rsrc(bc + ix_bc(a, bi, t0, 0, g, n0), (unsigned)(((rows - 1) * a.G * a.N + NB) * esz));
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
-      pr.o[it] = zero_u4();
-      pr.b[it] = zero_u4();
-      if (idx < LM * oc_row) {
-        const int r = idx / oc_row, col = (idx % oc_row) * E16, l = r / M, m = r % M;
-        if (l < Lc) pr.o[it] = load16(op + ix_xv(a, bi, t0 + l, m, h, col));
-      }
-      if (idx < LM * bc_row) {
-        const int r = idx / bc_row, col = (idx % bc_row) * E16, l = r / M, m = r % M;
-        if (l < Lc) pr.b[it] = load16(bc + ix_bc(a, bi, t0 + l, m, g, n0 + col));
-      }
+      const int r1 = idx / oc_row, c1 = (idx % oc_row) * E16;
+      const int r2 = idx / bc_row, c2 = (idx % bc_row) * E16;
+      pr.o[it] = bload16(ro, idx < LM * oc_row ? (unsigned)((r1 * a.H * P + c1) * esz) : BUF_OOB);
+      pr.b[it] = bload16(rb, idx < LM * bc_row ? (unsigned)((r2 * a.G * a.N + c2) * esz) : BUF_OOB);
     }
-    pr.z = lane < Lc ? a.dtda[(bi * a.T + t0 + lane) * a.H + h] : 0.0f;
   };
   // one chunk: step scalars, staging into LDS buffer sb, refill of pr with
-  // chunk step + 2, one barrier, then the state tiles
+  // chunk step + 2 (clamped to the last step: loads that are never used keep
+  // the issue unconditional), one barrier, then the state tiles
   auto process = [&](Pre& pr, i64 step, T* sb) {
     const i64 c = chunk_of(step);
     const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
-    const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, h, lane);
+    const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, Ah, lane);
     const float sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
     const float e_end = exp_hw(cs.end);
     T* opS = sb;
@@ -238,7 +253,7 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
       if (idx < LM * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(pr.o[it], s_r, (const T*)0);
       if (idx < LM * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = pr.b[it];
     }
-    if (step + 2 < a.nc) issue(pr, chunk_of(step + 2));
+    issue(pr, chunk_of(step + 2 < a.nc ? step + 2 : a.nc - 1));
     __syncthreads();
     T* outc = out + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
 #pragma unroll
@@ -258,11 +273,15 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   T* sb0 = (T*)smem_raw;
   T* sb1 = sb0 + BUF;
   Pre p0, p1;
-  if (a.nc > 0) issue(p0, chunk_of(0));  // T = 0 has no chunk to prefetch
-  if (a.nc > 1) issue(p1, chunk_of(1));
-  for (i64 step = 0; step < a.nc; step += 2) {
-    process(p0, step, sb0);
-    if (step + 1 < a.nc) process(p1, step + 1, sb1);
+  i64 step = 0;
+  if (a.nc > 0) {  // T = 0 has no chunk to prefetch
+    issue(p0, chunk_of(0));
+    issue(p1, chunk_of(a.nc > 1 ? 1 : 0));
+    for (; step + 1 < a.nc; step += 2) {
+      process(p0, step, sb0);
+      process(p1, step + 1, sb1);
+    }
+    if (step < a.nc) process(p0, step, sb0);
   }
   if (dir == 1) {
 #pragma unroll
@@ -333,6 +352,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
+  __builtin_assume(w >= 0 && w < CH_NW);  // lets per-wave item loops compile without branches
   i64 bid = blockIdx.x;
   const i64 hs = bid % a.hsplit;
   bid /= a.hsplit;
@@ -367,35 +387,38 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     *(u32x4*)(Cs + r * LDN + col) = uc;
   }
 
-  // ---- register prefetch of one head: x/v and dy rows, S_c and dS_{c+1}, dt/da ----
+  // ---- register prefetch of one head: dt/da and A, x/v and dy rows, S_c and dS_{c+1} ----
+  // Branch-free buffer loads (rows past the end of the sequence read zeros), so
+  // that the next head's loads stay in flight across this head's work.
   u32x4 rx[MAXX], ry[MAXX], rs[MAXS], rd[MAXS];
-  float rz = 0.0f;
+  float rz = 0.0f, rA = 0.0f;
   const i64 hbase = g * a.hpg + hs * a.hph;
+  const unsigned esz = sizeof(T);
+  const unsigned xbytes = (unsigned)(((i64)(Lc * M - 1) * xrs + P) * esz);  // valid rows of one head
+  const unsigned zbytes = (unsigned)(((Lc - 1) * a.H + 1) * 4);
+  const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));      // RAW: no A, reads zero
   auto issue = [&](i64 h) {
+    rz = bload_f32(make_rsrc(dtg + h, zbytes), (unsigned)(lane * a.H * 4));
+    rA = bload_f32(rsA, (unsigned)(h * 4));
+    const brsrc bx = make_rsrc(xg + (int)h * P, xbytes), by = make_rsrc(dyg + (int)h * P, xbytes);
 #pragma unroll
     for (int it = 0; it < MAXX; ++it) {
       const int idx = tid + it * CH_NTH;
-      rx[it] = ry[it] = zero_u4();
-      if (idx < LM * xrow) {
-        const int r = idx / xrow, col = (idx % xrow) * E16, l = r / M;
-        if (l < Lc) {
-          rx[it] = load16(xg + r * xrs + (int)h * P + col);
-          ry[it] = load16(dyg + r * xrs + (int)h * P + col);
-        }
-      }
+      const int r = idx / xrow, col = (idx % xrow) * E16;
+      const unsigned off = idx < LM * xrow ? (unsigned)(r * xrs + col) * esz : BUF_OOB;
+      rx[it] = bload16(bx, off);
+      ry[it] = bload16(by, off);
     }
     const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
     const T* dSg = (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+    const brsrc bs = make_rsrc(Sg, (unsigned)PN * esz), bd = make_rsrc(dSg, (unsigned)PN * esz);
 #pragma unroll
     for (int it = 0; it < MAXS; ++it) {
       const int idx = tid + it * CH_NTH;
-      rs[it] = rd[it] = zero_u4();
-      if (idx < PN / E16) {
-        if (BF) rs[it] = load16(Sg + idx * E16);
-        rd[it] = load16(dSg + idx * E16);
-      }
+      const unsigned off = idx < PN / E16 ? (unsigned)idx * 16u : BUF_OOB;
+      if (BF) rs[it] = bload16(bs, off);
+      rd[it] = bload16(bd, off);
     }
-    rz = lane < Lc ? dtg[lane * (int)a.H + (int)h] : 0.0f;
   };
   if (BF) issue(hbase);
   __syncthreads();  // B, C staged
@@ -430,8 +453,9 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   for (int k = 0; k < MAXG2; ++k) dcbacc[k] = zero4();
 
   // d_cumA from its four sources, the K1 suffix sum and the chain to d_dt for
-  // one head, from the partial row sums in pb; run by a single wave.
-  auto epilogue = [&](i64 h, const ChunkScalars& cs, float Ah, const float* pb) {
+  // one head, from the partial row sums in pb; run by a single wave, which gets
+  // the d_dt (RAW: d_da) value of step `lane` back.
+  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float {
     auto cum_of = [&](int l) { return __shfl(cs.cum, l, 64); };
     float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
     const float c_row = cum_of((lane / M) & 63);  // every lane takes part in the shuffle
@@ -465,7 +489,13 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     }
     if (lane == Lc - 1) dcl += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
     const float dda = wave_incl_suffix(lane < Lc ? dcl : 0.0f, lane);
-    if (lane < Lc) ddtg[lane * (int)a.H + (int)h] = a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
+    return a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
+  };
+  // every wave stores (dropped unless `on` and lane < Lc): no store sits in a
+  // branch, which keeps the compiler's count of outstanding loads exact
+  const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
+  auto epi_store = [&](bool on, i64 h, float v) {
+    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v);
   };
   i64 prev_h = 0;
   ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
@@ -475,8 +505,9 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     const i64 h = hbase + hh;
     if (!BF) issue(h);
     float* pb = pbase + (BF ? (hh & 1) * PB_N * 8 * 64 : 0);
-    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, h, lane);
-    const float Ah = a.raw ? 0.0f : a.A[h];
+    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, rA, lane);
+    const float Ah = rA;
+    const brsrc bdx = make_rsrc(dxg + (int)h * P, xbytes);
     // lane shuffles: call them where every lane of the wave is active (a
     // shuffle under a divergent mask reads zero from inactive source lanes)
     auto cum_of = [&](int l) { return __shfl(cs.cum, l, 64); };
@@ -500,12 +531,16 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         *(u32x4*)(dSs + idx * E16) = rd[it];
       }
     }
-    if (BF && hh + 1 < a.hph) issue(h + 1);
+    if (BF) issue(hh + 1 < a.hph ? h + 1 : h);  // unconditional: the last head reloads its own rows
     __syncthreads();
     // the previous head's partial sums are complete: assemble its d_cumA on a
     // rotating wave while the other waves start on this head
-    if (BF && hh > 0 && w == (int)((hh - 1) % CH_NW))
-      epilogue(prev_h, prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
+    if (BF) {
+      const bool on = hh > 0 && w == (int)((hh - 1) % CH_NW);
+      float v = 0.0f;
+      if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
+      epi_store(on, prev_h, v);
+    }
 
     // ---- ORANGE: G1 = dy . x^T on lower-triangular tile pairs; d_cb, row/col sums ----
     {
@@ -666,7 +701,8 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
         s1 += acc3[j] * xv[j];                      // d_decay / delta = sum_p d_decayed_v . x
         s2 += dv * xv[j];
       }
-      if (l < Lc) store4(dxg + r * xrs + (int)h * P + 16 * pt + 4 * q, f32x4{dvo[0], dvo[1], dvo[2], dvo[3]});
+      // rows past the end of the sequence fall outside the resource and are dropped
+      bstore4(bdx, (unsigned)(r * xrs + 16 * pt + 4 * q) * esz, f32x4{dvo[0], dvo[1], dvo[2], dvo[3]}, (const T*)0);
       s1 = sum4q(s1) * dl;
       s2 = sum4q(s2);
       if (q == 0) {
@@ -681,7 +717,9 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     // ---- d_cumA assembly: this head now (float32) or one head later (bf16) ----
     if (!BF) {
       __syncthreads();  // partial row sums complete
-      if (w == 0) epilogue(h, cs, Ah, pbase);
+      float v = 0.0f;
+      if (w == 0) v = epilogue(cs, Ah, pbase);
+      epi_store(w == 0, h, v);
     } else {
       prev_h = h;
       prev_cs = cs;
@@ -690,7 +728,10 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   }
   if (BF && a.hph > 0) {
     __syncthreads();
-    if (w == (int)((a.hph - 1) % CH_NW)) epilogue(prev_h, prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_N * 8 * 64);
+    const bool on = w == (int)((a.hph - 1) % CH_NW);
+    float v = 0.0f;
+    if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_N * 8 * 64);
+    epi_store(on, prev_h, v);
   }
 
   // ---- K2 backward on the head-summed d_cb: dC_k2 = d_cb . B, dB_k2 = d_cb^T . C ----
@@ -773,7 +814,9 @@ bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
   const i64 LM = d.chunk_len * d.mimo_rank;
   if (LM % 16 || LM > MAXRB * 16) return false;
   if (grads_lds_bytes(d) > 160 * 1024) return false;
-  if (LM * d.nheads * d.headdim >= (1ll << 31) || LM * d.ngroups * d.dstate >= (1ll << 31)) return false;
+  // byte offsets inside one chunk are 32-bit (buffer loads, int row offsets)
+  const i64 esz = d.dtype == SSMVJP_BF16 ? 2 : 4;
+  if (LM * d.nheads * d.headdim * esz >= (1ll << 31) || LM * d.ngroups * d.dstate * esz >= (1ll << 31)) return false;
   return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_TILES;
 }
 
