@@ -46,6 +46,16 @@ __device__ __forceinline__ float bload_f32(brsrc r, unsigned off) {
 __device__ __forceinline__ void bstore_f32(brsrc r, unsigned off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
 }
+// n stores that the range check drops.  Issued right after a loop's first
+// prefetch, they give the loop entry the same sequence of outstanding memory
+// operations as its back edge (next loads, then this iteration's stores), so
+// the compiler's wait counts inside the loop cover loads only and never wait
+// for stores to be acknowledged.
+template <int n>
+__device__ __forceinline__ void vmem_pad_stores(brsrc r) {
+#pragma unroll
+  for (int k = 0; k < n; ++k) bstore_f32(r, BUF_OOB, 0.0f);
+}
 
 // ---------------------------------------------------------------------------
 // step size: delta = softplus(z) (z > 20 -> z), its derivative sigmoid(z)

@@ -275,8 +275,12 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   Pre p0, p1;
   i64 step = 0;
   if (a.nc > 0) {  // T = 0 has no chunk to prefetch
+    // each process() ends with SCAN_MAXT state stores after its refill
+    const brsrc pad = make_rsrc(out, 0u);
     issue(p0, chunk_of(0));
+    vmem_pad_stores<SCAN_MAXT>(pad);
     issue(p1, chunk_of(a.nc > 1 ? 1 : 0));
+    vmem_pad_stores<SCAN_MAXT>(pad);
     for (; step + 1 < a.nc; step += 2) {
       process(p0, step, sb0);
       process(p1, step + 1, sb1);
@@ -420,7 +424,12 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
       rd[it] = bload16(bd, off);
     }
   };
-  if (BF) issue(hbase);
+  if (BF) {
+    issue(hbase);
+    // a head issues the next head's loads, then one d_dt store and one dx
+    // store per (p tile, row block) item of this wave
+    if constexpr (FIXED) vmem_pad_stores<1 + (CP / 16) * (CL * CM / 16) / CH_NW>(make_rsrc(a.dxv, 0u));
+  }
   __syncthreads();  // B, C staged
 
   // ---- C.B^T (K2 recompute) over the lower-triangular tile pairs; upper pairs zero ----
