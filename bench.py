@@ -53,16 +53,26 @@ def algorithmic_bytes(w, elem=2, state_elem=2):
     return {"state_scans": scans, "chunk_grads": grads, "path": path}
 
 
-def traffic_from_profile(kernel_name, src_file):
+KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/common.cuh")
+
+
+def sources_sha256(files=KERNEL_SOURCES):
+    """sha256 over the kernel sources, in order (identifies the kernels a counter run measured)."""
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(kernel_name):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; None otherwise."""
+    on the current kernel sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, src_file), "rb").read()
-        if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        if rec.get("sources_sha256") != sources_sha256():
             return None
         return float(rec["bytes_per_launch"])
     except Exception:
@@ -89,6 +99,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU: this build runs on a single MI355X and launches no multi-GPU work "
@@ -104,6 +116,15 @@ def main():
         log("bench.py needs a GPU")
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = 1 << 28  # 2^28 float32 = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
     w = dict(synth.WORKLOADS[WORKLOAD])
     inp = synth.workload_inputs(WORKLOAD)
     c = synth.as_dtype(inp, "bf16", "mamba")
@@ -149,7 +170,7 @@ def main():
     }
     dom_name = max(phases, key=lambda k: phases[k]["ms"])
     dom = phases[dom_name]
-    traffic = traffic_from_profile(dom["kernel"], "selective_state_space_vjp_amd/csrc/ssd_chunk.hip")
+    traffic = traffic_from_profile(dom["kernel"])
     roofline = {"bound": "hbm", "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom["kernel"],
                 "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_ms": round(dom["ms"], 4)}

@@ -802,11 +802,14 @@ static int scan_nb(const ssmvjp_ssd_desc& d) {
   return (int)nb;
 }
 
+// heads of a group split over workgroups only until there is one workgroup per
+// CU: the chunk kernel's LDS footprint admits one resident workgroup per CU, so
+// further splits would run back to back and only add the partial-sum pass
 static i64 pick_hsplit(const ssmvjp_ssd_desc& d, i64 nc) {
   const i64 hpg = d.nheads / d.ngroups;
   const i64 base = d.batch * nc * d.ngroups;
   i64 hs = 1;
-  while (base * hs < 512 && hs * 2 <= hpg && hpg % (hs * 2) == 0) hs *= 2;
+  while (base * hs < 256 && hs * 2 <= hpg && hpg % (hs * 2) == 0) hs *= 2;
   return hs;
 }
 
