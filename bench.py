@@ -53,7 +53,8 @@ def algorithmic_bytes(w, elem=2, state_elem=2):
     return {"state_scans": scans, "chunk_grads": grads, "path": path}
 
 
-KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/common.cuh")
+KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/ssd_common.cuh",
+                  "selective_state_space_vjp_amd/csrc/common.cuh")
 
 
 def sources_sha256(files=KERNEL_SOURCES):

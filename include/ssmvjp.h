@@ -122,10 +122,15 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
  *   dy, dx_or_dv like x_or_v;  d_dt_or_dda like dt_or_da;  dB, dC like B.
  * A last chunk shorter than L (T % L != 0) is handled as a shorter chunk.
  * Constraints (SSMVJP_EUNSUPPORTED otherwise): H % G == 0; P % 16 == 0,
- * N % 16 == 0, P <= 128, N <= 128; L*M % 16 == 0 and L*M <= 64;
- * (P/16) * (N/16) <= 32 unless N is a multiple of 32; and the per-chunk
- * working set fits one workgroup's 160 KiB of LDS (P*N <= 8192 with bf16
- * at L*M = 64; P*N <= 4096 more or less with float32). */
+ * N % 16 == 0, P <= 128, N <= 128; (P/16) * (N/16) <= 32 unless N is a
+ * multiple of 32; and the fused chunk length L*M is either
+ *   - a multiple of 16 up to 64 (one kernel holds the whole chunk): its
+ *     working set must fit 160 KiB of LDS (P*N <= 8192 with bf16 at
+ *     L*M = 64; P*N <= 4096 more or less with float32), or
+ *   - a multiple of 64 above 64 with L <= 64 and M dividing 64 (row-blocked
+ *     kernels, e.g. the rank-4 MIMO form with L = 64): 64 rows of B, C, x and
+ *     dy plus one state must fit 160 KiB of LDS (any P, N <= 128 with bf16;
+ *     P*N <= 8192 more or less with float32). */
 ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
                             const void* x_or_v, const float* dt_or_da, const float* A,
                             const void* B, const void* C, const float* s0,

@@ -1,0 +1,425 @@
+// ssd_blocked.hip -- per-chunk backward of the chunked SSD for long fused
+// chunks (L*M > 64 fused rows, e.g. the rank-4 MIMO form with L = 64), after
+// burn-mamba "combined_backward.rs": the same quantities as the chunk kernel of
+// ssd_chunk.hip (BLUE, ORANGE, the K3 / K2 / K1 backwards and the Mamba-2
+// chain), organised for chunks whose [L*M x L*M] matrices do not fit in LDS.
+//
+// The chunk's fused rows r = l*M + m are cut into 64-row blocks.  The causal
+// intra-chunk terms couple a target block (rows t) with every source block
+// (rows s) at or before it; those lower-triangular block pairs are walked by
+// two kinds of workgroup, one per (batch, chunk, group, block) each, with the
+// heads of the group in a loop (ascending, so group sums are deterministic):
+//
+//   source role (block = s): per head, the K3 backward (d_dv = dS_{c+1}.B^T,
+//     dB_k3 = decayed v^T.dS_{c+1}, d_decay), then for every target block
+//     t >= s the recomputed CB and G1 = dy.v^T tiles, the decay, d_cb and
+//     w = CB * decay, giving d_v_or += w^T.dy, dB_k2 += d_cb^T.C and the
+//     column sums of d_cb * CB.  Stores dx (d_v) per head and dB summed over
+//     the group's heads.
+//   target role (block = t): per head, BLUE (dC_blue = exp(cumA) dy.S_c and
+//     its row sums against C), then for every source block s <= t the same
+//     CB, G1, d_cb (recomputed, transposed), giving dC_k2 += d_cb.B and the
+//     row sums of d_cb * CB.  Stores dC summed over the group's heads.
+//
+// Each wave owns one 16-row tile of its block (an s tile or a t tile), so the
+// d_cb and w tiles it computes are already in the MFMA operand layout that its
+// next products need (the output layout of a tile is the operand layout of the
+// tile with its row index as contraction index): nothing goes through LDS but
+// the staged input rows and states.  The per-row partial sums of d_cumA go to
+// a small buffer; a third kernel, one wave per (batch, chunk, head), adds them
+// up, runs the K1 suffix sum and the chain to d_dt (or d_da).
+//
+// Products accumulate in float32; with bf16 storage the MFMA operands are bf16
+// (inputs as given, d_cb and w rounded once).
+#include "ssd_common.cuh"
+
+namespace ssmvjp {
+
+constexpr int BK_NW = 4;             // waves per workgroup: one 16-row tile of the 64-row block each
+constexpr int BK_NTH = 64 * BK_NW;
+constexpr int BK_R = 64;             // fused rows per block
+constexpr int BK_TMAX = 8;           // P / 16 and N / 16 at most
+
+// 64 rows of a [rows][stride] tensor (ncol columns from src) into LDS rows of
+// `pitch` elements; rows at or past `valid` read zeros (range-checked loads)
+template <typename T>
+__device__ __forceinline__ void bk_stage_rows(T* dst, int pitch, const T* src, i64 stride, int ncol, int valid,
+                                              int tid) {
+  constexpr int E16 = 16 / sizeof(T);
+  const int cpr = ncol / E16;
+  const brsrc r = make_rsrc(src, valid > 0 ? (unsigned)(((valid - 1) * stride + ncol) * sizeof(T)) : 0u);
+  for (int idx = tid; idx < BK_R * cpr; idx += BK_NTH) {
+    const int row = idx / cpr, col = (idx % cpr) * E16;
+    *(u32x4*)(dst + row * pitch + col) = bload16(r, (unsigned)((row * stride + col) * sizeof(T)));
+  }
+}
+// one [P x N] state in native tile order (contiguous)
+template <typename T>
+__device__ __forceinline__ void bk_stage_state(T* dst, const T* src, int PN, int tid) {
+  constexpr int E16 = 16 / sizeof(T);
+  const brsrc r = make_rsrc(src, (unsigned)(PN * sizeof(T)));
+  for (int idx = tid; idx < PN / E16; idx += BK_NTH) *(u32x4*)(dst + idx * E16) = bload16(r, (unsigned)idx * 16u);
+}
+
+template <typename T, int CP, int CN>
+__global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int PAD = BF ? 8 : 4;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int P = CP ? CP : (int)a.P, N = CN ? CN : (int)a.N, M = (int)a.M, L = (int)a.L;
+  const int PT = P / 16, NT = N / 16, LM = (int)a.LM, nblk = LM / BK_R;
+  const int LDN = N + PAD, LDP = P + PAD, PN = P * N;
+  T* Bs = (T*)smem_raw;    // [64][LDN] B rows of a source block
+  T* Cs = Bs + BK_R * LDN;  // [64][LDN] C rows of a target block
+  T* xs = Cs + BK_R * LDN;  // [64][LDP] x / v rows of a source block (one head)
+  T* dys = xs + BK_R * LDP; // [64][LDP] dy rows of a target block (one head)
+  T* STs = dys + BK_R * LDP; // [P*N] dS_{c+1} (source role) or S_c (target role), native tiles
+  float* red = (float*)(STs + PN);  // [BK_NW] cross-wave partial sums
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
+            r16 = lane & 15;
+  __builtin_assume(w >= 0 && w < BK_NW);
+  // XCD-aware order: consecutive workgroups of one (batch, chunk, group) share
+  // their input rows, so they are given ids that land on the same XCD (ids are
+  // dealt to the 8 XCDs round robin)
+  unsigned id = blockIdx.x;
+  if (gridDim.x % 8 == 0) id = (id % 8) * (gridDim.x / 8) + id / 8;
+  const int blk = (int)(id % nblk);
+  id /= nblk;
+  const int role = (int)(id % 2);  // 0 source block, 1 target block
+  id /= 2;
+  const i64 g = id % a.G;
+  id /= a.G;
+  const i64 c = id % a.nc, bi = id / a.nc;
+  const i64 t0 = c * L;
+  const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
+  const int vrows = Lc * M;  // valid fused rows of this chunk
+  auto valid_in = [&](int b) { const int v = vrows - b * BK_R; return v < 0 ? 0 : (v > BK_R ? BK_R : v); };
+  const unsigned esz = sizeof(T);
+  const i64 xstr = a.H * P, bstr = a.G * N;  // fused-row strides
+  const T* Bg = (const T*)a.B + ix_bc(a, bi, t0, 0, g, 0);
+  const T* Cg = (const T*)a.C + ix_bc(a, bi, t0, 0, g, 0);
+  const i64 xrow0 = ix_xv(a, bi, t0, 0, 0, 0);  // x / dy / dx offset of fused row 0, head 0
+  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
+  const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));
+  auto scalars = [&](i64 h) {
+    const float z = bload_f32(make_rsrc(dtg + h, (unsigned)(((Lc - 1) * a.H + 1) * 4)), (unsigned)(lane * a.H * 4));
+    return chunk_scalars(a, z, lane < Lc, bload_f32(rsA, (unsigned)(h * 4)), lane);
+  };
+  float* rowv_c = a.rowv + (bi * a.nc + c) * a.H * RV_N * LM;
+  auto tile_off = [&](int pt, int nt) { return (pt * NT + nt) * 256; };
+  // this lane's column: fused row blk*64 + 16w + r16 of the wave's tile
+  const int col = blk * BK_R + 16 * w + r16;
+  const int l_col = col / M;
+
+  if (role == 0) {
+    // ======================= source block s = blk =========================
+    f32x4 dBT[BK_TMAX];  // dB^T tiles (rows n, columns s), summed over the group's heads
+#pragma unroll
+    for (int i = 0; i < BK_TMAX; ++i) dBT[i] = zero4();
+    bk_stage_rows(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    for (i64 hh = 0; hh < a.hpg; ++hh) {
+      const i64 h = g * a.hpg + hh;
+      const ChunkScalars cs = scalars(h);
+      const float cum_s = __shfl(cs.cum, l_col & 63, 64), delta_s = __shfl(cs.delta, l_col & 63, 64);
+      const float edec = exp_hw(cs.end - cum_s), xcol = delta_s * edec;
+      __syncthreads();  // the previous head is done with xs / STs / Cs / dys
+      bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+      bk_stage_state(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+      __syncthreads();
+
+      // ---- K3: d_dv^T = dS_{c+1}.B^T (rows p, columns s); dB_k3^T += dS^T . (xcol v)^T ----
+      f32x4 dvT[BK_TMAX];
+      float s1 = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < BK_TMAX; ++pt) {
+        dvT[pt] = zero4();
+        if (pt >= PT) continue;
+        f32x4 acc = zero4();
+        for (int kb = 0; kb < NT; ++kb)
+          mma(acc, ld_ntv_t(STs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+        float xv[4];
+        frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);  // x[s][p .. p+3], p = 16 pt + 4q
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s1 += acc[j] * xv[j];  // d_decay / delta = sum_p d_dv . x
+          dvT[pt][j] = acc[j] * edec;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < BK_TMAX; ++nt) {
+        if (nt >= NT) continue;
+        f32x4 acc = zero4();
+        for (int kb = 0; kb < PT; ++kb)
+          mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dBT[nt][j] += acc[j] * xcol;
+      }
+
+      // ---- ORANGE and K2 over the target blocks t >= s ----
+      float ocol = 0.0f;
+      for (int tb = blk; tb < nblk; ++tb) {
+        __syncthreads();  // the previous target block is done with Cs / dys
+        bk_stage_rows(Cs, LDN, Cg + (i64)tb * BK_R * bstr, bstr, N, valid_in(tb), tid);
+        bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)tb * BK_R * xstr + h * P, xstr, P, valid_in(tb), tid);
+        __syncthreads();
+        Frag<T> wf[4], df[4];  // w and d_cb tiles (rows t, columns s): operands with k = t
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 cb = zero4(), g1 = zero4();
+          for (int kb = 0; kb < NT; ++kb)
+            mma(cb, ld_colk(Cs, LDN, 16 * tt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+          for (int kb = 0; kb < PT; ++kb)
+            mma(g1, ld_colk(dys, LDP, 16 * tt, 16 * kb, lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
+          float wv[4], dv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int lt = (tb * BK_R + 16 * tt + 4 * q + j) / M;
+            const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
+            const float dec = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
+            const float dcb = g1[j] * delta_s * dec;  // d_w = dy.v^T with v = delta x (delta = 1 for RAW)
+            ocol += dcb * cb[j];
+            wv[j] = cb[j] * dec;
+            dv[j] = dcb;
+          }
+          wf[tt] = frag_make<T>(wv);
+          df[tt] = frag_make<T>(dv);
+        }
+#pragma unroll
+        for (int pt = 0; pt < BK_TMAX; ++pt) {  // d_v_or^T += dy^T . w
+          if (pt >= PT) continue;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) mma(dvT[pt], ld_rowk(dys, LDP, 16 * tt, 16 * pt, lane), wf[tt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < BK_TMAX; ++nt) {  // dB_k2^T += C^T . d_cb
+          if (nt >= NT) continue;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], ld_rowk(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
+        }
+      }
+
+      // ---- per-head outputs: dx (= d_v, times delta for Mamba-2), the column sums ----
+      float dvx = 0.0f;
+      const brsrc rdx = make_rsrc((T*)a.dxv + xrow0 + (i64)blk * BK_R * xstr + h * P,
+                                  valid_in(blk) > 0 ? (unsigned)(((valid_in(blk) - 1) * xstr + P) * esz) : 0u);
+#pragma unroll
+      for (int pt = 0; pt < BK_TMAX; ++pt) {
+        if (pt >= PT) continue;
+        float xv[4];
+        frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dvx += dvT[pt][j] * xv[j];
+          o[j] = a.raw ? dvT[pt][j] : dvT[pt][j] * delta_s;
+        }
+        bstore4(rdx, (unsigned)(((16 * w + r16) * xstr + 16 * pt + 4 * q) * esz), o, (const T*)0);
+      }
+      s1 = sum4q(s1) * delta_s;
+      ocol = sum4q(ocol);
+      dvx = sum4q(dvx);
+      float* rv = rowv_c + h * RV_N * LM;
+      if (q == 0) {
+        rv[RV_DEC * LM + col] = s1;
+        rv[RV_OCOL * LM + col] = ocol;
+        rv[RV_DVX * LM + col] = dvx;
+      }
+    }
+    // dB (rows s, 4 consecutive n per lane), summed over the group's heads
+    const brsrc rdB = make_rsrc((T*)a.dB + ix_bc(a, bi, t0, 0, g, 0) + (i64)blk * BK_R * bstr,
+                                valid_in(blk) > 0 ? (unsigned)(((valid_in(blk) - 1) * bstr + N) * esz) : 0u);
+#pragma unroll
+    for (int nt = 0; nt < BK_TMAX; ++nt) {
+      if (nt >= NT) continue;
+      bstore4(rdB, (unsigned)(((16 * w + r16) * bstr + 16 * nt + 4 * q) * esz), dBT[nt], (const T*)0);
+    }
+  } else {
+    // ======================= target block t = blk =========================
+    f32x4 dCT[BK_TMAX];  // dC^T tiles (rows n, columns t), summed over the group's heads
+#pragma unroll
+    for (int i = 0; i < BK_TMAX; ++i) dCT[i] = zero4();
+    bk_stage_rows(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    for (i64 hh = 0; hh < a.hpg; ++hh) {
+      const i64 h = g * a.hpg + hh;
+      const ChunkScalars cs = scalars(h);
+      const float cum_t = __shfl(cs.cum, l_col & 63, 64);
+      const float ecol = exp_hw(cum_t);
+      __syncthreads();  // the previous head is done with dys / STs / Bs / xs
+      bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+      const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+      bk_stage_state(STs, Sg, PN, tid);
+      __syncthreads();
+
+      // ---- d_end = sum_{p,n} S_c * dS_{c+1} (once per chunk and head) ----
+      if (blk == 0) {
+        constexpr int E16 = 16 / sizeof(T);
+        const brsrc rdS = make_rsrc((const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, (unsigned)PN * esz);
+        float part = 0.0f;
+        for (int idx = tid; idx < PN / E16; idx += BK_NTH) {
+          const u32x4 u = bload16(rdS, (unsigned)idx * 16u);
+          const u32x4 v = *(const u32x4*)(STs + idx * E16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (BF) {
+              part += __uint_as_float(u[e] << 16) * __uint_as_float(v[e] << 16);
+              part += __uint_as_float(u[e] & 0xffff0000u) * __uint_as_float(v[e] & 0xffff0000u);
+            } else {
+              part += __uint_as_float(u[e]) * __uint_as_float(v[e]);
+            }
+          }
+        }
+        part = wave_sum(part);
+        if (lane == 0) red[w] = part;
+        __syncthreads();
+        if (tid == 0) {
+          float s = 0.0f;
+          for (int k = 0; k < BK_NW; ++k) s += red[k];
+          a.dend[(bi * a.nc + c) * a.H + h] = s;
+        }
+      }
+
+      // ---- BLUE: dC_blue^T = S_c^T . (dy * exp(cumA))^T ; its row sums against C ----
+      float blue = 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < BK_TMAX; ++nt) {
+        if (nt >= NT) continue;
+        f32x4 acc = zero4();
+        for (int kb = 0; kb < PT; ++kb)  // A: rows n, k = p (native tile); B: k = p, columns t
+          mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+        float cv[4];
+        frag_get(ld_colk(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float val = acc[j] * ecol;
+          dCT[nt][j] += val;
+          blue += cv[j] * val;
+        }
+      }
+
+      // ---- ORANGE row sums and K2 over the source blocks s <= t (transposed tiles) ----
+      float orow = 0.0f;
+      for (int sb = 0; sb <= blk; ++sb) {
+        __syncthreads();  // the previous source block is done with Bs / xs
+        bk_stage_rows(Bs, LDN, Bg + (i64)sb * BK_R * bstr, bstr, N, valid_in(sb), tid);
+        bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)sb * BK_R * xstr + h * P, xstr, P, valid_in(sb), tid);
+        __syncthreads();
+        Frag<T> df[4];  // d_cb^T tiles (rows s, columns t): operands with k = s
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          f32x4 cb = zero4(), g1 = zero4();
+          for (int kb = 0; kb < NT; ++kb)
+            mma(cb, ld_colk(Bs, LDN, 16 * ss, 16 * kb, lane), ld_colk(Cs, LDN, 16 * w, 16 * kb, lane));
+          for (int kb = 0; kb < PT; ++kb)
+            mma(g1, ld_colk(xs, LDP, 16 * ss, 16 * kb, lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+          float dv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ls = (sb * BK_R + 16 * ss + 4 * q + j) / M;
+            const float cs_s = __shfl(cs.cum, ls & 63, 64);  // every lane takes part in the shuffles
+            const float d_s = __shfl(cs.delta, ls & 63, 64);
+            const float dec = (ls <= l_col && l_col < Lc) ? exp_hw(cum_t - cs_s) : 0.0f;
+            const float dcb = g1[j] * d_s * dec;
+            orow += dcb * cb[j];
+            dv[j] = dcb;
+          }
+          df[ss] = frag_make<T>(dv);
+        }
+#pragma unroll
+        for (int nt = 0; nt < BK_TMAX; ++nt) {  // dC_k2^T += B^T . d_cb^T
+          if (nt >= NT) continue;
+#pragma unroll
+          for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], ld_rowk(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
+        }
+      }
+      blue = sum4q(blue);
+      orow = sum4q(orow);
+      float* rv = rowv_c + h * RV_N * LM;
+      if (q == 0) {
+        rv[RV_BLUE * LM + col] = blue;
+        rv[RV_OROW * LM + col] = orow;
+      }
+    }
+    // dC (rows t, 4 consecutive n per lane), summed over the group's heads
+    const brsrc rdC = make_rsrc((T*)a.dC + ix_bc(a, bi, t0, 0, g, 0) + (i64)blk * BK_R * bstr,
+                                valid_in(blk) > 0 ? (unsigned)(((valid_in(blk) - 1) * bstr + N) * esz) : 0u);
+#pragma unroll
+    for (int nt = 0; nt < BK_TMAX; ++nt) {
+      if (nt >= NT) continue;
+      bstore4(rdC, (unsigned)(((16 * w + r16) * bstr + 16 * nt + 4 * q) * esz), dCT[nt], (const T*)0);
+    }
+  }
+}
+
+// d_cumA from its sources, the K1 suffix sum and the chain to d_dt (or d_da):
+// one wave per (batch, chunk, head), one lane per step l (rows l*M .. l*M+M-1)
+__global__ void __launch_bounds__(64) ssd_blocked_epilogue_kernel(SsdArgs a) {
+  const int lane = threadIdx.x;
+  i64 id = blockIdx.x;
+  const i64 h = id % a.H;
+  id /= a.H;
+  const i64 c = id % a.nc, bi = id / a.nc;
+  const int L = (int)a.L, M = (int)a.M, LM = (int)a.LM;
+  const i64 t0 = c * L;
+  const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
+  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
+  const float z = bload_f32(make_rsrc(dtg + h, (unsigned)(((Lc - 1) * a.H + 1) * 4)), (unsigned)(lane * a.H * 4));
+  const float Ah = a.raw ? 0.0f : a.A[h];
+  const ChunkScalars cs = chunk_scalars(a, z, lane < Lc, Ah, lane);
+  const float* rv = a.rowv + ((bi * a.nc + c) * a.H + h) * RV_N * LM;
+  float dcl = 0.0f, dvxl = 0.0f, qv = 0.0f;
+  if (lane < Lc) {
+    const float e = exp_hw(cs.end - cs.cum);
+    for (int m = 0; m < M; ++m) {
+      const int r = lane * M + m;
+      const float q1 = rv[RV_DEC * LM + r] * e;
+      dcl += rv[RV_BLUE * LM + r] + rv[RV_OROW * LM + r] - rv[RV_OCOL * LM + r] - q1;
+      dvxl += rv[RV_DVX * LM + r];
+      qv += q1;
+    }
+  }
+  const float qsum = wave_sum(qv);
+  const float dendt = a.dend[(bi * a.nc + c) * a.H + h] * exp_hw(cs.end);
+  if (lane == Lc - 1) dcl += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
+  const float dda = wave_incl_suffix(lane < Lc ? dcl : 0.0f, lane);
+  if (lane < Lc) a.d_dtda[(bi * a.T + t0 + lane) * a.H + h] = a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
+}
+
+// ===========================================================================
+// host side
+// ===========================================================================
+static size_t blocked_lds_bytes(i64 P, i64 N, bool bf) {
+  const i64 e = bf ? 2 : 4, pad = bf ? 8 : 4;
+  return (size_t)(e * (2 * BK_R * (N + pad) + 2 * BK_R * (P + pad) + P * N) + 4 * BK_NW);
+}
+
+bool ssd_blocked_supported(const ssmvjp_ssd_desc& d) {
+  const i64 LM = d.chunk_len * d.mimo_rank;
+  // chunk_len <= 64: one lane per step in the chunk scalars; M divides 64: the
+  // rows of a step never straddle two blocks, so the causal pairs are exactly
+  // the (target block >= source block) pairs that the two roles walk
+  if (LM <= 64 || LM % BK_R || d.chunk_len > 64 || BK_R % d.mimo_rank) return false;
+  if (d.headdim % 16 || d.dstate % 16 || d.headdim > 16 * BK_TMAX || d.dstate > 16 * BK_TMAX) return false;
+  return blocked_lds_bytes(d.headdim, d.dstate, d.dtype == SSMVJP_BF16) <= 160 * 1024;
+}
+
+template <typename T>
+static void launch_blocked_t(const SsdArgs& a, hipStream_t stream) {
+  const size_t lds = blocked_lds_bytes(a.P, a.N, sizeof(T) == 2);
+  const i64 grid = a.b * a.nc * a.G * 2 * (a.LM / BK_R);
+  if (a.P == 64 && a.N == 128)
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  else
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  hipLaunchKernelGGL(ssd_blocked_epilogue_kernel, dim3((unsigned)(a.b * a.nc * a.H)), dim3(64), 0, stream, a);
+}
+
+void launch_ssd_blocked_grads(const SsdArgs& a, bool is_bf16, hipStream_t stream) {
+  if (a.T == 0) return;
+  if (is_bf16)
+    launch_blocked_t<bf16>(a, stream);
+  else
+    launch_blocked_t<float>(a, stream);
+}
+
+}  // namespace ssmvjp

@@ -34,115 +34,9 @@
 // All products accumulate in float32.  With bf16 storage the MFMA operands are
 // bf16 (inputs as given; exp-scaled operands rounded once); decays, cumsums,
 // states and all reductions stay float32.
-#include "common.cuh"
-#include "kernels.h"
+#include "ssd_common.cuh"
 
 namespace ssmvjp {
-
-struct SsdArgs {
-  i64 b, T, H, P, N, G, M, L, LM, nc, hpg, hsplit, hph;
-  int raw;  // 1: (v, da) inputs; 0: Mamba-2 (x, dt, A)
-  const void* xv;
-  const float* dtda;
-  const float* A;
-  const void* B;
-  const void* C;
-  const float* s0;
-  const void* dy;
-  const float* dsf;
-  void* dxv;
-  float* d_dtda;
-  void* dB;
-  void* dC;
-  float* d_s0;
-  void* S;      // [b][nc][H][P*N] chunk-input states, native tiles
-  void* dS;     // [b][nc][H][P*N] dS_{c+1}, native tiles
-  float* part;  // [2][hsplit][b*T*M*G*N] per-split dB / dC partials (hsplit > 1)
-};
-
-static inline i64 cdiv(i64 a, i64 b) { return (a + b - 1) / b; }
-
-// Offsets.  Big tensors x/v, dy, dx/dv: [b][T][M][H][P]; B, C, dB, dC: [b][T][M][G][N].
-__device__ __forceinline__ i64 ix_xv(const SsdArgs& a, i64 bi, i64 t, i64 m, i64 h, i64 p) {
-  return (((bi * a.T + t) * a.M + m) * a.H + h) * a.P + p;
-}
-__device__ __forceinline__ i64 ix_bc(const SsdArgs& a, i64 bi, i64 t, i64 m, i64 g, i64 n) {
-  return (((bi * a.T + t) * a.M + m) * a.G + g) * a.N + n;
-}
-// native tile offset of state element (p, n) inside one [P x N] state
-__device__ __forceinline__ i64 native_off(int N, int pt, int nt, int lane, int j) {
-  return ((i64)(pt * (N / 16) + nt) * 64 + lane) * 4 + j;
-}
-
-__device__ __forceinline__ void store4(float* p, const f32x4& v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
-__device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
-  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 u = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  *(bf16x4*)p = u;
-}
-
-// four float results stored as 4 consecutive elements of T through a resource
-// (dropped past the resource size)
-__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const float*) {
-  u32x4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-  __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 0);
-}
-__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const bf16*) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 u = {(unsigned)(unsigned short)bf16_bits(v[0]) | ((unsigned)(unsigned short)bf16_bits(v[1]) << 16),
-             (unsigned)(unsigned short)bf16_bits(v[2]) | ((unsigned)(unsigned short)bf16_bits(v[3]) << 16)};
-  __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
-}
-
-// 16-byte global <-> register chunks for staging (8 bf16 or 4 float)
-__device__ __forceinline__ u32x4 zero_u4() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return z;
-}
-__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
-// scale the elements of a 16-byte chunk by s (float math, result in T)
-__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const float*) {
-  u32x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(__uint_as_float(u[e]) * s);
-  return o;
-}
-__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
-  u32x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float lo = __uint_as_float(u[e] << 16) * s, hi = __uint_as_float(u[e] & 0xffff0000u) * s;
-    o[e] = (unsigned)(unsigned short)bf16_bits(lo) | ((unsigned)(unsigned short)bf16_bits(hi) << 16);
-  }
-  return o;
-}
-
-// Per-chunk step sizes for one head, one lane per step l < L (lanes >= L and
-// steps past T get zeros, which keeps cumA flat over a short last chunk).
-// z is this lane's dt (Mamba-2) or da (RAW) value, Ah the head's A (Mamba-2).
-struct ChunkScalars {
-  float delta;  // softplus(dt) (Mamba-2) or 1 (RAW)
-  float sig;    // sigmoid(dt) (Mamba-2)
-  float cum;    // inclusive cumsum of da within the chunk
-  float end;    // cumsum at the last step of the chunk (same in every lane)
-};
-
-__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z, bool valid, float Ah, int lane) {
-  ChunkScalars s;
-  float da;
-  if (a.raw) {
-    s.delta = 1.0f;
-    s.sig = 0.0f;
-    da = z;
-  } else {
-    s.delta = valid ? softplus_f(z) : 0.0f;
-    s.sig = sigmoid_f(z);
-    da = s.delta * Ah;
-  }
-  s.cum = wave_incl_scan(valid ? da : 0.0f, lane);
-  s.end = __shfl(s.cum, 63, 64);
-  return s;
-}
 
 // ===========================================================================
 // kernel 1: forward and reverse state scans over chunks
@@ -151,31 +45,39 @@ constexpr int SCAN_NW = 8;                   // waves per workgroup
 constexpr int SCAN_NTH = 64 * SCAN_NW;
 constexpr int SCAN_TILES = 32;               // state tiles per workgroup (at most)
 constexpr int SCAN_MAXT = SCAN_TILES / SCAN_NW;  // state tiles per wave
+constexpr int SCAN_SB = 64;                  // fused rows staged per step (at most)
 
 // Shape parameters CP, CNB (n block), CL, CM: a non-zero value fixes P, the n
-// block, the chunk length or the rank at compile time (the workload shape gets
-// its own instantiation); zero reads it from the arguments.
+// block, the chunk length or the rank at compile time (the workload shapes get
+// their own instantiations); zero reads it from the arguments.
 //
-// Pipeline: the operand rows of chunk c+2 are in flight in registers while
-// chunk c is staged into one of two LDS buffers and chunk c+1's registers wait;
-// with two LDS buffers a single barrier per chunk separates the staging of a
-// buffer from its fragment reads (the reads of that buffer two chunks back
-// ended before the previous chunk's barrier).
+// A step stages SB = min(L*M, 64) fused rows of one chunk: a whole chunk when
+// L*M <= 64, else one of the chunk's L*M/64 row blocks, whose products add up
+// in registers until the chunk's last block applies the state update.
+//
+// Pipeline: the rows of step s+2 are in flight in registers while step s is
+// staged into one of two LDS buffers and step s+1's registers wait; with two
+// LDS buffers a single barrier per step separates the staging of a buffer from
+// its fragment reads (the reads of that buffer two steps back ended before the
+// previous step's barrier).
 template <typename T, int CP, int CNB, int CL, int CM>
 __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int nb_arg) {
   constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr bool FIXED = CP && CNB && CL && CM;
-  constexpr int MAXC_O = FIXED ? (CL * CM * CP / E16 + SCAN_NTH - 1) / SCAN_NTH : 64 * 128 / E16 / SCAN_NTH;
-  constexpr int MAXC_B = FIXED ? (CL * CM * CNB / E16 + SCAN_NTH - 1) / SCAN_NTH : 64 * 128 / E16 / SCAN_NTH;
+  constexpr int CSB = FIXED ? (CL * CM < SCAN_SB ? CL * CM : SCAN_SB) : 0;
+  constexpr int MAXC_O = FIXED ? (CSB * CP / E16 + SCAN_NTH - 1) / SCAN_NTH : SCAN_SB * 128 / E16 / SCAN_NTH;
+  constexpr int MAXC_B = FIXED ? (CSB * CNB / E16 + SCAN_NTH - 1) / SCAN_NTH : SCAN_SB * 128 / E16 / SCAN_NTH;
   constexpr int MAXC = MAXC_O > MAXC_B ? MAXC_O : MAXC_B;  // staging chunks per thread
   constexpr int PAD = 16 / sizeof(T);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int P = CP ? CP : (int)a.P, N = (int)a.N, L = CL ? CL : (int)a.L, M = CM ? CM : (int)a.M;
   const int NB = CNB ? CNB : nb_arg, LM = L * M;
-  const int PT = P / 16, NTB = NB / 16, RB = LM / 16;
+  const int SB = CSB ? CSB : (LM < SCAN_SB ? LM : SCAN_SB);  // fused rows per step
+  const int NSUB = LM / SB;                                  // steps per chunk
+  const int PT = P / 16, NTB = NB / 16, RB = SB / 16;
   const int PPO = P + PAD, PPB = NB + PAD;  // row pitches (elements) of the staged tiles
-  const int BUF = LM * (PPO + PPB);         // elements per LDS buffer
-  // buffer k: [LM][PPO] v or dy rows scaled per step, then [LM][PPB] B or C rows (this n block)
+  const int BUF = SB * (PPO + PPB);         // elements per LDS buffer
+  // buffer k: [SB][PPO] v or dy rows scaled per step, then [SB][PPB] B or C rows (this n block)
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
@@ -194,11 +96,11 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   const float* init = dir == 0 ? a.s0 : a.dsf;
 
   const int ntiles = PT * NTB;  // tiles of this wave: ti = pt * NTB + nt, ti % SCAN_NW == w
-  f32x4 st[SCAN_MAXT];
+  f32x4 st[SCAN_MAXT], acc[SCAN_MAXT];
 #pragma unroll
   for (int k = 0; k < SCAN_MAXT; ++k) {
     const int ti = w + SCAN_NW * k;
-    st[k] = zero4();
+    st[k] = acc[k] = zero4();
     if (ti < ntiles && init) {
       const int pt = ti / NTB, nt = ti % NTB;
 #pragma unroll
@@ -207,7 +109,7 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
     }
   }
 
-  // register prefetch of one chunk: the step values, operand rows, B/C rows.
+  // register prefetch of one step: the chunk's step values, operand rows, B/C rows.
   // Branch-free buffer loads: rows past the end of the sequence read zeros.
   struct Pre {
     float z;
@@ -216,57 +118,73 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   const int oc_row = P / E16, bc_row = NB / E16;
   const unsigned esz = sizeof(T);
   const float Ah = a.raw ? 0.0f : a.A[h];
-  auto chunk_of = [&](i64 step) { return dir == 0 ? step : a.nc - 1 - step; };
-  auto issue = [&](Pre& pr, i64 c) {
+  const i64 nsteps = a.nc * NSUB;
+  auto chunk_of = [&](i64 step) { const i64 ci = step / NSUB; return dir == 0 ? ci : a.nc - 1 - ci; };
+  auto issue = [&](Pre& pr, i64 step) {
+    const i64 c = chunk_of(step);
+    const int R0 = (int)(step % NSUB) * SB;  // first fused row of this step
     const i64 t0 = c * L;
     const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
-    const int rows = Lc * M;  // valid fused rows (>= 1)
+    const int rows = Lc * M - R0;  // valid fused rows of this step (may be <= 0)
     const brsrc rz = make_rsrc(a.dtda + (bi * a.T + t0) * a.H + h, (unsigned)(((Lc - 1) * a.H + 1) * 4));
     pr.z = bload_f32(rz, (unsigned)(lane * a.H * 4));
-    const brsrc ro = make_rsrc(op + ix_xv(a, bi, t0, 0, h, 0), (unsigned)(((rows - 1) * a.H * P + P) * esz));
-    const brsrc rb = make_rsrc(bc + ix_bc(a, bi, t0, 0, g, n0), (unsigned)(((rows - 1) * a.G * a.N + NB) * esz));
+    const brsrc ro = make_rsrc(op + ix_xv(a, bi, t0, 0, h, 0) + (i64)R0 * a.H * P,
+                               rows > 0 ? (unsigned)(((rows - 1) * a.H * P + P) * esz) : 0u);
+    const brsrc rb = make_rsrc(bc + ix_bc(a, bi, t0, 0, g, n0) + (i64)R0 * a.G * a.N,
+                               rows > 0 ? (unsigned)(((rows - 1) * a.G * a.N + NB) * esz) : 0u);
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
       const int r1 = idx / oc_row, c1 = (idx % oc_row) * E16;
       const int r2 = idx / bc_row, c2 = (idx % bc_row) * E16;
-      pr.o[it] = bload16(ro, idx < LM * oc_row ? (unsigned)((r1 * a.H * P + c1) * esz) : BUF_OOB);
-      pr.b[it] = bload16(rb, idx < LM * bc_row ? (unsigned)((r2 * a.G * a.N + c2) * esz) : BUF_OOB);
+      pr.o[it] = bload16(ro, idx < SB * oc_row ? (unsigned)((r1 * a.H * P + c1) * esz) : BUF_OOB);
+      pr.b[it] = bload16(rb, idx < SB * bc_row ? (unsigned)((r2 * a.G * a.N + c2) * esz) : BUF_OOB);
     }
   };
-  // one chunk: step scalars, staging into LDS buffer sb, refill of pr with
-  // chunk step + 2 (clamped to the last step: loads that are never used keep
-  // the issue unconditional), one barrier, then the state tiles
+  // per-chunk scalars, set on the chunk's first step
+  float sc = 0.0f, e_end = 1.0f;
+  // one step: (first step of a chunk) step scalars, staging into LDS buffer sb,
+  // refill of pr with step + 2 (clamped to the last step: loads that are never
+  // used keep the issue unconditional), one barrier, then the state tiles; the
+  // chunk's last step stores S_c (or dS_{c+1}) and applies the state update
   auto process = [&](Pre& pr, i64 step, T* sb) {
     const i64 c = chunk_of(step);
-    const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
-    const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, Ah, lane);
-    const float sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
-    const float e_end = exp_hw(cs.end);
+    const int ks = (int)(step % NSUB);
+    const bool last = ks == NSUB - 1;
+    if (ks == 0) {
+      const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
+      const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, Ah, lane);
+      sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
+      e_end = exp_hw(cs.end);
+    }
     T* opS = sb;
-    T* bcS = sb + LM * PPO;
+    T* bcS = sb + SB * PPO;
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
       const int r = idx / oc_row;
-      const float s_r = __shfl(sc, (r / M) & 63, 64);
-      if (idx < LM * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(pr.o[it], s_r, (const T*)0);
-      if (idx < LM * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = pr.b[it];
+      const float s_r = __shfl(sc, ((ks * SB + r) / M) & 63, 64);
+      if (idx < SB * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(pr.o[it], s_r, (const T*)0);
+      if (idx < SB * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = pr.b[it];
     }
-    issue(pr, chunk_of(step + 2 < a.nc ? step + 2 : a.nc - 1));
+    issue(pr, step + 2 < nsteps ? step + 2 : nsteps - 1);
     __syncthreads();
-    T* outc = out + ((bi * a.nc + c) * a.H + h) * (i64)P * N;
+    // state block of this chunk and head; the store is dropped except on the
+    // chunk's last step (a range check, so that no store sits in a branch)
+    const brsrc rout = make_rsrc(out + ((bi * a.nc + c) * a.H + h) * (i64)P * N, (unsigned)(P * N) * esz);
 #pragma unroll
     for (int k = 0; k < SCAN_MAXT; ++k) {
       const int ti = w + SCAN_NW * k;
       if (ti >= ntiles) continue;
       const int pt = ti / NTB, nt = ti % NTB;
-      store4(outc + native_off(N, pt, n0 / 16 + nt, lane, 0), st[k]);
-      f32x4 acc = zero4();
+      bstore4(rout, last ? (unsigned)native_off(N, pt, n0 / 16 + nt, lane, 0) * esz : BUF_OOB, st[k], (const T*)0);
       for (int kb = 0; kb < RB; ++kb)
-        mma(acc, ld_rowk(opS, PPO, 16 * kb, 16 * pt, lane), ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane));
+        mma(acc[k], ld_rowk(opS, PPO, 16 * kb, 16 * pt, lane), ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st[k][j] = e_end * st[k][j] + acc[j];
+      for (int j = 0; j < 4; ++j) {
+        st[k][j] = last ? e_end * st[k][j] + acc[k][j] : st[k][j];
+        acc[k][j] = last ? 0.0f : acc[k][j];
+      }
     }
   };
 
@@ -274,18 +192,18 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   T* sb1 = sb0 + BUF;
   Pre p0, p1;
   i64 step = 0;
-  if (a.nc > 0) {  // T = 0 has no chunk to prefetch
+  if (nsteps > 0) {  // T = 0 has no chunk to prefetch
     // each process() ends with SCAN_MAXT state stores after its refill
     const brsrc pad = make_rsrc(out, 0u);
-    issue(p0, chunk_of(0));
+    issue(p0, 0);
     vmem_pad_stores<SCAN_MAXT>(pad);
-    issue(p1, chunk_of(a.nc > 1 ? 1 : 0));
+    issue(p1, nsteps > 1 ? 1 : 0);
     vmem_pad_stores<SCAN_MAXT>(pad);
-    for (; step + 1 < a.nc; step += 2) {
+    for (; step + 1 < nsteps; step += 2) {
       process(p0, step, sb0);
       process(p1, step + 1, sb1);
     }
-    if (step < a.nc) process(p0, step, sb0);
+    if (step < nsteps) process(p0, step, sb0);
   }
   if (dir == 1) {
 #pragma unroll
@@ -797,8 +715,10 @@ __global__ void ssd_head_sum_kernel(const float* __restrict__ part, i64 n, i64 h
 // ===========================================================================
 static int scan_nb(const ssmvjp_ssd_desc& d) {
   // n block per scan workgroup: at most SCAN_TILES state tiles per workgroup
+  // (and halved while the scan has fewer workgroups than CUs)
   i64 nb = d.dstate;
   while ((d.headdim / 16) * (nb / 16) > SCAN_TILES && nb % 32 == 0) nb /= 2;
+  while (d.batch * d.nheads * 2 * (d.dstate / nb) < 256 && nb % 32 == 0) nb /= 2;
   return (int)nb;
 }
 
@@ -824,19 +744,20 @@ static size_t grads_lds_bytes(const ssmvjp_ssd_desc& d) {
 bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
   if (d.headdim % 16 || d.dstate % 16 || d.headdim > 128 || d.dstate > 16 * CH_NW) return false;
   const i64 LM = d.chunk_len * d.mimo_rank;
-  if (LM % 16 || LM > MAXRB * 16) return false;
-  if (grads_lds_bytes(d) > 160 * 1024) return false;
+  if (LM % 16) return false;
   // byte offsets inside one chunk are 32-bit (buffer loads, int row offsets)
   const i64 esz = d.dtype == SSMVJP_BF16 ? 2 : 4;
   if (LM * d.nheads * d.headdim * esz >= (1ll << 31) || LM * d.ngroups * d.dstate * esz >= (1ll << 31)) return false;
-  return (d.headdim / 16) * (scan_nb(d) / 16) <= SCAN_TILES;
+  if ((d.headdim / 16) * (scan_nb(d) / 16) > SCAN_TILES) return false;
+  if (LM > SCAN_SB) return ssd_blocked_supported(d);  // long fused chunks: row-blocked kernels
+  return LM <= MAXRB * 16 && grads_lds_bytes(d) <= 160 * 1024;
 }
 
 SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
   SsdPlan p{};
   p.nc = cdiv(d.seqlen, d.chunk_len);
   p.LM = d.chunk_len * d.mimo_rank;
-  p.hsplit = pick_hsplit(d, p.nc);
+  p.hsplit = p.LM > SCAN_SB ? 1 : pick_hsplit(d, p.nc);  // the row-blocked path loops over all heads
   p.state_elem = d.dtype == SSMVJP_BF16 ? 2 : 4;
   const i64 states = d.batch * p.nc * d.nheads * d.headdim * d.dstate;
   i64 off = 0;
@@ -848,6 +769,9 @@ SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
   p.off_S = carve(states * p.state_elem);
   p.off_dS = carve(states * p.state_elem);
   p.off_part = carve(p.hsplit > 1 ? 2 * p.hsplit * d.batch * d.seqlen * d.mimo_rank * d.ngroups * d.dstate * 4 : 0);
+  const bool blocked = p.LM > SCAN_SB;
+  p.off_rowv = carve(blocked ? d.batch * p.nc * d.nheads * RV_N * p.LM * 4 : 0);
+  p.off_dend = carve(blocked ? d.batch * p.nc * d.nheads * 4 : 0);
   p.bytes = (size_t)off;
   return p;
 }
@@ -865,13 +789,16 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
   a.S = ws + plan.off_S;
   a.dS = ws + plan.off_dS;
   a.part = (float*)(ws + plan.off_part);
+  a.rowv = (float*)(ws + plan.off_rowv);
+  a.dend = (float*)(ws + plan.off_dend);
   return a;
 }
 
 template <typename T>
 static size_t states_lds(const SsdArgs& a, int NB) {
   const int PAD = 16 / sizeof(T);
-  return 2 * sizeof(T) * (size_t)a.LM * ((a.P + PAD) + (NB + PAD));  // two buffers
+  const size_t SB = a.LM < SCAN_SB ? a.LM : SCAN_SB;
+  return 2 * sizeof(T) * SB * ((a.P + PAD) + (NB + PAD));  // two buffers
 }
 
 template <typename T>
@@ -883,14 +810,19 @@ static size_t grads_lds(const SsdArgs& a) {
                       (bf ? 10 * 256 : 0));
 }
 
-// the Mamba-2 chunked workload shape gets compile-time sizes
+// the Mamba-2 chunked workload shape and the rank-4 MIMO workload shape get
+// compile-time sizes
 static bool workload_shape(const SsdArgs& a) { return a.P == 64 && a.N == 128 && a.L == 64 && a.M == 1; }
+static bool mimo_shape(const SsdArgs& a) { return a.P == 64 && a.N == 128 && a.L == 64 && a.M == 4; }
 
 template <typename T>
 static void launch_states_t(const SsdArgs& a, hipStream_t stream, int NB) {
   const i64 grid1 = a.b * a.H * 2 * (a.N / NB);
   if (workload_shape(a) && NB == 128)
     hipLaunchKernelGGL((ssd_state_scan_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid1), dim3(SCAN_NTH),
+                       states_lds<T>(a, NB), stream, a, NB);
+  else if (mimo_shape(a) && NB == 64)
+    hipLaunchKernelGGL((ssd_state_scan_kernel<T, 64, 64, 64, 4>), dim3((unsigned)grid1), dim3(SCAN_NTH),
                        states_lds<T>(a, NB), stream, a, NB);
   else
     hipLaunchKernelGGL((ssd_state_scan_kernel<T, 0, 0, 0, 0>), dim3((unsigned)grid1), dim3(SCAN_NTH),
@@ -900,6 +832,10 @@ static void launch_states_t(const SsdArgs& a, hipStream_t stream, int NB) {
 template <typename T>
 static void launch_grads_t(const SsdArgs& a, hipStream_t stream) {
   if (a.T == 0) return;
+  if (a.LM > SCAN_SB) {
+    launch_ssd_blocked_grads(a, sizeof(T) == 2, stream);
+    return;
+  }
   const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
   if (workload_shape(a))
     hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid2), dim3(CH_NTH),

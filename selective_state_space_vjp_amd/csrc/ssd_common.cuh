@@ -1,0 +1,129 @@
+// ssd_common.cuh -- pieces shared by the chunked SSD backward kernels
+// (ssd_chunk.hip: state scans and the per-chunk backward for fused chunks of at
+// most 64 rows; ssd_blocked.hip: the row-blocked per-chunk backward for longer
+// fused chunks): the argument block, tensor offsets, staging and store helpers
+// and the per-chunk step scalars.
+#pragma once
+
+#include "common.cuh"
+#include "kernels.h"
+
+namespace ssmvjp {
+
+struct SsdArgs {
+  i64 b, T, H, P, N, G, M, L, LM, nc, hpg, hsplit, hph;
+  int raw;  // 1: (v, da) inputs; 0: Mamba-2 (x, dt, A)
+  const void* xv;
+  const float* dtda;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* s0;
+  const void* dy;
+  const float* dsf;
+  void* dxv;
+  float* d_dtda;
+  void* dB;
+  void* dC;
+  float* d_s0;
+  void* S;      // [b][nc][H][P*N] chunk-input states, native tiles
+  void* dS;     // [b][nc][H][P*N] dS_{c+1}, native tiles
+  float* part;  // [2][hsplit][b*T*M*G*N] per-split dB / dC partials (hsplit > 1)
+  // row-blocked path (L*M > 64) only:
+  float* rowv;  // [b][nc][H][RV_N][LM] per-row partial sums of d_cumA terms
+  float* dend;  // [b][nc][H] sum over (p, n) of S_c * dS_{c+1}
+};
+
+// per-row partial sums kept by the row-blocked path, in this order
+enum { RV_BLUE = 0, RV_OROW, RV_OCOL, RV_DEC, RV_DVX, RV_N };
+
+static inline i64 cdiv(i64 a, i64 b) { return (a + b - 1) / b; }
+
+// Offsets.  Big tensors x/v, dy, dx/dv: [b][T][M][H][P]; B, C, dB, dC: [b][T][M][G][N].
+__device__ __forceinline__ i64 ix_xv(const SsdArgs& a, i64 bi, i64 t, i64 m, i64 h, i64 p) {
+  return (((bi * a.T + t) * a.M + m) * a.H + h) * a.P + p;
+}
+__device__ __forceinline__ i64 ix_bc(const SsdArgs& a, i64 bi, i64 t, i64 m, i64 g, i64 n) {
+  return (((bi * a.T + t) * a.M + m) * a.G + g) * a.N + n;
+}
+// native tile offset of state element (p, n) inside one [P x N] state
+__device__ __forceinline__ i64 native_off(int N, int pt, int nt, int lane, int j) {
+  return ((i64)(pt * (N / 16) + nt) * 64 + lane) * 4 + j;
+}
+
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+__device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
+  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 u = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *(bf16x4*)p = u;
+}
+
+// four float results stored as 4 consecutive elements of T through a resource
+// (dropped past the resource size)
+__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const float*) {
+  u32x4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const bf16*) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 u = {(unsigned)(unsigned short)bf16_bits(v[0]) | ((unsigned)(unsigned short)bf16_bits(v[1]) << 16),
+             (unsigned)(unsigned short)bf16_bits(v[2]) | ((unsigned)(unsigned short)bf16_bits(v[3]) << 16)};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
+}
+
+// 16-byte global <-> register chunks for staging (8 bf16 or 4 float)
+__device__ __forceinline__ u32x4 zero_u4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
+// scale the elements of a 16-byte chunk by s (float math, result in T)
+__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const float*) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(__uint_as_float(u[e]) * s);
+  return o;
+}
+__device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __uint_as_float(u[e] << 16) * s, hi = __uint_as_float(u[e] & 0xffff0000u) * s;
+    o[e] = (unsigned)(unsigned short)bf16_bits(lo) | ((unsigned)(unsigned short)bf16_bits(hi) << 16);
+  }
+  return o;
+}
+
+// Per-chunk step sizes for one head, one lane per step l < L (lanes >= L and
+// steps past T get zeros, which keeps cumA flat over a short last chunk).
+// z is this lane's dt (Mamba-2) or da (RAW) value, Ah the head's A (Mamba-2).
+struct ChunkScalars {
+  float delta;  // softplus(dt) (Mamba-2) or 1 (RAW)
+  float sig;    // sigmoid(dt) (Mamba-2)
+  float cum;    // inclusive cumsum of da within the chunk
+  float end;    // cumsum at the last step of the chunk (same in every lane)
+};
+
+__device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z, bool valid, float Ah, int lane) {
+  ChunkScalars s;
+  float da;
+  if (a.raw) {
+    s.delta = 1.0f;
+    s.sig = 0.0f;
+    da = z;
+  } else {
+    s.delta = valid ? softplus_f(z) : 0.0f;
+    s.sig = sigmoid_f(z);
+    da = s.delta * Ah;
+  }
+  s.cum = wave_incl_scan(valid ? da : 0.0f, lane);
+  s.end = __shfl(s.cum, 63, 64);
+  return s;
+}
+
+
+// row-blocked chunk backward (L*M > 64), defined in ssd_blocked.hip
+bool ssd_blocked_supported(const ssmvjp_ssd_desc& d);
+void launch_ssd_blocked_grads(const SsdArgs& a, bool is_bf16, hipStream_t stream);
+
+}  // namespace ssmvjp

@@ -105,6 +105,15 @@ def _ssd(**kw):
     (dict(headdim=128, dstate=128), bd.EUNSUPPORTED),
     (dict(headdim=128, dstate=64), bd.OK),
     (dict(chunk_len=72), bd.EUNSUPPORTED),
+    # fused chunks longer than 64 rows (row-blocked kernels): multiples of 64, chunk_len <= 64
+    (dict(form=1, mimo_rank=2), bd.OK),
+    (dict(form=1, mimo_rank=3), bd.EUNSUPPORTED),  # rows of a step would straddle 64-row blocks
+    (dict(form=1, mimo_rank=4, chunk_len=48), bd.OK),
+    (dict(form=1, mimo_rank=4, ngroups=4), bd.OK),
+    (dict(form=1, mimo_rank=5, chunk_len=16), bd.EUNSUPPORTED),
+    (dict(chunk_len=128), bd.EUNSUPPORTED),
+    (dict(form=1, mimo_rank=4, headdim=128, dstate=128), bd.OK),
+    (dict(form=1, mimo_rank=4, headdim=128, dstate=128, dtype=0), bd.EUNSUPPORTED),
 ])
 def test_ssd_descriptor_validation(kw, status):
     st, _ = _ws("ssd_chunk_bwd_workspace", _ssd(**kw))

@@ -1,0 +1,102 @@
+"""GPU parity of ssd_chunk_bwd on long fused chunks (L*M > 64 rows: the
+row-blocked chunk kernels), through the C ABI.
+
+* RAW (v, da) rank-M form against the float64 oracle in fp32 (1e-4) and bf16
+  (2e-2): two and four 64-row blocks, several heads per B/C group (group sums
+  over heads), a shorter last chunk, the generic and the compile-time shapes;
+* the full rank-4 MIMO workload (b=2, T=4096, M=4, H=32, P=64, N=128, G=32,
+  L=64, bf16) in the launch configuration of the library's default plan,
+  batch element 0 against the oracle and the whole batch through the identity
+  <dB, B> = <dv, v> of the exact VJP (y and the final state are bilinear in
+  (v, B) apart from the s0 term, which depends on neither);
+* edge cases: T = 1, a single short chunk, T = 0, determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import rel_maxabs
+from gpu_common import BIG_RAW, TOL, announce, to_device, to_numpy
+from selective_state_space_vjp_amd import binding as bd
+from selective_state_space_vjp_amd import synth
+
+pytestmark = pytest.mark.gpu
+RAW_OUTS = ("dv", "d_da", "dB", "dC", "d_s0")
+
+
+def _gpu_raw(inp, dtype, L):
+    t = to_device(inp, dtype, BIG_RAW)
+    out = bd.ssd_chunk_bwd(t["v"], t["da"], None, t["B"], t["C"], t["s0"], t["dy"], t["ds_final"], chunk_len=L)
+    torch.cuda.synchronize()
+    return {k: to_numpy(v) for k, v in out.items()}
+
+
+def _oracle_raw(inp, dtype):
+    c = synth.as_dtype(inp, dtype, "raw")
+    return oracle.raw_seq_bwd(c["v"], c["da"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"])
+
+
+def _compare(got, ref, keys, tol):
+    errs = {k: rel_maxabs(got[k], ref[k]) for k in keys if ref[k].size}
+    print("[rel_maxabs]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs and max(errs.values()) < tol, errs
+    return errs
+
+
+BLOCKED_SHAPES = [
+    # b, T, M, H, P, N, G, L        fused chunk L*M
+    (1, 128, 4, 2, 32, 32, 2, 32),   # 128: two blocks, one head per group
+    (1, 200, 4, 4, 16, 32, 2, 64),   # 256: four blocks, two heads per group, last chunk of 8 steps
+    (2, 96, 2, 2, 64, 128, 2, 64),   # 128: the compile-time P=64, N=128 instance
+    (1, 130, 4, 2, 64, 128, 1, 64),  # 256: P=64, N=128, two heads per group, last chunk of 2 steps
+    (1, 72, 4, 3, 48, 16, 3, 48),    # 192: three blocks, odd sizes, last chunk of 24 steps
+]
+
+
+@pytest.mark.parametrize("shape", BLOCKED_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_blocked_raw_parity(shape, dtype):
+    b, T, M, H, P, N, G, L = shape
+    announce(f"ssd blocked raw {dtype} {shape}")
+    inp = synth.raw_inputs(b, T, M, H, P, N, G, seed=3 + sum(shape))
+    _compare(_gpu_raw(inp, dtype, L), _oracle_raw(inp, dtype), RAW_OUTS, TOL[dtype])
+
+
+def test_blocked_full_mimo_workload_batch0_and_identity():
+    w = synth.WORKLOADS["mimo_chunk"]
+    announce("ssd blocked bf16 full MIMO workload b=2 T=4096 M=4 H=32 P=64 N=128 G=32 L=64")
+    inp = synth.workload_inputs("mimo_chunk")
+    got = _gpu_raw(inp, "bf16", w["L"])
+    c = synth.as_dtype(inp, "bf16", "raw")
+    lhs = float(np.sum(got["dB"] * c["B"]))
+    rhs = float(np.sum(got["dv"] * c["v"]))
+    print("[identity] <dB,B> =", lhs, " <dv,v> =", rhs, flush=True)
+    assert abs(lhs - rhs) <= 2e-2 * max(abs(rhs), 1e-30) + 1e-3, (lhs, rhs)
+    c0 = {k: (v[:1] if isinstance(v, np.ndarray) and v.ndim >= 3 else v) for k, v in c.items()}
+    ref = oracle.raw_seq_bwd(c0["v"], c0["da"], c0["B"], c0["C"], c0["s0"], c0["dy"], c0["ds_final"])
+    got0 = {k: v[:1] for k, v in got.items()}
+    _compare(got0, ref, RAW_OUTS, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T", [1, 10, 64])
+def test_blocked_short_sequences(T):
+    announce(f"ssd blocked short T={T}")
+    inp = synth.raw_inputs(1, T, 4, 2, 32, 32, 1, seed=T)
+    _compare(_gpu_raw(inp, "f32", 64), _oracle_raw(inp, "f32"), RAW_OUTS, TOL["f32"])
+
+
+def test_blocked_empty_sequence_returns_seed():
+    announce("ssd blocked T=0")
+    inp = synth.raw_inputs(1, 0, 4, 2, 16, 16, 1, seed=2)
+    got = _gpu_raw(inp, "f32", 32)
+    assert np.array_equal(got["d_s0"], inp["ds_final"].astype(np.float32).astype(np.float64))
+
+
+def test_blocked_deterministic_across_runs():
+    announce("ssd blocked determinism bf16")
+    inp = synth.raw_inputs(1, 256, 4, 4, 64, 128, 2, seed=5)
+    a = _gpu_raw(inp, "bf16", 64)
+    b = _gpu_raw(inp, "bf16", 64)
+    for k in RAW_OUTS:
+        assert np.array_equal(a[k], b[k]), k
