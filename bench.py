@@ -40,11 +40,11 @@ def algorithmic_bytes(w, elem=2, state_elem=2):
     Every input read once, every output written once; the stored chunk states
     count once written (state scans) and once read (chunk gradients).
     """
-    b, T, H, P, N, G, L = w["b"], w["T"], w["H"], w["P"], w["N"], w["G"], w["L"]
+    b, T, H, P, N, G, L, M = w["b"], w["T"], w["H"], w["P"], w["N"], w["G"], w["L"], w.get("M", 1)
     nc = -(-T // L)
-    big_x = b * T * H * P * elem           # x, dy, dx each
-    big_bc = b * T * G * N * elem          # B, C, dB, dC each
-    small = b * T * H * 4                  # dt, d_dt each
+    big_x = b * T * M * H * P * elem       # x (or v), dy, dx (or dv) each
+    big_bc = b * T * M * G * N * elem      # B, C, dB, dC each
+    small = b * T * H * 4                  # dt (or da), d_dt (or d_da) each
     state32 = b * H * P * N * 4            # s0, ds_final, d_s0 each
     states = b * nc * H * P * N * state_elem  # stored S or dS
     scans = 2 * big_x + 2 * big_bc + 2 * small + 3 * state32 + 2 * states
@@ -87,7 +87,11 @@ def cpu_baseline(inp_bf16, w):
     threads = oracle.default_threads()
     c = {k: (v[:1] if hasattr(v, "ndim") and v.ndim >= 3 else v) for k, v in inp_bf16.items()}
     t0 = time.perf_counter()
-    oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"], nthreads=threads)
+    if w["form"] == "raw":
+        oracle.raw_seq_bwd(c["v"], c["da"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"], nthreads=threads)
+    else:
+        oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"],
+                             nthreads=threads)
     sec = time.perf_counter() - t0
     return {"value": w["T"] / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"1 of {w['b']} sequences (T={w['T']}, all {w['H']} heads), float64 store-all "
@@ -100,6 +104,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk"),
+                    help="mamba2_chunk (default, the headline line) or mimo_chunk (rank-4 MIMO, RAW form)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -126,17 +132,26 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
         return
-    w = dict(synth.WORKLOADS[WORKLOAD])
-    inp = synth.workload_inputs(WORKLOAD)
-    c = synth.as_dtype(inp, "bf16", "mamba")
+    w = dict(synth.WORKLOADS[args.workload])
+    w.setdefault("M", 1)
+    inp = synth.workload_inputs(args.workload)
+    raw = w["form"] == "raw"
+    c = synth.as_dtype(inp, "bf16", "raw" if raw else "mamba")
 
     def dt_(a, dtype=torch.float32):
         return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(dtype).to(dev).contiguous()
 
     bf = torch.bfloat16
-    x, dy, B, C = dt_(c["x"], bf), dt_(c["dy"], bf), dt_(c["B"], bf), dt_(c["C"], bf)
-    dt, A, s0, dsf = dt_(c["dt"]), dt_(c["A"]), dt_(c["s0"]), dt_(c["ds_final"])
-    call = binding.SsdCall(x, dt, A, B, C, s0, dy, dsf, chunk_len=w["L"])
+    if raw:  # pre-scaled (v, da) form: no A
+        xv, dy, B, C = dt_(c["v"], bf), dt_(c["dy"], bf), dt_(c["B"], bf), dt_(c["C"], bf)
+        dtda, A = dt_(c["da"]), None
+    else:
+        xv, dy, B, C = dt_(c["x"], bf), dt_(c["dy"], bf), dt_(c["B"], bf), dt_(c["C"], bf)
+        dtda, A = dt_(c["dt"]), dt_(c["A"])
+    s0, dsf = dt_(c["s0"]), dt_(c["ds_final"])
+    call = binding.SsdCall(xv, dtda, A, B, C, s0, dy, dsf, chunk_len=w["L"])
+    del inp
+    grads_kernel = "ssd_blocked_bwd_kernel" if w["L"] * w["M"] > 64 else "ssd_chunk_bwd_kernel"
 
     for _ in range(args.warmup):
         call.states()
@@ -166,7 +181,7 @@ def main():
     phases = {
         "state_scans": {"kernel": "ssd_state_scan_kernel", "ms": scans_ms, "bytes": ab["state_scans"],
                         "GBps": ab["state_scans"] / (scans_ms * 1e6)},
-        "chunk_grads": {"kernel": "ssd_chunk_bwd_kernel", "ms": grads_ms, "bytes": ab["chunk_grads"],
+        "chunk_grads": {"kernel": grads_kernel, "ms": grads_ms, "bytes": ab["chunk_grads"],
                         "GBps": ab["chunk_grads"] / (grads_ms * 1e6)},
     }
     dom_name = max(phases, key=lambda k: phases[k]["ms"])
@@ -180,8 +195,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": w["b"], "seqlen": w["T"], "heads": w["H"], "headdim": w["P"],
-                   "dstate": w["N"], "ngroups": w["G"], "chunk_len": w["L"], "accumulate": "fp32"},
+        "config": {"workload": args.workload, "batch": w["b"], "seqlen": w["T"], "heads": w["H"], "headdim": w["P"],
+                   "dstate": w["N"], "ngroups": w["G"], "chunk_len": w["L"], "mimo_rank": w["M"],
+                   "form": w["form"], "accumulate": "fp32"},
         "roofline": roofline,
         "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                    for k, v in phases.items()},
