@@ -112,118 +112,166 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
   const int col = blk * BK_R + 16 * w + r16;
   const int l_col = col / M;
 
+  // ---- register prefetch of one block pair's staged rows: 64 rows of a B or C
+  // tensor (N wide) and 64 rows of an x or dy tensor (P wide, one head).
+  // Branch-free range-checked loads, issued one block pair ahead. ----
+  constexpr int E16 = 16 / sizeof(T);
+  constexpr int MAXN = CN ? (BK_R * CN / E16 + BK_NTH - 1) / BK_NTH : BK_R * 128 / E16 / BK_NTH;
+  constexpr int MAXP = CP ? (BK_R * CP / E16 + BK_NTH - 1) / BK_NTH : BK_R * 128 / E16 / BK_NTH;
+  u32x4 pn[MAXN], pp[MAXP];
+  const int cpn = N / E16, cpp = P / E16;  // 16-byte chunks per row
+  auto issue = [&](const T* srcN, const T* srcP, int valid) {
+    const brsrc rn = make_rsrc(srcN, valid > 0 ? (unsigned)(((valid - 1) * bstr + N) * esz) : 0u);
+    const brsrc rp = make_rsrc(srcP, valid > 0 ? (unsigned)(((valid - 1) * xstr + P) * esz) : 0u);
+#pragma unroll
+    for (int it = 0; it < MAXN; ++it) {
+      const int idx = tid + it * BK_NTH, row = idx / cpn, cc = (idx % cpn) * E16;
+      pn[it] = bload16(rn, idx < BK_R * cpn ? (unsigned)((row * bstr + cc) * esz) : BUF_OOB);
+    }
+#pragma unroll
+    for (int it = 0; it < MAXP; ++it) {
+      const int idx = tid + it * BK_NTH, row = idx / cpp, cc = (idx % cpp) * E16;
+      pp[it] = bload16(rp, idx < BK_R * cpp ? (unsigned)((row * xstr + cc) * esz) : BUF_OOB);
+    }
+  };
+  auto commit = [&](T* dstN, T* dstP) {
+#pragma unroll
+    for (int it = 0; it < MAXN; ++it) {
+      const int idx = tid + it * BK_NTH;
+      if (idx < BK_R * cpn) *(u32x4*)(dstN + (idx / cpn) * LDN + (idx % cpn) * E16) = pn[it];
+    }
+#pragma unroll
+    for (int it = 0; it < MAXP; ++it) {
+      const int idx = tid + it * BK_NTH;
+      if (idx < BK_R * cpp) *(u32x4*)(dstP + (idx / cpp) * LDP + (idx % cpp) * E16) = pp[it];
+    }
+  };
+
   if (role == 0) {
     // ======================= source block s = blk =========================
+    // steps: (head hh, target block tb) for tb = blk .. nblk-1, heads in order
+    const int nT = nblk - blk;
+    const i64 nsteps = a.hpg * nT;
+    auto issue_step = [&](i64 k) {
+      const i64 h = g * a.hpg + k / nT;
+      const int tb = blk + (int)(k % nT);
+      issue(Cg + (i64)tb * BK_R * bstr, (const T*)a.dy + xrow0 + (i64)tb * BK_R * xstr + h * P, valid_in(tb));
+    };
     f32x4 dBT[BK_TMAX];  // dB^T tiles (rows n, columns s), summed over the group's heads
 #pragma unroll
     for (int i = 0; i < BK_TMAX; ++i) dBT[i] = zero4();
+    f32x4 dvT[BK_TMAX];  // d_v^T tiles (rows p, columns s) of the current head
+    float s1 = 0.0f, ocol = 0.0f, cum_s = 0.0f, delta_s = 0.0f;
+    ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
     bk_stage_rows(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
-    for (i64 hh = 0; hh < a.hpg; ++hh) {
-      const i64 h = g * a.hpg + hh;
-      const ChunkScalars cs = scalars(h);
-      const float cum_s = __shfl(cs.cum, l_col & 63, 64), delta_s = __shfl(cs.delta, l_col & 63, 64);
-      const float edec = exp_hw(cs.end - cum_s), xcol = delta_s * edec;
-      __syncthreads();  // the previous head is done with xs / STs / Cs / dys
-      bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-      bk_stage_state(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
-      __syncthreads();
-
-      // ---- K3: d_dv^T = dS_{c+1}.B^T (rows p, columns s); dB_k3^T += dS^T . (xcol v)^T ----
-      f32x4 dvT[BK_TMAX];
-      float s1 = 0.0f;
-#pragma unroll
-      for (int pt = 0; pt < BK_TMAX; ++pt) {
-        dvT[pt] = zero4();
-        if (pt >= PT) continue;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < NT; ++kb)
-          mma(acc, ld_ntv_t(STs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
-        float xv[4];
-        frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);  // x[s][p .. p+3], p = 16 pt + 4q
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          s1 += acc[j] * xv[j];  // d_decay / delta = sum_p d_dv . x
-          dvT[pt][j] = acc[j] * edec;
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < BK_TMAX; ++nt) {
-        if (nt >= NT) continue;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < PT; ++kb)
-          mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dBT[nt][j] += acc[j] * xcol;
-      }
-
-      // ---- ORANGE and K2 over the target blocks t >= s ----
-      float ocol = 0.0f;
-      for (int tb = blk; tb < nblk; ++tb) {
-        __syncthreads();  // the previous target block is done with Cs / dys
-        bk_stage_rows(Cs, LDN, Cg + (i64)tb * BK_R * bstr, bstr, N, valid_in(tb), tid);
-        bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)tb * BK_R * xstr + h * P, xstr, P, valid_in(tb), tid);
+    issue_step(0);
+    for (i64 k = 0; k < nsteps; ++k) {
+      const i64 hh = k / nT, h = g * a.hpg + hh;
+      const int tb = blk + (int)(k % nT);
+      if (tb == blk) {
+        // ---- a new head: its scalars, x / v rows and dS_{c+1}; then the K3 backward ----
+        cs = scalars(h);
+        cum_s = __shfl(cs.cum, l_col & 63, 64);
+        delta_s = __shfl(cs.delta, l_col & 63, 64);
+        const float edec = exp_hw(cs.end - cum_s), xcol = delta_s * edec;
+        __syncthreads();  // the previous head is done with xs / STs
+        bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+        bk_stage_state(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
         __syncthreads();
-        Frag<T> wf[4], df[4];  // w and d_cb tiles (rows t, columns s): operands with k = t
+        // K3: d_dv^T = dS_{c+1}.B^T (rows p, columns s); dB_k3^T += dS^T . (xcol v)^T
+        s1 = 0.0f;
+        ocol = 0.0f;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          f32x4 cb = zero4(), g1 = zero4();
+        for (int pt = 0; pt < BK_TMAX; ++pt) {
+          dvT[pt] = zero4();
+          if (pt >= PT) continue;
+          f32x4 acc = zero4();
           for (int kb = 0; kb < NT; ++kb)
-            mma(cb, ld_colk(Cs, LDN, 16 * tt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
-          for (int kb = 0; kb < PT; ++kb)
-            mma(g1, ld_colk(dys, LDP, 16 * tt, 16 * kb, lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
-          float wv[4], dv[4];
+            mma(acc, ld_ntv_t(STs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+          float xv[4];
+          frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);  // x[s][p .. p+3], p = 16 pt + 4q
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int lt = (tb * BK_R + 16 * tt + 4 * q + j) / M;
-            const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
-            const float dec = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
-            const float dcb = g1[j] * delta_s * dec;  // d_w = dy.v^T with v = delta x (delta = 1 for RAW)
-            ocol += dcb * cb[j];
-            wv[j] = cb[j] * dec;
-            dv[j] = dcb;
+            s1 += acc[j] * xv[j];  // d_decay / delta = sum_p d_dv . x
+            dvT[pt][j] = acc[j] * edec;
           }
-          wf[tt] = frag_make<T>(wv);
-          df[tt] = frag_make<T>(dv);
         }
 #pragma unroll
-        for (int pt = 0; pt < BK_TMAX; ++pt) {  // d_v_or^T += dy^T . w
-          if (pt >= PT) continue;
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) mma(dvT[pt], ld_rowk(dys, LDP, 16 * tt, 16 * pt, lane), wf[tt]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < BK_TMAX; ++nt) {  // dB_k2^T += C^T . d_cb
+        for (int nt = 0; nt < BK_TMAX; ++nt) {
           if (nt >= NT) continue;
+          f32x4 acc = zero4();
+          for (int kb = 0; kb < PT; ++kb)
+            mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], ld_rowk(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
+          for (int j = 0; j < 4; ++j) dBT[nt][j] += acc[j] * xcol;
         }
       }
 
-      // ---- per-head outputs: dx (= d_v, times delta for Mamba-2), the column sums ----
-      float dvx = 0.0f;
-      const brsrc rdx = make_rsrc((T*)a.dxv + xrow0 + (i64)blk * BK_R * xstr + h * P,
-                                  valid_in(blk) > 0 ? (unsigned)(((valid_in(blk) - 1) * xstr + P) * esz) : 0u);
+      // ---- ORANGE and K2 for the pair (t block tb, s block blk) ----
+      __syncthreads();  // the previous pair is done with Cs / dys
+      commit(Cs, dys);
+      issue_step(k + 1 < nsteps ? k + 1 : k);  // unconditional: the last step reloads its own rows
+      __syncthreads();
+      Frag<T> wf[4], df[4];  // w and d_cb tiles (rows t, columns s): operands with k = t
 #pragma unroll
-      for (int pt = 0; pt < BK_TMAX; ++pt) {
-        if (pt >= PT) continue;
-        float xv[4];
-        frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);
-        f32x4 o;
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 cb = zero4(), g1 = zero4();
+        for (int kb = 0; kb < NT; ++kb)
+          mma(cb, ld_colk(Cs, LDN, 16 * tt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+        for (int kb = 0; kb < PT; ++kb)
+          mma(g1, ld_colk(dys, LDP, 16 * tt, 16 * kb, lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
+        float wv[4], dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          dvx += dvT[pt][j] * xv[j];
-          o[j] = a.raw ? dvT[pt][j] : dvT[pt][j] * delta_s;
+          const int lt = (tb * BK_R + 16 * tt + 4 * q + j) / M;
+          const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
+          const float dec = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
+          const float dcb = g1[j] * delta_s * dec;  // d_w = dy.v^T with v = delta x (delta = 1 for RAW)
+          ocol += dcb * cb[j];
+          wv[j] = cb[j] * dec;
+          dv[j] = dcb;
         }
-        bstore4(rdx, (unsigned)(((16 * w + r16) * xstr + 16 * pt + 4 * q) * esz), o, (const T*)0);
+        wf[tt] = frag_make<T>(wv);
+        df[tt] = frag_make<T>(dv);
       }
-      s1 = sum4q(s1) * delta_s;
-      ocol = sum4q(ocol);
-      dvx = sum4q(dvx);
-      float* rv = rowv_c + h * RV_N * LM;
-      if (q == 0) {
-        rv[RV_DEC * LM + col] = s1;
-        rv[RV_OCOL * LM + col] = ocol;
-        rv[RV_DVX * LM + col] = dvx;
+#pragma unroll
+      for (int pt = 0; pt < BK_TMAX; ++pt) {  // d_v_or^T += dy^T . w
+        if (pt >= PT) continue;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) mma(dvT[pt], ld_rowk(dys, LDP, 16 * tt, 16 * pt, lane), wf[tt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < BK_TMAX; ++nt) {  // dB_k2^T += C^T . d_cb
+        if (nt >= NT) continue;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], ld_rowk(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
+      }
+
+      if (tb == nblk - 1) {
+        // ---- the head's outputs: dx (= d_v, times delta for Mamba-2), the column sums ----
+        float dvx = 0.0f;
+        const brsrc rdx = make_rsrc((T*)a.dxv + xrow0 + (i64)blk * BK_R * xstr + h * P,
+                                    valid_in(blk) > 0 ? (unsigned)(((valid_in(blk) - 1) * xstr + P) * esz) : 0u);
+#pragma unroll
+        for (int pt = 0; pt < BK_TMAX; ++pt) {
+          if (pt >= PT) continue;
+          float xv[4];
+          frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);
+          f32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dvx += dvT[pt][j] * xv[j];
+            o[j] = a.raw ? dvT[pt][j] : dvT[pt][j] * delta_s;
+          }
+          bstore4(rdx, (unsigned)(((16 * w + r16) * xstr + 16 * pt + 4 * q) * esz), o, (const T*)0);
+        }
+        const float s1w = sum4q(s1) * delta_s, ocw = sum4q(ocol), dvxw = sum4q(dvx);
+        float* rv = rowv_c + h * RV_N * LM;
+        if (q == 0) {
+          rv[RV_DEC * LM + col] = s1w;
+          rv[RV_OCOL * LM + col] = ocw;
+          rv[RV_DVX * LM + col] = dvxw;
+        }
       }
     }
     // dB (rows s, 4 consecutive n per lane), summed over the group's heads
@@ -236,108 +284,118 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
     }
   } else {
     // ======================= target block t = blk =========================
+    // steps: (head hh, source block sb) for sb = 0 .. blk, heads in order
+    const int nS = blk + 1;
+    const i64 nsteps = a.hpg * nS;
+    auto issue_step = [&](i64 k) {
+      const i64 h = g * a.hpg + k / nS;
+      const int sb = (int)(k % nS);
+      issue(Bg + (i64)sb * BK_R * bstr, (const T*)a.xv + xrow0 + (i64)sb * BK_R * xstr + h * P, valid_in(sb));
+    };
     f32x4 dCT[BK_TMAX];  // dC^T tiles (rows n, columns t), summed over the group's heads
 #pragma unroll
     for (int i = 0; i < BK_TMAX; ++i) dCT[i] = zero4();
+    float blue = 0.0f, orow = 0.0f, cum_t = 0.0f;
+    ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
     bk_stage_rows(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
-    for (i64 hh = 0; hh < a.hpg; ++hh) {
-      const i64 h = g * a.hpg + hh;
-      const ChunkScalars cs = scalars(h);
-      const float cum_t = __shfl(cs.cum, l_col & 63, 64);
-      const float ecol = exp_hw(cum_t);
-      __syncthreads();  // the previous head is done with dys / STs / Bs / xs
-      bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-      const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
-      bk_stage_state(STs, Sg, PN, tid);
-      __syncthreads();
-
-      // ---- d_end = sum_{p,n} S_c * dS_{c+1} (once per chunk and head) ----
-      if (blk == 0) {
-        constexpr int E16 = 16 / sizeof(T);
-        const brsrc rdS = make_rsrc((const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, (unsigned)PN * esz);
-        float part = 0.0f;
-        for (int idx = tid; idx < PN / E16; idx += BK_NTH) {
-          const u32x4 u = bload16(rdS, (unsigned)idx * 16u);
-          const u32x4 v = *(const u32x4*)(STs + idx * E16);
+    issue_step(0);
+    for (i64 k = 0; k < nsteps; ++k) {
+      const i64 hh = k / nS, h = g * a.hpg + hh;
+      const int sb = (int)(k % nS);
+      if (sb == 0) {
+        // ---- a new head: its scalars, dy rows and S_c; d_end; BLUE ----
+        cs = scalars(h);
+        cum_t = __shfl(cs.cum, l_col & 63, 64);
+        const float ecol = exp_hw(cum_t);
+        __syncthreads();  // the previous head is done with dys / STs
+        bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+        bk_stage_state(STs, (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+        __syncthreads();
+        if (blk == 0) {  // d_end = sum_{p,n} S_c * dS_{c+1}, once per chunk and head
+          const brsrc rdS = make_rsrc((const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, (unsigned)PN * esz);
+          float part = 0.0f;
+          for (int idx = tid; idx < PN / E16; idx += BK_NTH) {
+            const u32x4 u = bload16(rdS, (unsigned)idx * 16u);
+            const u32x4 v = *(const u32x4*)(STs + idx * E16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (BF) {
-              part += __uint_as_float(u[e] << 16) * __uint_as_float(v[e] << 16);
-              part += __uint_as_float(u[e] & 0xffff0000u) * __uint_as_float(v[e] & 0xffff0000u);
-            } else {
-              part += __uint_as_float(u[e]) * __uint_as_float(v[e]);
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (BF) {
+                part += __uint_as_float(u[e] << 16) * __uint_as_float(v[e] << 16);
+                part += __uint_as_float(u[e] & 0xffff0000u) * __uint_as_float(v[e] & 0xffff0000u);
+              } else {
+                part += __uint_as_float(u[e]) * __uint_as_float(v[e]);
+              }
             }
           }
+          part = wave_sum(part);
+          if (lane == 0) red[w] = part;
+          __syncthreads();
+          if (tid == 0) {
+            float sum = 0.0f;
+            for (int kw = 0; kw < BK_NW; ++kw) sum += red[kw];
+            a.dend[(bi * a.nc + c) * a.H + h] = sum;
+          }
         }
-        part = wave_sum(part);
-        if (lane == 0) red[w] = part;
-        __syncthreads();
-        if (tid == 0) {
-          float s = 0.0f;
-          for (int k = 0; k < BK_NW; ++k) s += red[k];
-          a.dend[(bi * a.nc + c) * a.H + h] = s;
-        }
-      }
-
-      // ---- BLUE: dC_blue^T = S_c^T . (dy * exp(cumA))^T ; its row sums against C ----
-      float blue = 0.0f;
+        // BLUE: dC_blue^T = S_c^T . (dy * exp(cumA))^T ; its row sums against C
+        blue = 0.0f;
+        orow = 0.0f;
 #pragma unroll
-      for (int nt = 0; nt < BK_TMAX; ++nt) {
-        if (nt >= NT) continue;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < PT; ++kb)  // A: rows n, k = p (native tile); B: k = p, columns t
-          mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
-        float cv[4];
-        frag_get(ld_colk(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float val = acc[j] * ecol;
-          dCT[nt][j] += val;
-          blue += cv[j] * val;
-        }
-      }
-
-      // ---- ORANGE row sums and K2 over the source blocks s <= t (transposed tiles) ----
-      float orow = 0.0f;
-      for (int sb = 0; sb <= blk; ++sb) {
-        __syncthreads();  // the previous source block is done with Bs / xs
-        bk_stage_rows(Bs, LDN, Bg + (i64)sb * BK_R * bstr, bstr, N, valid_in(sb), tid);
-        bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)sb * BK_R * xstr + h * P, xstr, P, valid_in(sb), tid);
-        __syncthreads();
-        Frag<T> df[4];  // d_cb^T tiles (rows s, columns t): operands with k = s
-#pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-          f32x4 cb = zero4(), g1 = zero4();
-          for (int kb = 0; kb < NT; ++kb)
-            mma(cb, ld_colk(Bs, LDN, 16 * ss, 16 * kb, lane), ld_colk(Cs, LDN, 16 * w, 16 * kb, lane));
-          for (int kb = 0; kb < PT; ++kb)
-            mma(g1, ld_colk(xs, LDP, 16 * ss, 16 * kb, lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
-          float dv[4];
+        for (int nt = 0; nt < BK_TMAX; ++nt) {
+          if (nt >= NT) continue;
+          f32x4 acc = zero4();
+          for (int kb = 0; kb < PT; ++kb)  // A: rows n, k = p (native tile); B: k = p, columns t
+            mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+          float cv[4];
+          frag_get(ld_colk(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int ls = (sb * BK_R + 16 * ss + 4 * q + j) / M;
-            const float cs_s = __shfl(cs.cum, ls & 63, 64);  // every lane takes part in the shuffles
-            const float d_s = __shfl(cs.delta, ls & 63, 64);
-            const float dec = (ls <= l_col && l_col < Lc) ? exp_hw(cum_t - cs_s) : 0.0f;
-            const float dcb = g1[j] * d_s * dec;
-            orow += dcb * cb[j];
-            dv[j] = dcb;
+            const float val = acc[j] * ecol;
+            dCT[nt][j] += val;
+            blue += cv[j] * val;
           }
-          df[ss] = frag_make<T>(dv);
-        }
-#pragma unroll
-        for (int nt = 0; nt < BK_TMAX; ++nt) {  // dC_k2^T += B^T . d_cb^T
-          if (nt >= NT) continue;
-#pragma unroll
-          for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], ld_rowk(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
         }
       }
-      blue = sum4q(blue);
-      orow = sum4q(orow);
-      float* rv = rowv_c + h * RV_N * LM;
-      if (q == 0) {
-        rv[RV_BLUE * LM + col] = blue;
-        rv[RV_OROW * LM + col] = orow;
+
+      // ---- ORANGE row sums and K2 for the pair (t block blk, s block sb), transposed tiles ----
+      __syncthreads();  // the previous pair is done with Bs / xs
+      commit(Bs, xs);
+      issue_step(k + 1 < nsteps ? k + 1 : k);  // unconditional: the last step reloads its own rows
+      __syncthreads();
+      Frag<T> df[4];  // d_cb^T tiles (rows s, columns t): operands with k = s
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+        f32x4 cb = zero4(), g1 = zero4();
+        for (int kb = 0; kb < NT; ++kb)
+          mma(cb, ld_colk(Bs, LDN, 16 * ss, 16 * kb, lane), ld_colk(Cs, LDN, 16 * w, 16 * kb, lane));
+        for (int kb = 0; kb < PT; ++kb)
+          mma(g1, ld_colk(xs, LDP, 16 * ss, 16 * kb, lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+        float dv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ls = (sb * BK_R + 16 * ss + 4 * q + j) / M;
+          const float cs_s = __shfl(cs.cum, ls & 63, 64);  // every lane takes part in the shuffles
+          const float d_s = __shfl(cs.delta, ls & 63, 64);
+          const float dec = (ls <= l_col && l_col < Lc) ? exp_hw(cum_t - cs_s) : 0.0f;
+          const float dcb = g1[j] * d_s * dec;
+          orow += dcb * cb[j];
+          dv[j] = dcb;
+        }
+        df[ss] = frag_make<T>(dv);
+      }
+#pragma unroll
+      for (int nt = 0; nt < BK_TMAX; ++nt) {  // dC_k2^T += B^T . d_cb^T
+        if (nt >= NT) continue;
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], ld_rowk(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
+      }
+
+      if (sb == blk) {  // the head's row sums
+        const float bw = sum4q(blue), ow = sum4q(orow);
+        float* rv = rowv_c + h * RV_N * LM;
+        if (q == 0) {
+          rv[RV_BLUE * LM + col] = bw;
+          rv[RV_OROW * LM + col] = ow;
+        }
       }
     }
     // dC (rows t, 4 consecutive n per lane), summed over the group's heads
