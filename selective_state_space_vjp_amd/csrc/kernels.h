@@ -48,6 +48,7 @@ struct SsdPlan {
   int64_t state_elem;  // bytes per stored state element (2 for bf16, 4 for f32)
   int64_t off_S, off_dS, off_part;
   int64_t off_rowv, off_dend;  // row-blocked path (L*M > 64): per-row partial sums, d_end
+  int64_t off_csv;             // per-chunk step scalars (cumA, delta, sigmoid(dt))
   size_t bytes;
 };
 

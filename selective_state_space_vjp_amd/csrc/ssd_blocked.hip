@@ -100,12 +100,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
   const T* Bg = (const T*)a.B + ix_bc(a, bi, t0, 0, g, 0);
   const T* Cg = (const T*)a.C + ix_bc(a, bi, t0, 0, g, 0);
   const i64 xrow0 = ix_xv(a, bi, t0, 0, 0, 0);  // x / dy / dx offset of fused row 0, head 0
-  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
-  const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));
-  auto scalars = [&](i64 h) {
-    const float z = bload_f32(make_rsrc(dtg + h, (unsigned)(((Lc - 1) * a.H + 1) * 4)), (unsigned)(lane * a.H * 4));
-    return chunk_scalars(a, z, lane < Lc, bload_f32(rsA, (unsigned)(h * 4)), lane);
-  };
+  auto scalars = [&](i64 h) { return load_scalars(a, bi, c, h, lane); };
   float* rowv_c = a.rowv + (bi * a.nc + c) * a.H * RV_N * LM;
   auto tile_off = [&](int pt, int nt) { return (pt * NT + nt) * 256; };
   // this lane's column: fused row blk*64 + 16w + r16 of the wave's tile
@@ -420,10 +415,8 @@ __global__ void __launch_bounds__(64) ssd_blocked_epilogue_kernel(SsdArgs a) {
   const int L = (int)a.L, M = (int)a.M, LM = (int)a.LM;
   const i64 t0 = c * L;
   const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
-  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
-  const float z = bload_f32(make_rsrc(dtg + h, (unsigned)(((Lc - 1) * a.H + 1) * 4)), (unsigned)(lane * a.H * 4));
   const float Ah = a.raw ? 0.0f : a.A[h];
-  const ChunkScalars cs = chunk_scalars(a, z, lane < Lc, Ah, lane);
+  const ChunkScalars cs = load_scalars(a, bi, c, h, lane);
   const float* rv = a.rowv + ((bi * a.nc + c) * a.H + h) * RV_N * LM;
   float dcl = 0.0f, dvxl = 0.0f, qv = 0.0f;
   if (lane < Lc) {

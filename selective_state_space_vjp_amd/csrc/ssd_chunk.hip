@@ -39,6 +39,28 @@
 namespace ssmvjp {
 
 // ===========================================================================
+// kernel 0: the per-chunk step scalars (K1 cumsum, delta, sigmoid(dt)), one
+// wave per (batch, chunk, head), stored for the scan and gradient kernels
+// ===========================================================================
+__global__ void __launch_bounds__(256) ssd_chunk_scalars_kernel(SsdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const i64 id = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (id >= a.b * a.nc * a.H) return;  // whole waves
+  const i64 h = id % a.H, c = (id / a.H) % a.nc, bi = id / (a.H * a.nc);
+  const int L = (int)a.L;
+  const i64 t0 = c * L;
+  const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
+  const float z = bload_f32(make_rsrc(a.dtda + (bi * a.T + t0) * a.H + h, (unsigned)(((Lc - 1) * a.H + 1) * 4)),
+                            (unsigned)(lane * a.H * 4));
+  const float Ah = a.raw ? 0.0f : a.A[h];
+  const ChunkScalars cs = chunk_scalars(a, z, lane < Lc, Ah, lane);
+  float* o = a.csv + id * 3 * 64;
+  o[lane] = cs.cum;
+  o[64 + lane] = cs.delta;
+  o[128 + lane] = cs.sig;
+}
+
+// ===========================================================================
 // kernel 1: forward and reverse state scans over chunks
 // ===========================================================================
 constexpr int SCAN_NW = 8;                   // waves per workgroup
@@ -112,12 +134,11 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   // register prefetch of one step: the chunk's step values, operand rows, B/C rows.
   // Branch-free buffer loads: rows past the end of the sequence read zeros.
   struct Pre {
-    float z;
+    float cum, delta;  // the chunk's step scalars (this lane's step)
     u32x4 o[MAXC], b[MAXC];
   };
   const int oc_row = P / E16, bc_row = NB / E16;
   const unsigned esz = sizeof(T);
-  const float Ah = a.raw ? 0.0f : a.A[h];
   const i64 nsteps = a.nc * NSUB;
   auto chunk_of = [&](i64 step) { const i64 ci = step / NSUB; return dir == 0 ? ci : a.nc - 1 - ci; };
   auto issue = [&](Pre& pr, i64 step) {
@@ -126,8 +147,9 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
     const i64 t0 = c * L;
     const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
     const int rows = Lc * M - R0;  // valid fused rows of this step (may be <= 0)
-    const brsrc rz = make_rsrc(a.dtda + (bi * a.T + t0) * a.H + h, (unsigned)(((Lc - 1) * a.H + 1) * 4));
-    pr.z = bload_f32(rz, (unsigned)(lane * a.H * 4));
+    const brsrc rcs = make_rsrc(csv_at(a, bi, c, h), 3 * 64 * 4);
+    pr.cum = bload_f32(rcs, (unsigned)lane * 4u);
+    pr.delta = bload_f32(rcs, (unsigned)(64 + lane) * 4u);
     const brsrc ro = make_rsrc(op + ix_xv(a, bi, t0, 0, h, 0) + (i64)R0 * a.H * P,
                                rows > 0 ? (unsigned)(((rows - 1) * a.H * P + P) * esz) : 0u);
     const brsrc rb = make_rsrc(bc + ix_bc(a, bi, t0, 0, g, n0) + (i64)R0 * a.G * a.N,
@@ -152,10 +174,9 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
     const int ks = (int)(step % NSUB);
     const bool last = ks == NSUB - 1;
     if (ks == 0) {
-      const int Lc = (int)((a.T - c * L) < L ? (a.T - c * L) : L);
-      const ChunkScalars cs = chunk_scalars(a, pr.z, lane < Lc, Ah, lane);
-      sc = dir == 0 ? cs.delta * exp_hw(cs.end - cs.cum) : exp_hw(cs.cum);
-      e_end = exp_hw(cs.end);
+      const float end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr.cum), 63));
+      sc = dir == 0 ? pr.delta * exp_hw(end - pr.cum) : exp_hw(pr.cum);
+      e_end = exp_hw(end);
     }
     T* opS = sb;
     T* bcS = sb + SB * PPO;
@@ -291,7 +312,6 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   T* dxg = (T*)a.dxv + xoff0;
   const T* Bg = (const T*)a.B + boff0;
   const T* Cg = (const T*)a.C + boff0;
-  const float* dtg = a.dtda + (bi * a.T + t0) * a.H;
   float* ddtg = a.d_dtda + (bi * a.T + t0) * a.H;
   const int xrow = P / E16, nrow = N / E16, PN = P * N;
   auto tile_off = [&](int pt, int nt) { return (pt * NT + nt) * 256; };
@@ -313,14 +333,14 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   // Branch-free buffer loads (rows past the end of the sequence read zeros), so
   // that the next head's loads stay in flight across this head's work.
   u32x4 rx[MAXX], ry[MAXX], rs[MAXS], rd[MAXS];
-  float rz = 0.0f, rA = 0.0f;
+  ChunkScalars rcs = {0.f, 0.f, 0.f, 0.f};  // the head's stored step scalars
+  float rA = 0.0f;
   const i64 hbase = g * a.hpg + hs * a.hph;
   const unsigned esz = sizeof(T);
   const unsigned xbytes = (unsigned)(((i64)(Lc * M - 1) * xrs + P) * esz);  // valid rows of one head
-  const unsigned zbytes = (unsigned)(((Lc - 1) * a.H + 1) * 4);
   const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));      // RAW: no A, reads zero
   auto issue = [&](i64 h) {
-    rz = bload_f32(make_rsrc(dtg + h, zbytes), (unsigned)(lane * a.H * 4));
+    rcs = issue_scalars(a, bi, c, h, lane);
     rA = bload_f32(rsA, (unsigned)(h * 4));
     const brsrc bx = make_rsrc(xg + (int)h * P, xbytes), by = make_rsrc(dyg + (int)h * P, xbytes);
 #pragma unroll
@@ -432,7 +452,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     const i64 h = hbase + hh;
     if (!BF) issue(h);
     float* pb = pbase + (BF ? (hh & 1) * PB_N * 8 * 64 : 0);
-    const ChunkScalars cs = chunk_scalars(a, rz, lane < Lc, rA, lane);
+    const ChunkScalars cs = finish_scalars(rcs);
     const float Ah = rA;
     const brsrc bdx = make_rsrc(dxg + (int)h * P, xbytes);
     // lane shuffles: call them where every lane of the wave is active (a
@@ -772,6 +792,7 @@ SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
   const bool blocked = p.LM > SCAN_SB;
   p.off_rowv = carve(blocked ? d.batch * p.nc * d.nheads * RV_N * p.LM * 4 : 0);
   p.off_dend = carve(blocked ? d.batch * p.nc * d.nheads * 4 : 0);
+  p.off_csv = carve(d.batch * p.nc * d.nheads * 3 * 64 * 4);
   p.bytes = (size_t)off;
   return p;
 }
@@ -791,6 +812,7 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
   a.part = (float*)(ws + plan.off_part);
   a.rowv = (float*)(ws + plan.off_rowv);
   a.dend = (float*)(ws + plan.off_dend);
+  a.csv = (float*)(ws + plan.off_csv);
   return a;
 }
 
@@ -817,6 +839,9 @@ static bool mimo_shape(const SsdArgs& a) { return a.P == 64 && a.N == 128 && a.L
 
 template <typename T>
 static void launch_states_t(const SsdArgs& a, hipStream_t stream, int NB) {
+  const i64 nw = a.b * a.nc * a.H;  // one wave per (batch, chunk, head)
+  if (nw > 0)
+    hipLaunchKernelGGL(ssd_chunk_scalars_kernel, dim3((unsigned)cdiv(nw, 4)), dim3(256), 0, stream, a);
   const i64 grid1 = a.b * a.H * 2 * (a.N / NB);
   if (workload_shape(a) && NB == 128)
     hipLaunchKernelGGL((ssd_state_scan_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid1), dim3(SCAN_NTH),

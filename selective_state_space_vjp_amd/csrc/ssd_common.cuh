@@ -29,6 +29,7 @@ struct SsdArgs {
   void* S;      // [b][nc][H][P*N] chunk-input states, native tiles
   void* dS;     // [b][nc][H][P*N] dS_{c+1}, native tiles
   float* part;  // [2][hsplit][b*T*M*G*N] per-split dB / dC partials (hsplit > 1)
+  float* csv;   // [b][nc][H][3][64] per-chunk step scalars: cumA, delta, sigmoid(dt) (see ssd_chunk_scalars_kernel)
   // row-blocked path (L*M > 64) only:
   float* rowv;  // [b][nc][H][RV_N][LM] per-row partial sums of d_cumA terms
   float* dend;  // [b][nc][H] sum over (p, n) of S_c * dS_{c+1}
@@ -121,6 +122,30 @@ __device__ __forceinline__ ChunkScalars chunk_scalars(const SsdArgs& a, float z,
   return s;
 }
 
+
+// The step scalars of chunk c, head h as stored by ssd_chunk_scalars_kernel,
+// one lane per step (lanes past the chunk's end hold zero delta and a flat
+// cumsum); `end` is the cumsum at the chunk's last step.
+__device__ __forceinline__ const float* csv_at(const SsdArgs& a, i64 bi, i64 c, i64 h) {
+  return a.csv + ((bi * a.nc + c) * a.H + h) * 3 * 64;
+}
+// issue the loads (end not set yet: finish_scalars, once the loads are needed)
+__device__ __forceinline__ ChunkScalars issue_scalars(const SsdArgs& a, i64 bi, i64 c, i64 h, int lane) {
+  const brsrc r = make_rsrc(csv_at(a, bi, c, h), 3 * 64 * 4);
+  ChunkScalars s;
+  s.cum = bload_f32(r, (unsigned)lane * 4u);
+  s.delta = bload_f32(r, (unsigned)(64 + lane) * 4u);
+  s.sig = bload_f32(r, (unsigned)(128 + lane) * 4u);
+  s.end = 0.0f;
+  return s;
+}
+__device__ __forceinline__ ChunkScalars finish_scalars(ChunkScalars s) {
+  s.end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.cum), 63));
+  return s;
+}
+__device__ __forceinline__ ChunkScalars load_scalars(const SsdArgs& a, i64 bi, i64 c, i64 h, int lane) {
+  return finish_scalars(issue_scalars(a, bi, c, h, lane));
+}
 
 // row-blocked chunk backward (L*M > 64), defined in ssd_blocked.hip
 bool ssd_blocked_supported(const ssmvjp_ssd_desc& d);
