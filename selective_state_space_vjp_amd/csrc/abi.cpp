@@ -49,7 +49,7 @@ ssmvjp_status delta_check(const ssmvjp_delta_desc* d) {
   if (d->batch < 0 || d->seqlen < 0 || d->nqk_heads <= 0 || d->nv_heads <= 0 || d->dk <= 0 || d->dv <= 0)
     return SSMVJP_EINVAL;
   if (d->nv_heads % d->nqk_heads || d->reserved != 0) return SSMVJP_EINVAL;
-  if (d->dk > 256 || d->dv > 256) return SSMVJP_EUNSUPPORTED;
+  if (!delta_shape_supported(*d)) return SSMVJP_EUNSUPPORTED;
   return SSMVJP_OK;
 }
 
@@ -193,7 +193,7 @@ ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, cons
     return SSMVJP_EINVAL;
   const void* pf[] = {q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0};
   for (const void* p : pf)
-    if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
+    if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
   const DeltaPlan plan = delta_plan(d);
   if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
     return SSMVJP_EWORKSPACE;

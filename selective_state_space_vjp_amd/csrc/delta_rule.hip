@@ -1,9 +1,453 @@
-// placeholder until the delta-rule kernels land
+// delta_rule.hip -- backward of the KDA gated delta rule (K3 notes, section
+// "反向传播推导": forward F1..F6, BPTT steps 1..6 and the GVA view+sum).
+//
+// Per (batch b, value head hv) the forward keeps a [K x V] state S and, at
+// step t, with the key/query of qk head h = hv / (HV/H):
+//   S_dec = exp(g_t) (.) S_{t-1}     (one gate per key channel, F1)
+//   r     = v_t - k_t^T S_dec        (F2, F3)
+//   S_t   = S_dec + (beta_t k_t) (x) r     (F4, F5)
+//   o_t   = (scale q_t)^T S_t        (F6)
+// The backward walks t = T-1 .. 0 carrying dS (seeded with dS_final):
+//   dS += (scale q_t) (x) do_t ;  dq_e = S_t do_t                       (step 1)
+//   da  = dS r ;  dr = dS^T (beta_t k_t)                                (step 2)
+//   dbeta = k_t . da                                                    (step 3)
+//   dv = dr ;  dk_e = beta_t da - S_dec dr                              (step 4)
+//   dS -= k_t (x) dr   (the second path into dS_dec, summed with the first)
+//   dg  = rowsum(S_dec (.) dS) ;  dS = exp(g_t) (.) dS                  (step 5)
+//   dq = scale * sum of dq_e, dk = sum of dk_e over the value heads of a qk head  (step 6)
+//
+// MI355X organisation (three launches):
+//  * Columns of S are independent in the recurrence (r[v] and the update of
+//    column v read column v only), so V is cut into 32-column slices and every
+//    kernel runs one workgroup (4 waves) per (batch, value head, slice).  A
+//    thread owns a 4 x 4 block of its slice (rows 4kq..4kq+3, columns
+//    4vq..4vq+3); the 32 threads that share a column block sit in one half
+//    wave, so the per-column sums over k (k^T S_dec, dS^T a) are DPP row sums
+//    plus one permlane16 swap, with no LDS traffic and no barrier.
+//  * delta_fwd_ckpt_kernel walks the sequence forward and stores the state
+//    at the start of every NS-step sub-segment (the checkpoints).
+//  * delta_bwd_kernel walks the sub-segments in reverse: it recomputes the
+//    NS states of a sub-segment from its checkpoint into registers, then runs
+//    the NS backward steps.  dv is a per-column output and is stored
+//    directly.  The per-row outputs (dq_e, da, S_dec dr, dg: sums over v)
+//    never feed back into the recurrence; each thread folds its 4 columns,
+//    half waves are paired with one permlane32 swap, and the 4 waves are
+//    summed through LDS once per sub-segment into the slice's partial sums.
+//  * delta_reduce_kernel adds the slice partials in slice order, applies the
+//    GVA sum over the value heads of each qk head (ascending), and forms dq,
+//    dk, dg and dbeta.
+// The next sub-segment's inputs and checkpoint are loaded into registers while
+// the current one runs.  Everything is float32; every sum runs in a fixed
+// order, so results are bitwise reproducible.  No float atomics.
 #include "common.cuh"
 #include "kernels.h"
+
 namespace ssmvjp {
-DeltaPlan delta_plan(const ssmvjp_delta_desc& d) { DeltaPlan p{}; (void)d; return p; }
-hipError_t launch_delta_bwd(const ssmvjp_delta_desc&, const DeltaPlan&, const DeltaPointers&, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int DK = 128;          // key dimension: rows of the state
+constexpr int NW = 4;            // waves per workgroup
+constexpr int NTH = 64 * NW;
+constexpr int VS = 32;           // columns of the state per workgroup (8 column blocks of 4)
+constexpr int NS = 8;            // steps per sub-segment = checkpoint interval
+constexpr int NQ = 4;            // per-row outputs: dq_e, da, S_dec dr, dg
+
+struct DeltaArgs {
+  i64 b, T, H, HV, V, nvs, nck, grp;
+  float scale;
+  const float *q, *k, *v, *beta, *g, *S0, *d_o, *dSf;
+  float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+  float* ck;    // [b][HV][nvs][nck][4][NTH] float4: state at the start of each sub-segment
+  float* part;  // [b][T][HV][nvs][NQ][DK] per-slice partial sums of the per-row outputs
+};
+
+// sum over the 32 lanes of a half wave; every lane of the half wave gets the
+// same bits (the rotation tree and the pair swap add the same operands)
+__device__ __forceinline__ float sum32(float v) {
+  v = sum16(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
 }
+
+// lanes 0..31 get x[l] + x[l+32] of a, lanes 32..63 get the same sum of b
+__device__ __forceinline__ float pair_halves(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), false, false);
+  return __builtin_bit_cast(float, (int)s[0]) + __builtin_bit_cast(float, (int)s[1]);
+}
+
+__device__ __forceinline__ f32x4 as_f4(u32x4 u) {
+  return f32x4{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
+}
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *(const f32x4*)p; }
+
+// Workgroup -> (batch, qk head, value head, slice).  The value heads and
+// slices that read the same q/k rows get ids congruent modulo b*H, so they
+// land on the same XCD (ids are dealt to the 8 XCDs round robin) when b*H is
+// a multiple of 8 and share those rows in its L2.
+struct Slot {
+  i64 bi, h, hv, vs;
+};
+__device__ __forceinline__ Slot slot_of(const DeltaArgs& a) {
+  const i64 ngrp = a.b * a.H, id = blockIdx.x;
+  const i64 grp_id = id % ngrp, member = id / ngrp;
+  Slot s;
+  s.bi = grp_id / a.H;
+  s.h = grp_id % a.H;
+  s.hv = s.h * a.grp + member / a.nvs;
+  s.vs = member % a.nvs;
+  return s;
+}
+
+// One forward step on this thread's 4x4 block (S[4i+c]: row 4kq+i, column
+// 4vq+c): sd = exp(g) (.) S, r = v - k^T sd (column sums over the half wave),
+// S = sd + (beta k) (x) r.
+__device__ __forceinline__ void fwd_step(float S[16], float sd[16], f32x4 eg, f32x4 kk, float beta, f32x4 vv,
+                                         float r[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sd[4 * i + c] = eg[i] * S[4 * i + c];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float p = kk[0] * sd[c];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) p = fmaf(kk[i], sd[4 * i + c], p);
+    r[c] = vv[c] - sum32(p);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ai = beta * kk[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S[4 * i + c] = fmaf(ai, r[c], sd[4 * i + c]);
+  }
+}
+
+// byte size of the valid rows of one sub-segment in a [.., T, heads, width] tensor
+__device__ __forceinline__ unsigned seg_bytes(int ns, i64 row_stride, int width) {
+  return (unsigned)(((i64)(ns - 1) * row_stride + width) * 4);
+}
+
+// ===========================================================================
+// forward walk: checkpoints at the start of every sub-segment
+// ===========================================================================
+__global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
+  __shared__ __align__(16) float sk[NS][DK];
+  __shared__ __align__(16) float se[NS][DK];
+  __shared__ __align__(16) float sv[NS][VS];
+  __shared__ float sb[NS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kq = lane & 31, vq = 2 * w + (lane >> 5);
+  const Slot sl = slot_of(a);
+  const i64 T = a.T, V = a.V;
+
+  float S[16];
+  {
+    const brsrc r0 = make_rsrc(a.S0 ? a.S0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : a.dq,
+                               a.S0 ? (unsigned)(((DK - 1) * V + VS) * 4) : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x = as_f4(bload16(r0, (unsigned)(((4 * kq + i) * V + 4 * vq) * 4)));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[4 * i + c] = x[c];
+    }
+  }
+  // register prefetch of one sub-segment: k and g rows (one float4 each per
+  // thread), the slice of v (threads 0..63), beta (threads 0..NS-1)
+  u32x4 pk, pg, pv;
+  float pb;
+  const int srow = tid >> 5, scol = 4 * (tid & 31);
+  auto issue = [&](i64 j) {
+    const i64 t0 = j * NS;
+    const int ns = (int)(T - t0 < NS ? T - t0 : NS);
+    const brsrc rk = make_rsrc(a.k + ((sl.bi * T + t0) * a.H + sl.h) * DK, seg_bytes(ns, a.H * DK, DK));
+    const brsrc rg = make_rsrc(a.g + ((sl.bi * T + t0) * a.HV + sl.hv) * DK, seg_bytes(ns, a.HV * DK, DK));
+    const brsrc rv = make_rsrc(a.v + ((sl.bi * T + t0) * a.HV + sl.hv) * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
+    const brsrc rb = make_rsrc(a.beta + (sl.bi * T + t0) * a.HV + sl.hv, seg_bytes(ns, a.HV, 1));
+    pk = bload16(rk, (unsigned)((srow * a.H * DK + scol) * 4));
+    pg = bload16(rg, (unsigned)((srow * a.HV * DK + scol) * 4));
+    pv = bload16(rv, tid < NS * VS / 4 ? (unsigned)(((tid >> 3) * a.HV * V + 4 * (tid & 7)) * 4) : BUF_OOB);
+    pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
+  };
+  float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (4 * NTH * 4);
+  if (a.nck > 0) issue(0);
+  for (i64 j = 0; j < a.nck; ++j) {
+    const int ns = (int)(T - j * NS < NS ? T - j * NS : NS);
+    // checkpoint j: the state before step j*NS
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(f32x4*)(ckb + (j * 4 + i) * NTH * 4 + tid * 4) = f32x4{S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]};
+    __syncthreads();  // the previous sub-segment is done with the staged rows
+    {
+      *(f32x4*)&sk[srow][scol] = as_f4(pk);
+      const f32x4 gg = as_f4(pg);
+      *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
+      if (tid < NS * VS / 4) *(f32x4*)&sv[tid >> 3][4 * (tid & 7)] = as_f4(pv);
+      if (tid < NS) sb[tid] = pb;
+    }
+    if (j + 1 < a.nck) issue(j + 1);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s >= ns) break;
+      float sd[16], r[4];
+      fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], lds4(&sv[s][4 * vq]), r);
+    }
+  }
+}
+
+// ===========================================================================
+// backward walk over the sub-segments, in reverse
+// ===========================================================================
+__global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
+  __shared__ __align__(16) float sq[NS][DK];  // scale * q
+  __shared__ __align__(16) float sk[NS][DK];
+  __shared__ __align__(16) float se[NS][DK];  // exp(g)
+  __shared__ __align__(16) float sv[NS][VS];
+  __shared__ __align__(16) float sdo[NS][VS];
+  __shared__ __align__(16) float sr[NS][VS];  // r of each step, per column
+  __shared__ float sb[NS];
+  __shared__ __align__(16) float red[NS][NW][16][32];  // per-wave per-row outputs
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+  const int kq = lane & 31, vq = 2 * w + half;
+  const Slot sl = slot_of(a);
+  const i64 T = a.T, V = a.V;
+
+  float dS[16];
+  {
+    const brsrc r0 = make_rsrc(a.dSf ? a.dSf + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : a.dq,
+                               a.dSf ? (unsigned)(((DK - 1) * V + VS) * 4) : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x = as_f4(bload16(r0, (unsigned)(((4 * kq + i) * V + 4 * vq) * 4)));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dS[4 * i + c] = x[c];
+    }
+  }
+
+  // register prefetch of one sub-segment: q, k, g rows (one float4 each per
+  // thread), the slices of v (threads 0..63) and do (threads 64..127), beta
+  // (threads 0..NS-1) and this thread's part of the checkpoint
+  u32x4 pq, pk, pg, pv, pd, pc[4];
+  float pb;
+  const int srow = tid >> 5, scol = 4 * (tid & 31);
+  const int vrow = (tid & 63) >> 3, vcol = 4 * (tid & 7);
+  const float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (4 * NTH * 4);
+  auto issue = [&](i64 j) {
+    const i64 t0 = j * NS;
+    const int ns = (int)(T - t0 < NS ? T - t0 : NS);
+    const i64 qk0 = ((sl.bi * T + t0) * a.H + sl.h) * DK, hv0 = (sl.bi * T + t0) * a.HV + sl.hv;
+    const brsrc rq = make_rsrc(a.q + qk0, seg_bytes(ns, a.H * DK, DK));
+    const brsrc rk = make_rsrc(a.k + qk0, seg_bytes(ns, a.H * DK, DK));
+    const brsrc rg = make_rsrc(a.g + hv0 * DK, seg_bytes(ns, a.HV * DK, DK));
+    const brsrc rv = make_rsrc(a.v + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
+    const brsrc rd = make_rsrc(a.d_o + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
+    const brsrc rb = make_rsrc(a.beta + hv0, seg_bytes(ns, a.HV, 1));
+    const brsrc rc = make_rsrc(ckb + j * 4 * NTH * 4, 4 * NTH * 16);
+    const unsigned qoff = (unsigned)((srow * a.H * DK + scol) * 4);
+    const unsigned voff = (unsigned)((vrow * a.HV * V + vcol) * 4);
+    pq = bload16(rq, qoff);
+    pk = bload16(rk, qoff);
+    pg = bload16(rg, (unsigned)((srow * a.HV * DK + scol) * 4));
+    pv = bload16(rv, tid < 64 ? voff : BUF_OOB);
+    pd = bload16(rd, tid >= 64 && tid < 128 ? voff : BUF_OOB);
+    pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pc[i] = bload16(rc, (unsigned)((i * NTH + tid) * 16));
+  };
+
+  float* partb = a.part;
+  if (a.nck > 0) issue(a.nck - 1);
+  for (i64 j = a.nck - 1; j >= 0; --j) {
+    const i64 t0 = j * NS;
+    const int ns = (int)(T - t0 < NS ? T - t0 : NS);
+    // stage this sub-segment (the previous one finished reading the staged
+    // rows before its last barrier)
+    float S[16];
+    {
+      const f32x4 qq = as_f4(pq), gg = as_f4(pg);
+      *(f32x4*)&sq[srow][scol] = f32x4{a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]};
+      *(f32x4*)&sk[srow][scol] = as_f4(pk);
+      *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
+      if (tid < 64) *(f32x4*)&sv[vrow][vcol] = as_f4(pv);
+      if (tid >= 64 && tid < 128) *(f32x4*)&sdo[vrow][vcol] = as_f4(pd);
+      if (tid < NS) sb[tid] = pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 x = as_f4(pc[i]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[4 * i + c] = x[c];
+      }
+    }
+    if (j > 0) issue(j - 1);
+    __syncthreads();  // staged rows visible; the previous reduction is done with red
+
+    // recompute the sub-segment's S_dec (registers) and r (LDS, per column)
+    float sd[NS][16];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s >= ns) break;
+      float r[4];
+      fwd_step(S, sd[s], lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], lds4(&sv[s][4 * vq]), r);
+      if (kq == 0) *(f32x4*)&sr[s][4 * vq] = f32x4{r[0], r[1], r[2], r[3]};
+    }
+    // sr is written and read by the same wave (a column block lives in one
+    // half wave), and LDS operations of a wave complete in order
+
+    // backward steps
+#pragma unroll
+    for (int s = NS - 1; s >= 0; --s) {
+      if (s >= ns) continue;
+      const f32x4 qq = lds4(&sq[s][4 * kq]), kk = lds4(&sk[s][4 * kq]), eg = lds4(&se[s][4 * kq]);
+      const f32x4 dd = lds4(&sdo[s][4 * vq]), rr = lds4(&sr[s][4 * vq]);
+      const float beta = sb[s];
+      float o[16];  // per-row outputs: o[4*qd + i], qd = dq_e, da, S_dec dr, dg
+      float drp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = beta * kk[i];
+        float dq_e = 0.0f, da = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = 4 * i + c;
+          dS[e] = fmaf(qq[i], dd[c], dS[e]);                     // step 1: dS += (scale q) (x) do
+          dq_e = fmaf(fmaf(ai, rr[c], sd[s][e]), dd[c], dq_e);  //         dq_e = S_t do
+          da = fmaf(rr[c], dS[e], da);                          // step 2: da = dS r
+          drp[c] = i == 0 ? ai * dS[e] : fmaf(ai, dS[e], drp[c]);  //      dr = dS^T a
+        }
+        o[i] = dq_e;
+        o[4 + i] = da;
+      }
+      float dr[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dr[c] = sum32(drp[c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sdr = 0.0f, dg = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = 4 * i + c;
+          sdr = fmaf(sd[s][e], dr[c], sdr);     // step 4: S_dec dr
+          dS[e] = fmaf(-kk[i], dr[c], dS[e]);   // step 5: dS_dec = dS - k (x) dr
+          dg = fmaf(sd[s][e], dS[e], dg);       //         dg = rowsum(S_dec (.) dS_dec)
+          dS[e] *= eg[i];                       //         dS_{t-1} = exp(g) (.) dS_dec
+        }
+        o[8 + i] = sdr;
+        o[12 + i] = dg;
+      }
+      // dv = dr: this column block's four values, from one lane per half wave
+      if (kq == 0) {
+        float* dvp = a.dv + ((sl.bi * T + t0 + s) * a.HV + sl.hv) * V + sl.vs * VS + 4 * vq;
+        *(f32x4*)dvp = f32x4{dr[0], dr[1], dr[2], dr[3]};
+      }
+      // per-row outputs: pair the half waves (same rows, other 4 columns)
+#pragma unroll
+      for (int jv = 0; jv < 8; ++jv) red[s][w][8 * half + jv][kq] = pair_halves(o[jv], o[8 + jv]);
+    }
+    __syncthreads();  // red complete
+    // sum the 4 waves; thread -> row k, (step, output) pairs half, half+2, ...
+    {
+      const int kr = tid & (DK - 1), hsel = tid >> 7;
+#pragma unroll
+      for (int m = 0; m < 2 * NS; ++m) {
+        const int pidx = hsel + 2 * m, s = pidx >> 2, qd = pidx & 3;
+        if (s >= ns) continue;
+        float acc = red[s][0][4 * qd + (kr & 3)][kr >> 2];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) acc += red[s][ww][4 * qd + (kr & 3)][kr >> 2];
+        partb[((((sl.bi * T + t0 + s) * a.HV + sl.hv) * a.nvs + sl.vs) * NQ + qd) * DK + kr] = acc;
+      }
+    }
+  }
+  if (a.dS0) {
+    float* o = a.dS0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS + 4 * vq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(f32x4*)(o + (4 * kq + i) * V) = f32x4{dS[4 * i], dS[4 * i + 1], dS[4 * i + 2], dS[4 * i + 3]};
+  }
+}
+
+// ===========================================================================
+// slice sums, GVA sum, dq / dk / dg / dbeta: one wave per (batch, t, qk head)
+// ===========================================================================
+__global__ void __launch_bounds__(256) delta_reduce_kernel(DeltaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const i64 id = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (id >= a.b * a.T * a.H) return;  // whole waves
+  const i64 h = id % a.H, bt = id / a.H;
+  const int k0 = 2 * lane;
+  const float2 kk = *(const float2*)(a.k + (bt * a.H + h) * DK + k0);
+  float dq0 = 0.f, dq1 = 0.f, dk0 = 0.f, dk1 = 0.f;
+  for (i64 j = 0; j < a.grp; ++j) {
+    const i64 hv = h * a.grp + j;
+    const float* pp = a.part + (bt * a.HV + hv) * a.nvs * NQ * DK + k0;
+    float s[NQ][2];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) s[qd][0] = s[qd][1] = 0.0f;
+    for (i64 vs = 0; vs < a.nvs; ++vs)
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const float2 x = *(const float2*)(pp + (vs * NQ + qd) * DK);
+        s[qd][0] += x.x;
+        s[qd][1] += x.y;
+      }
+    *(float2*)(a.dg + (bt * a.HV + hv) * DK + k0) = make_float2(s[3][0], s[3][1]);
+    const float db = wave_sum(fmaf(kk.x, s[1][0], kk.y * s[1][1]));
+    if (lane == 0) a.dbeta[bt * a.HV + hv] = db;
+    const float bta = a.beta[bt * a.HV + hv];
+    dq0 += s[0][0];
+    dq1 += s[0][1];
+    dk0 += bta * s[1][0] - s[2][0];
+    dk1 += bta * s[1][1] - s[2][1];
+  }
+  *(float2*)(a.dq + (bt * a.H + h) * DK + k0) = make_float2(a.scale * dq0, a.scale * dq1);
+  *(float2*)(a.dk + (bt * a.H + h) * DK + k0) = make_float2(dk0, dk1);
+}
+
+}  // namespace
+
+// ===========================================================================
+// host side
+// ===========================================================================
+bool delta_shape_supported(const ssmvjp_delta_desc& d) {
+  if (d.dk != DK || d.dv % VS != 0) return false;
+  // 32-bit byte offsets inside one sub-segment's rows
+  return (NS * d.nv_heads * d.dv + d.nqk_heads * DK) * 4 < (1ll << 31);
+}
+
+DeltaPlan delta_plan(const ssmvjp_delta_desc& d) {
+  DeltaPlan p{};
+  p.CK = NS;
+  p.nck = (d.seqlen + NS - 1) / NS;
+  p.vsplit = d.dv / VS;
+  int64_t off = 0;
+  auto carve = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  p.off_ck = carve(d.batch * d.nv_heads * p.nck * DK * d.dv * 4);
+  p.off_part = carve(d.batch * d.seqlen * d.nv_heads * p.vsplit * NQ * DK * 4);
+  p.bytes = (size_t)off;
+  return p;
+}
+
+hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
+                            hipStream_t stream) {
+  DeltaArgs a;
+  a.b = d.batch; a.T = d.seqlen; a.H = d.nqk_heads; a.HV = d.nv_heads; a.V = d.dv;
+  a.nvs = plan.vsplit; a.nck = plan.nck; a.grp = d.nv_heads / d.nqk_heads; a.scale = d.scale;
+  a.q = ptr.q; a.k = ptr.k; a.v = ptr.v; a.beta = ptr.beta; a.g = ptr.g; a.S0 = ptr.S0; a.d_o = ptr.d_o;
+  a.dSf = ptr.dS_final; a.dq = ptr.dq; a.dk = ptr.dk; a.dv = ptr.dv; a.dg = ptr.dg; a.dbeta = ptr.dbeta;
+  a.dS0 = ptr.dS0;
+  char* ws = (char*)ptr.workspace;
+  a.ck = (float*)(ws + plan.off_ck);
+  a.part = (float*)(ws + plan.off_part);
+  const i64 nwg = d.batch * d.nv_heads * plan.vsplit;
+  if (nwg == 0) return hipSuccess;
+  if (d.seqlen > 0) hipLaunchKernelGGL(delta_fwd_ckpt_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
+  hipLaunchKernelGGL(delta_bwd_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
+  const i64 nred = d.batch * d.seqlen * d.nqk_heads;
+  if (nred > 0) hipLaunchKernelGGL(delta_reduce_kernel, dim3((unsigned)((nred + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace ssmvjp

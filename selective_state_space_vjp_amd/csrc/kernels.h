@@ -79,8 +79,8 @@ hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const S
 struct DeltaPlan {
   int64_t CK;          // checkpoint interval (steps)
   int64_t nck;         // checkpoints per (b, hv)
-  int64_t vsplit;      // value-column blocks per (b, hv)
-  int64_t off_ck, off_dqe, off_dke, off_part;
+  int64_t vsplit;      // value-column slices per (b, hv), one workgroup each
+  int64_t off_ck, off_part;
   size_t bytes;
 };
 
@@ -90,6 +90,7 @@ struct DeltaPointers {
   void* workspace;
 };
 
+bool delta_shape_supported(const ssmvjp_delta_desc& d);
 DeltaPlan delta_plan(const ssmvjp_delta_desc& d);
 hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
                             hipStream_t stream);

@@ -122,12 +122,16 @@ def test_ssd_descriptor_validation(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(), bd.OK),
+    (dict(dv=256), bd.OK),
+    (dict(seqlen=0), bd.OK),
     (dict(nv_heads=3, nqk_heads=2), bd.EINVAL),
     (dict(dk=0), bd.EINVAL),
     (dict(reserved=1), bd.EINVAL),
+    (dict(dk=64), bd.EUNSUPPORTED),   # the kernels hold K = 128 rows of the state
+    (dict(dv=48), bd.EUNSUPPORTED),   # V is cut into 32-column slices
 ])
 def test_delta_descriptor_validation(kw, status):
-    d = dict(batch=1, seqlen=64, nqk_heads=2, nv_heads=4, dk=32, dv=32, scale=0.25, reserved=0)
+    d = dict(batch=1, seqlen=64, nqk_heads=2, nv_heads=4, dk=128, dv=32, scale=0.25, reserved=0)
     d.update(kw)
     st, _ = _ws("delta_rule_bwd_workspace", bd.DeltaDesc(**d))
     assert st == status
