@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed FP32 FMA)
 METRIC = "scan-backward tokens/s (B·T/s) at Mamba-2 bf16 shape; % of HBM/MFMA roofline"
 WORKLOAD = "mamba2_chunk"
 
@@ -98,14 +99,106 @@ def cpu_baseline(inp_bf16, w):
                       f"sequential reverse recurrence, {sec:.2f} s"}
 
 
+def kda_cpu_baseline(c, w):
+    """The float64 oracle on batch element 0, qk head 0 and its value heads (all T steps)."""
+    import oracle
+
+    threads = oracle.default_threads()
+    grp = w["HV"] // w["H"]
+    sl = {k: c[k][:1, :, :1] for k in ("q", "k")}
+    sl.update({k: c[k][:1, :, :grp] for k in ("v", "beta", "g", "do")})
+    t0 = time.perf_counter()
+    oracle.kda_bwd(sl["q"], sl["k"], sl["v"], sl["beta"], sl["g"], c["S0"][:1, :grp], sl["do"], None,
+                   scale=c["scale"], nthreads=threads)
+    sec = time.perf_counter() - t0
+    frac = grp / (w["b"] * w["HV"])  # share of the workload's (batch, value head) sequences
+    return {"value": w["b"] * w["T"] * frac / sec, "unit": "tokens/s", "cores": min(threads, grp), "kind": "oracle",
+            "sample": f"batch element 0, qk head 0 and its {grp} value heads (T={w['T']}), float64 store-all "
+                      f"reverse recurrence, {sec:.2f} s; scaled by the {grp}/{w['b'] * w['HV']} share of the "
+                      f"(batch, value head) sequences"}
+
+
+def kda_flops(w):
+    """Algorithmic flops per launch: 5KV per (token, value head) for the forward
+    recompute (exp-gate scaling, k^T S_dec, rank-1 update) and 15KV for the
+    backward (q-do outer product, S_t do, dS r, dS^T a, S_dec dr, k-dr update,
+    rowsum(S_dec dS), gate scaling), counting an FMA as 2."""
+    per = w["b"] * w["T"] * w["HV"] * w["K"] * w["V"]
+    return {"ckpt": 5 * per, "bwd": 20 * per}
+
+
+def bench_kda(args, dev):
+    import numpy as np
+    import torch
+
+    from selective_state_space_vjp_amd import binding, synth
+
+    w = dict(synth.WORKLOADS["kda"])
+    inp = synth.workload_inputs("kda")
+    c = {k: (v.astype(np.float32).astype(np.float64) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(torch.float32).to(dev).contiguous()
+         for k, v in inp.items() if isinstance(v, np.ndarray)}
+    call = binding.DeltaCall(t["q"], t["k"], t["v"], t["beta"], t["g"], t["S0"], t["do"], None, scale=inp["scale"])
+    del inp
+    stages = (binding.DELTA_CKPT, binding.DELTA_BWD, binding.DELTA_REDUCE)
+    for _ in range(args.warmup):
+        for s in stages:
+            call.stage(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        for j, s in enumerate(stages):
+            call.stage(s)
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K for j in range(3)]
+    tokens = w["b"] * w["T"]
+    fl = kda_flops(w)
+    part_bytes = w["b"] * w["T"] * w["HV"] * (w["V"] // 32) * 4 * w["K"] * 4
+    red_bytes = part_bytes + 4 * (2 * w["b"] * w["T"] * w["H"] * w["K"] + w["b"] * w["T"] * w["HV"] * (w["K"] + 2)
+                                  + w["b"] * w["T"] * w["H"] * w["K"])
+    phases = {
+        "ckpt": {"kernel": "delta_fwd_ckpt_kernel", "ms": ms[0], "flops": fl["ckpt"],
+                 "TFLOPs": fl["ckpt"] / (ms[0] * 1e9)},
+        "bwd": {"kernel": "delta_bwd_kernel", "ms": ms[1], "flops": fl["bwd"], "TFLOPs": fl["bwd"] / (ms[1] * 1e9)},
+        "reduce": {"kernel": "delta_reduce_kernel", "ms": ms[2], "bytes": red_bytes,
+                   "GBps": red_bytes / (ms[2] * 1e6)},
+    }
+    dom = phases["bwd"]
+    roofline = {"bound": "alu", "achieved": round(dom["TFLOPs"], 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom["TFLOPs"] / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": dom["kernel"], "algorithmic_flops_per_launch": dom["flops"],
+                "avg_launch_ms": round(dom["ms"], 4)}
+    line = {
+        "metric": METRIC, "value": round(tokens / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "kda", "batch": w["b"], "seqlen": w["T"], "qk_heads": w["H"], "v_heads": w["HV"],
+                   "dk": w["K"], "dv": w["V"]},
+        "roofline": roofline,
+        "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in phases.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = kda_cpu_baseline(c, w)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk"),
-                    help="mamba2_chunk (default, the headline line) or mimo_chunk (rank-4 MIMO, RAW form)")
+    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk", "kda"),
+                    help="mamba2_chunk (default, the headline line), mimo_chunk (rank-4 MIMO, RAW form) or "
+                         "kda (gated delta rule, b=2 T=4096 H=16 HV=32 K=V=128, fp32)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -132,6 +225,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
         return
+    if args.workload == "kda":
+        return bench_kda(args, dev)
     w = dict(synth.WORKLOADS[args.workload])
     w.setdefault("M", 1)
     inp = synth.workload_inputs(args.workload)

@@ -173,17 +173,45 @@ typedef struct {
 
 ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* bytes);
 
-/* KDA backward (all float32).
+/* KDA backward (all float32), K3 notes section "反向传播推导": the forward
+ *   S_dec = exp(g_t) (.) S_{t-1};  r = v_t - k_t^T S_dec;  S_t = S_dec + (beta_t k_t) (x) r;
+ *   o_t = (scale q_t)^T S_t
+ * (F1..F6) with S_{-1} = S0, and its reverse-time backward (BPTT steps 1..5)
+ * seeded with dS_final, followed by the GVA sum of dq and dk over the value
+ * heads of each qk head (step 6).  The gradients are those of
+ *     J = <d_o, o> + <dS_final, S_{T-1}>.
  *   q, k [b,T,H,K]   v [b,T,HV,V]   beta [b,T,HV]   g [b,T,HV,K] (log gate)
  *   S0 [b,HV,K,V] (NULL = zeros)   d_o [b,T,HV,V]   dS_final [b,HV,K,V] (NULL = zeros)
  * Outputs: dq, dk [b,T,H,K]   dv [b,T,HV,V]   dg [b,T,HV,K]   dbeta [b,T,HV]
  *   dS0 [b,HV,K,V] (NULL = not written).
- * Value head hv reads qk head hv / (HV/H).  Constraint: HV % H == 0. */
+ * Value head hv reads qk head hv / (HV/H).
+ * Constraints: HV % H == 0 (SSMVJP_EINVAL otherwise); K == 128 and V a
+ * multiple of 32 (SSMVJP_EUNSUPPORTED otherwise).  Every pointer must be
+ * 16-byte aligned.  T = 0 writes dS0 = dS_final only. */
 ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc,
                              const float* q, const float* k, const float* v, const float* beta,
                              const float* g, const float* S0, const float* d_o, const float* dS_final,
                              float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* The three stages of delta_rule_bwd as separate calls, for callers that
+ * schedule or time them apart.  `stages` is a non-empty bit mask of
+ *  - SSMVJP_DELTA_CKPT:   forward walk that leaves the state at the start of
+ *                         every checkpoint segment in the workspace;
+ *  - SSMVJP_DELTA_BWD:    reverse walk (recompute from the checkpoints, BPTT
+ *                         steps 1..5): writes dv and dS0 and leaves per-slice
+ *                         partial sums of the per-key outputs in the workspace;
+ *  - SSMVJP_DELTA_REDUCE: slice sums and the GVA sum: writes dq, dk, dg, dbeta.
+ * The stages run in that order; calls for the three stages in order on one
+ * stream, with the same descriptor, arguments and workspace, are exactly
+ * delta_rule_bwd (the workspace must not be modified in between).  Arguments
+ * mean what they mean for delta_rule_bwd and are validated the same way. */
+enum { SSMVJP_DELTA_CKPT = 1, SSMVJP_DELTA_BWD = 2, SSMVJP_DELTA_REDUCE = 4, SSMVJP_DELTA_ALL = 7 };
+ssmvjp_status delta_rule_bwd_stages(const ssmvjp_delta_desc* desc, int32_t stages,
+                                    const float* q, const float* k, const float* v, const float* beta,
+                                    const float* g, const float* S0, const float* d_o, const float* dS_final,
+                                    float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* ssmvjp_status_str(ssmvjp_status status);

@@ -18,10 +18,11 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
 FORM_MAMBA2, FORM_RAW = 0, 1
+DELTA_CKPT, DELTA_BWD, DELTA_REDUCE, DELTA_ALL = 1, 2, 4, 7
 
 EXPORTS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
            "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd",
-           "ssmvjp_status_str", "ssmvjp_version")
+           "delta_rule_bwd_stages", "ssmvjp_status_str", "ssmvjp_version")
 
 
 class ScanDesc(ctypes.Structure):
@@ -69,8 +70,10 @@ def lib():
         L.ssd_chunk_bwd_grads.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11 + [sz, vp]
         L.delta_rule_bwd_workspace.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.POINTER(sz)]
         L.delta_rule_bwd.argtypes = [ctypes.POINTER(DeltaDesc)] + [vp] * 15 + [sz, vp]
+        L.delta_rule_bwd_stages.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.c_int32] + [vp] * 15 + [sz, vp]
         for name in ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-                     "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd"):
+                     "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd",
+                     "delta_rule_bwd_stages"):
             getattr(L, name).restype = ctypes.c_int
         L.ssmvjp_status_str.argtypes = [ctypes.c_int]
         L.ssmvjp_status_str.restype = ctypes.c_char_p
@@ -286,10 +289,8 @@ def delta_rule_bwd_workspace(desc):
     return n.value
 
 
-def delta_rule_bwd(q, k, v, beta, g, S0, d_o, dS_final=None, *, scale, want_dS0=True, out=None, workspace=None,
-                   stream=None):
-    """KDA gated delta-rule backward (float32).  Returns dict dq, dk, dv, dg, dbeta, dS0."""
-    desc = delta_desc(q, v, scale)
+def _delta_args(q, k, v, beta, g, S0, d_o, dS_final, want_dS0, out):
+    desc = delta_desc(q, v, 1.0)
     b, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     dev, f32 = q.device, torch.float32
@@ -305,10 +306,42 @@ def delta_rule_bwd(q, k, v, beta, g, S0, d_o, dS_final=None, *, scale, want_dS0=
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
                    dbeta=torch.empty_like(beta),
                    dS0=torch.empty((b, HV, K, V), dtype=f32, device=dev) if want_dS0 else None)
-    ws, wsb = _workspace(delta_rule_bwd_workspace(desc), dev, workspace)
-    st = lib().delta_rule_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
-                              _ptr(d_o), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(ws), wsb,
-                              _stream(stream))
+    p = _ptr
+    args = (p(q), p(k), p(v), p(beta), p(g), p(S0), p(d_o), p(dS_final), p(out["dq"]), p(out["dk"]), p(out["dv"]),
+            p(out["dg"]), p(out["dbeta"]), p(out.get("dS0")))
+    return desc, out, args
+
+
+def delta_rule_bwd(q, k, v, beta, g, S0, d_o, dS_final=None, *, scale, want_dS0=True, out=None, workspace=None,
+                   stream=None):
+    """KDA gated delta-rule backward (float32).  Returns dict dq, dk, dv, dg, dbeta, dS0."""
+    desc, out, args = _delta_args(q, k, v, beta, g, S0, d_o, dS_final, want_dS0, out)
+    desc.scale = float(scale)
+    ws, wsb = _workspace(delta_rule_bwd_workspace(desc), q.device, workspace)
+    st = lib().delta_rule_bwd(ctypes.byref(desc), *args, _ptr(ws), wsb, _stream(stream))
     _check("delta_rule_bwd", st)
     return out
+
+
+class DeltaCall:
+    """A prepared delta_rule_bwd call on fixed device buffers (for repeated timing).
+
+    ``run()`` enqueues the whole backward; ``stage(DELTA_CKPT)``,
+    ``stage(DELTA_BWD)`` and ``stage(DELTA_REDUCE)`` in that order enqueue its
+    three kernels separately (together they are exactly ``run()``).
+    """
+
+    def __init__(self, q, k, v, beta, g, S0, d_o, dS_final=None, *, scale, want_dS0=True, out=None, stream=None):
+        self.desc, self.out, self._args = _delta_args(q, k, v, beta, g, S0, d_o, dS_final, want_dS0, out)
+        self.desc.scale = float(scale)
+        self.ws, self.wsb = _workspace(delta_rule_bwd_workspace(self.desc), q.device, None)
+        self.stream = stream
+        self._keep = (q, k, v, beta, g, S0, d_o, dS_final)
+
+    def stage(self, stages):
+        st = lib().delta_rule_bwd_stages(ctypes.byref(self.desc), int(stages), *self._args, _ptr(self.ws), self.wsb,
+                                         _stream(self.stream))
+        _check("delta_rule_bwd_stages", st)
+
+    def run(self):
+        self.stage(DELTA_ALL)

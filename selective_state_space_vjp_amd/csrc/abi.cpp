@@ -181,12 +181,13 @@ ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* by
   return SSMVJP_OK;
 }
 
-ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, const float* k, const float* v,
-                             const float* beta, const float* g, const float* S0, const float* d_o,
-                             const float* dS_final, float* dq, float* dk, float* dv, float* dg, float* dbeta,
-                             float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+static ssmvjp_status delta_run(const ssmvjp_delta_desc* desc, int32_t stages, const float* q, const float* k,
+                               const float* v, const float* beta, const float* g, const float* S0, const float* d_o,
+                               const float* dS_final, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                               float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
   ssmvjp_status s = delta_check(desc);
   if (s != SSMVJP_OK) return s;
+  if (stages <= 0 || (stages & ~SSMVJP_DELTA_ALL)) return SSMVJP_EINVAL;
   const ssmvjp_delta_desc& d = *desc;
   const bool has_tokens = d.batch * d.seqlen > 0;
   if (has_tokens && (!q || !k || !v || !beta || !g || !d_o || !dq || !dk || !dv || !dg || !dbeta))
@@ -199,7 +200,24 @@ ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, cons
     return SSMVJP_EWORKSPACE;
   if (d.batch == 0) return SSMVJP_OK;
   DeltaPointers ptr{q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace};
-  return hip_status(launch_delta_bwd(d, plan, ptr, (hipStream_t)stream));
+  return hip_status(launch_delta_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+}
+
+ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, const float* k, const float* v,
+                             const float* beta, const float* g, const float* S0, const float* d_o,
+                             const float* dS_final, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                             float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  return delta_run(desc, SSMVJP_DELTA_ALL, q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0,
+                   workspace, workspace_bytes, stream);
+}
+
+ssmvjp_status delta_rule_bwd_stages(const ssmvjp_delta_desc* desc, int32_t stages, const float* q, const float* k,
+                                    const float* v, const float* beta, const float* g, const float* S0,
+                                    const float* d_o, const float* dS_final, float* dq, float* dk, float* dv,
+                                    float* dg, float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return delta_run(desc, stages, q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace,
+                   workspace_bytes, stream);
 }
 
 }  // extern "C"

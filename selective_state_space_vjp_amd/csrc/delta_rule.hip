@@ -431,7 +431,7 @@ DeltaPlan delta_plan(const ssmvjp_delta_desc& d) {
 }
 
 hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
-                            hipStream_t stream) {
+                            hipStream_t stream, int stages) {
   DeltaArgs a;
   a.b = d.batch; a.T = d.seqlen; a.H = d.nqk_heads; a.HV = d.nv_heads; a.V = d.dv;
   a.nvs = plan.vsplit; a.nck = plan.nck; a.grp = d.nv_heads / d.nqk_heads; a.scale = d.scale;
@@ -443,10 +443,12 @@ hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, c
   a.part = (float*)(ws + plan.off_part);
   const i64 nwg = d.batch * d.nv_heads * plan.vsplit;
   if (nwg == 0) return hipSuccess;
-  if (d.seqlen > 0) hipLaunchKernelGGL(delta_fwd_ckpt_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
-  hipLaunchKernelGGL(delta_bwd_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
+  if ((stages & SSMVJP_DELTA_CKPT) && d.seqlen > 0)
+    hipLaunchKernelGGL(delta_fwd_ckpt_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
+  if (stages & SSMVJP_DELTA_BWD) hipLaunchKernelGGL(delta_bwd_kernel, dim3((unsigned)nwg), dim3(NTH), 0, stream, a);
   const i64 nred = d.batch * d.seqlen * d.nqk_heads;
-  if (nred > 0) hipLaunchKernelGGL(delta_reduce_kernel, dim3((unsigned)((nred + 3) / 4)), dim3(256), 0, stream, a);
+  if ((stages & SSMVJP_DELTA_REDUCE) && nred > 0)
+    hipLaunchKernelGGL(delta_reduce_kernel, dim3((unsigned)((nred + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -93,6 +93,6 @@ struct DeltaPointers {
 bool delta_shape_supported(const ssmvjp_delta_desc& d);
 DeltaPlan delta_plan(const ssmvjp_delta_desc& d);
 hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
-                            hipStream_t stream);
+                            hipStream_t stream, int stages);
 
 }  // namespace ssmvjp
