@@ -68,6 +68,10 @@ constexpr int SCAN_NTH = 64 * SCAN_NW;
 constexpr int SCAN_TILES = 32;               // state tiles per workgroup (at most)
 constexpr int SCAN_MAXT = SCAN_TILES / SCAN_NW;  // state tiles per wave
 constexpr int SCAN_SB = 64;                  // fused rows staged per step (at most)
+// row padding (elements) of the staged tiles: 32 bytes, so that the 16 rows a
+// transposed fragment read touches start 8 banks apart
+template <typename T>
+constexpr int scan_pad() { return 32 / (int)sizeof(T); }
 
 // Shape parameters CP, CNB (n block), CL, CM: a non-zero value fixes P, the n
 // block, the chunk length or the rank at compile time (the workload shapes get
@@ -77,11 +81,11 @@ constexpr int SCAN_SB = 64;                  // fused rows staged per step (at m
 // L*M <= 64, else one of the chunk's L*M/64 row blocks, whose products add up
 // in registers until the chunk's last block applies the state update.
 //
-// Pipeline: the rows of step s+2 are in flight in registers while step s is
-// staged into one of two LDS buffers and step s+1's registers wait; with two
-// LDS buffers a single barrier per step separates the staging of a buffer from
-// its fragment reads (the reads of that buffer two steps back ended before the
-// previous step's barrier).
+// Pipeline: the rows of steps s+1 .. s+DEPTH are in flight in registers
+// (DEPTH = 4 for the compile-time bf16 shapes, else 2) while step s is staged
+// into one of two LDS buffers; with two LDS buffers a single barrier per step
+// separates the staging of a buffer from its fragment reads (the reads of that
+// buffer two steps back ended before the previous step's barrier).
 template <typename T, int CP, int CNB, int CL, int CM>
 __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int nb_arg) {
   constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte chunk
@@ -90,7 +94,13 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   constexpr int MAXC_O = FIXED ? (CSB * CP / E16 + SCAN_NTH - 1) / SCAN_NTH : SCAN_SB * 128 / E16 / SCAN_NTH;
   constexpr int MAXC_B = FIXED ? (CSB * CNB / E16 + SCAN_NTH - 1) / SCAN_NTH : SCAN_SB * 128 / E16 / SCAN_NTH;
   constexpr int MAXC = MAXC_O > MAXC_B ? MAXC_O : MAXC_B;  // staging chunks per thread
-  constexpr int PAD = 16 / sizeof(T);
+  constexpr int PAD = scan_pad<T>();
+  // bf16 with compile-time shapes whose n-tile count divides the wave count:
+  // fragments are read ahead of the MFMAs (PRE_RB row blocks per step)
+  constexpr bool PRE = sizeof(T) == 2 && FIXED && CNB / 16 <= SCAN_NW && SCAN_NW % (CNB / 16 > 0 ? CNB / 16 : 1) == 0;
+  constexpr int PRE_RB = PRE ? CSB / 16 : 0;
+  // steps whose rows are in flight in registers (2 or 4)
+  constexpr int DEPTH = PRE ? 4 : 2;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int P = CP ? CP : (int)a.P, N = (int)a.N, L = CL ? CL : (int)a.L, M = CM ? CM : (int)a.M;
   const int NB = CNB ? CNB : nb_arg, LM = L * M;
@@ -166,7 +176,7 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   // per-chunk scalars, set on the chunk's first step
   float sc = 0.0f, e_end = 1.0f;
   // one step: (first step of a chunk) step scalars, staging into LDS buffer sb,
-  // refill of pr with step + 2 (clamped to the last step: loads that are never
+  // refill of pr with step + DEPTH (clamped to the last step: loads that are never
   // used keep the issue unconditional), one barrier, then the state tiles; the
   // chunk's last step stores S_c (or dS_{c+1}) and applies the state update
   auto process = [&](Pre& pr, i64 step, T* sb) {
@@ -188,43 +198,93 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
       if (idx < SB * oc_row) *(u32x4*)(opS + r * PPO + (idx % oc_row) * E16) = scale16(pr.o[it], s_r, (const T*)0);
       if (idx < SB * bc_row) *(u32x4*)(bcS + (idx / bc_row) * PPB + (idx % bc_row) * E16) = pr.b[it];
     }
-    issue(pr, step + 2 < nsteps ? step + 2 : nsteps - 1);
+    issue(pr, step + DEPTH < nsteps ? step + DEPTH : nsteps - 1);
     __syncthreads();
     // state block of this chunk and head; the store is dropped except on the
     // chunk's last step (a range check, so that no store sits in a branch)
     const brsrc rout = make_rsrc(out + ((bi * a.nc + c) * a.H + h) * (i64)P * N, (unsigned)(P * N) * esz);
-#pragma unroll
-    for (int k = 0; k < SCAN_MAXT; ++k) {
-      const int ti = w + SCAN_NW * k;
-      if (ti >= ntiles) continue;
-      const int pt = ti / NTB, nt = ti % NTB;
-      bstore4(rout, last ? (unsigned)native_off(N, pt, n0 / 16 + nt, lane, 0) * esz : BUF_OOB, st[k], (const T*)0);
-      for (int kb = 0; kb < RB; ++kb)
-        mma(acc[k], ld_rowk(opS, PPO, 16 * kb, 16 * pt, lane), ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane));
+    auto update = [&](int k) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         st[k][j] = last ? e_end * st[k][j] + acc[k][j] : st[k][j];
         acc[k][j] = last ? 0.0f : acc[k][j];
+      }
+    };
+    if constexpr (PRE_RB > 0) {
+      // all of the step's fragment reads are issued before the first MFMA
+      // waits on them.  With the n-tile count dividing the wave count every
+      // tile of a wave has the same n tile (nt = w % NTB), so the B or C
+      // fragments are read once per wave.
+      Frag<T> fa[SCAN_MAXT][PRE_RB], fb[PRE_RB];
+      const int nt = w % NTB;
+#pragma unroll
+      for (int kb = 0; kb < PRE_RB; ++kb) fb[kb] = ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane);
+#pragma unroll
+      for (int k = 0; k < SCAN_MAXT; ++k) {
+        const int ti = w + SCAN_NW * k;
+        if (ti >= ntiles) continue;
+#pragma unroll
+        for (int kb = 0; kb < PRE_RB; ++kb) fa[k][kb] = ld_rowk(opS, PPO, 16 * kb, 16 * (ti / NTB), lane);
+      }
+#pragma unroll
+      for (int k = 0; k < SCAN_MAXT; ++k) {
+        const int ti = w + SCAN_NW * k;
+        if (ti >= ntiles) continue;
+        bstore4(rout, last ? (unsigned)native_off(N, ti / NTB, n0 / 16 + nt, lane, 0) * esz : BUF_OOB, st[k],
+                (const T*)0);
+#pragma unroll
+        for (int kb = 0; kb < PRE_RB; ++kb) mma(acc[k], fa[k][kb], fb[kb]);
+        update(k);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < SCAN_MAXT; ++k) {
+        const int ti = w + SCAN_NW * k;
+        if (ti >= ntiles) continue;
+        const int pt = ti / NTB, nt = ti % NTB;
+        bstore4(rout, last ? (unsigned)native_off(N, pt, n0 / 16 + nt, lane, 0) * esz : BUF_OOB, st[k], (const T*)0);
+        for (int kb = 0; kb < RB; ++kb)
+          mma(acc[k], ld_rowk(opS, PPO, 16 * kb, 16 * pt, lane), ld_rowk(bcS, PPB, 16 * kb, 16 * nt, lane));
+        update(k);
       }
     }
   };
 
   T* sb0 = (T*)smem_raw;
   T* sb1 = sb0 + BUF;
-  Pre p0, p1;
   i64 step = 0;
   if (nsteps > 0) {  // T = 0 has no chunk to prefetch
     // each process() ends with SCAN_MAXT state stores after its refill
     const brsrc pad = make_rsrc(out, 0u);
-    issue(p0, 0);
-    vmem_pad_stores<SCAN_MAXT>(pad);
-    issue(p1, nsteps > 1 ? 1 : 0);
-    vmem_pad_stores<SCAN_MAXT>(pad);
-    for (; step + 1 < nsteps; step += 2) {
-      process(p0, step, sb0);
-      process(p1, step + 1, sb1);
+    auto first = [&](Pre& pr, i64 s) {
+      issue(pr, s < nsteps ? s : nsteps - 1);
+      vmem_pad_stores<SCAN_MAXT>(pad);
+    };
+    if constexpr (DEPTH == 4) {
+      Pre p0, p1, p2, p3;
+      first(p0, 0);
+      first(p1, 1);
+      first(p2, 2);
+      first(p3, 3);
+      for (; step + 3 < nsteps; step += 4) {
+        process(p0, step, sb0);
+        process(p1, step + 1, sb1);
+        process(p2, step + 2, sb0);
+        process(p3, step + 3, sb1);
+      }
+      if (step < nsteps) process(p0, step, sb0);
+      if (step + 1 < nsteps) process(p1, step + 1, sb1);
+      if (step + 2 < nsteps) process(p2, step + 2, sb0);
+    } else {
+      Pre p0, p1;
+      first(p0, 0);
+      first(p1, 1);
+      for (; step + 1 < nsteps; step += 2) {
+        process(p0, step, sb0);
+        process(p1, step + 1, sb1);
+      }
+      if (step < nsteps) process(p0, step, sb0);
     }
-    if (step < nsteps) process(p0, step, sb0);
   }
   if (dir == 1) {
 #pragma unroll
@@ -818,7 +878,7 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
 
 template <typename T>
 static size_t states_lds(const SsdArgs& a, int NB) {
-  const int PAD = 16 / sizeof(T);
+  const int PAD = scan_pad<T>();
   const size_t SB = a.LM < SCAN_SB ? a.LM : SCAN_SB;
   return 2 * sizeof(T) * SB * ((a.P + PAD) + (NB + PAD));  // two buffers
 }
