@@ -922,7 +922,9 @@ static void launch_grads_t(const SsdArgs& a, hipStream_t stream) {
     return;
   }
   const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
-  if (workload_shape(a))
+  if (sizeof(T) == 2 && workload_shape(a))
+    launch_ssd_chunk16(a, stream);  // 16 waves, bf16 at P = 64, N = 128, L = 64, M = 1
+  else if (workload_shape(a))
     hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid2), dim3(CH_NTH),
                        grads_lds<T>(a), stream, a);
   else

@@ -1,0 +1,411 @@
+// ssd_chunk16.hip -- the per-chunk backward of the chunked SSD scan (burn-mamba
+// "combined_backward.rs": the BLUE, ORANGE, K3, K2 and K1 backwards and, in the
+// Mamba-2 form, the chain to (dx, d_dt)) for bf16 storage at head dim P = 64,
+// state size N = 128 and 64-step chunks of rank 1, organised for four waves
+// per SIMD.
+//
+// Same method, data layout and results as ssd_chunk_bwd_kernel in ssd_chunk.hip
+// (one workgroup per (batch, chunk, group, head split), the heads of a group in
+// a loop, dB / dC summed over the heads in registers in ascending head order,
+// K2 once on the head-summed d_cb, no float atomics).  What differs is the
+// division of the work: 16 waves with fixed roles and at most 128 registers
+// each, so that every SIMD interleaves four instruction streams (MFMA, LDS and
+// VALU work of different waves overlap):
+//   phase A  waves 0..7   BLUE: dC_blue^T for n tile w (S_c^T . (dy e^cumA)^T),
+//                         dC += dC_blue, the BLUE d_cumA row sums;
+//            waves 8..15  K3: dB_k3^T for n tile w-8 (dS^T . (x delta e^(end-cumA))^T),
+//                         dB += dB_k3, the d_end partial sum of S_c (.) dS_{c+1};
+//            waves 15..6  one ORANGE (t, s) tile pair each (10 pairs): G1 = dy x^T,
+//                         d_cb (summed over heads), masked w = CB * decay, the
+//                         ORANGE d_cumA row and column sums;
+//            one of waves 0..3 (rotating) assembles the previous head's d_cumA,
+//                         K1 suffix sum and d_dt.
+//   phase B  wave w       item (p tile w/4, row block w%4): K3 d_v = dS B^T and
+//                         ORANGE d_v = dy^T w, dx, the K3 decay and dvx row sums.
+// The per-head step scalars (cumA, delta) sit in LDS so that per-element values
+// are LDS reads rather than lane shuffles.
+#include "ssd_common.cuh"
+
+namespace ssmvjp {
+namespace {
+
+constexpr int W16 = 16;          // waves per workgroup
+constexpr int NTH16 = 64 * W16;
+constexpr int P16 = 64, N16 = 128, LM16 = 64;
+constexpr int PT = P16 / 16, NT = N16 / 16, RB = LM16 / 16;
+constexpr int NPAIR = RB * (RB + 1) / 2;  // lower-triangular (t, s) tile pairs
+constexpr int LDC = LM16 + 4;             // CB pitch (float)
+constexpr int LDN = N16 + 8;              // B / C pitch (bf16)
+constexpr int LDP = P16 + 8;              // x / dy pitch (bf16)
+constexpr int PN = P16 * N16;
+
+// partial row sums of one head (float offsets inside one set)
+constexpr int PB_BLUE = 0;                     // [NT][64]    BLUE, by n tile
+constexpr int PB_OROW = PB_BLUE + NT * 64;     // [NPAIR][16] ORANGE row sums, rows of the pair's t block
+constexpr int PB_OCOL = PB_OROW + NPAIR * 16;  // [NPAIR][16] ORANGE column sums, columns of the pair's s block
+constexpr int PB_DEC = PB_OCOL + NPAIR * 16;   // [PT][64]    K3 decay term, by p tile
+constexpr int PB_DVX = PB_DEC + PT * 64;       // [PT][64]    sum_p d_v x, by p tile
+constexpr int PB_DEND = PB_DVX + PT * 64;      // [NT]        sum S (.) dS, by n tile
+constexpr int PB_SET = PB_DEND + 16;
+
+// LDS layout (bytes)
+constexpr int L_CB = 0;                                  // float [64][LDC]
+constexpr int L_PB = L_CB + LM16 * LDC * 4;              // float [2][PB_SET]
+constexpr int L_SC = L_PB + 2 * PB_SET * 4;              // float [2][64]: cumA, delta of the current head
+constexpr int L_B = L_SC + 2 * 64 * 4;                   // bf16 [64][LDN]
+constexpr int L_C = L_B + LM16 * LDN * 2;                // bf16 [64][LDN]
+constexpr int L_X = L_C + LM16 * LDN * 2;                // bf16 [64][LDP]
+constexpr int L_DY = L_X + LM16 * LDP * 2;               // bf16 [64][LDP]
+constexpr int L_DS = L_DY + LM16 * LDP * 2;              // bf16 [P*N] dS_{c+1}, native tiles
+constexpr int L_S = L_DS + PN * 2;                       // bf16 [P*N] S_c, native tiles
+constexpr int L_W = L_S + PN * 2;                        // bf16 [NPAIR][256] w tiles in MFMA output order
+constexpr int L_TOTAL = L_W + NPAIR * 256 * 2;
+
+__device__ __forceinline__ int pair_of(int rt, int rs) { return rt * (rt + 1) / 2 + rs; }
+__device__ __forceinline__ int tile_off(int pt, int nt) { return (pt * NT + nt) * 256; }
+
+template <int UNUSED>
+__global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* CBs = (float*)(smem_raw + L_CB);
+  float* pbase = (float*)(smem_raw + L_PB);
+  float* cumL = (float*)(smem_raw + L_SC);
+  float* delL = cumL + 64;
+  bf16* Bs = (bf16*)(smem_raw + L_B);
+  bf16* Cs = (bf16*)(smem_raw + L_C);
+  bf16* xs = (bf16*)(smem_raw + L_X);
+  bf16* dys = (bf16*)(smem_raw + L_DY);
+  bf16* dSs = (bf16*)(smem_raw + L_DS);
+  bf16* Ss = (bf16*)(smem_raw + L_S);
+  bf16* Wt = (bf16*)(smem_raw + L_W);
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
+            r16 = lane & 15;
+  __builtin_assume(w >= 0 && w < W16);
+  i64 bid = blockIdx.x;
+  const i64 hs = bid % a.hsplit;
+  bid /= a.hsplit;
+  const i64 g = bid % a.G;
+  bid /= a.G;
+  const i64 c = bid % a.nc, bi = bid / a.nc;
+  const i64 t0 = c * LM16;
+  const int Lc = (int)((a.T - t0) < LM16 ? (a.T - t0) : LM16);
+  const int xrs = (int)(a.H * P16), brs = (int)(a.G * N16);  // row strides of x/dy/dx and B/C/dB/dC
+  const i64 xoff0 = (bi * a.T + t0) * a.H * P16, boff0 = (bi * a.T + t0) * a.G * N16 + g * N16;
+  const bf16* xg = (const bf16*)a.xv + xoff0;
+  const bf16* dyg = (const bf16*)a.dy + xoff0;
+  bf16* dxg = (bf16*)a.dxv + xoff0;
+  const bf16* Bg = (const bf16*)a.B + boff0;
+  const bf16* Cg = (const bf16*)a.C + boff0;
+  float* ddtg = a.d_dtda + (bi * a.T + t0) * a.H;
+
+  // ---- B and C rows of the chunk into LDS (rows past the sequence: zeros) ----
+  {
+    const unsigned bcbytes = (unsigned)(((i64)(Lc - 1) * brs + N16) * 2);
+    const brsrc rb_ = make_rsrc(Bg, bcbytes), rc_ = make_rsrc(Cg, bcbytes);
+    const int r = tid >> 4, col = (tid & 15) * 8;  // 64 rows x 16 chunks of 16 bytes
+    *(u32x4*)(Bs + r * LDN + col) = bload16(rb_, (unsigned)(r * brs + col) * 2);
+    *(u32x4*)(Cs + r * LDN + col) = bload16(rc_, (unsigned)(r * brs + col) * 2);
+  }
+
+  // ---- register prefetch of one head: step scalars, A, x or dy rows, S_c and dS_{c+1} ----
+  // threads 0..511 stage x, 512..1023 dy (one 16-byte chunk each); every
+  // thread stages one chunk of S_c and one of dS_{c+1}
+  u32x4 rxy, rs, rd;
+  ChunkScalars rcs = {0.f, 0.f, 0.f, 0.f};
+  float rA = 0.0f;
+  const i64 hbase = g * a.hpg + hs * a.hph;
+  const unsigned xbytes = (unsigned)(((i64)(Lc - 1) * xrs + P16) * 2);
+  const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));
+  const int xy_sel = tid >> 9, xy_idx = tid & 511, xy_r = xy_idx >> 3, xy_col = (xy_idx & 7) * 8;
+  auto issue = [&](i64 h) {
+    rcs = issue_scalars(a, bi, c, h, lane);
+    rA = bload_f32(rsA, (unsigned)(h * 4));
+    const brsrc bxy = make_rsrc((xy_sel ? dyg : xg) + (int)h * P16, xbytes);
+    rxy = bload16(bxy, (unsigned)(xy_r * xrs + xy_col) * 2);
+    const i64 so = ((bi * a.nc + c) * a.H + h) * (i64)PN;
+    rs = bload16(make_rsrc((const bf16*)a.S + so, PN * 2), (unsigned)tid * 16u);
+    rd = bload16(make_rsrc((const bf16*)a.dS + so, PN * 2), (unsigned)tid * 16u);
+  };
+  issue(hbase);
+  // each head issues the next head's loads, then the d_dt store and one dx store
+  vmem_pad_stores<2>(make_rsrc(a.dxv, 0u));
+  __syncthreads();  // B, C staged
+
+  // ---- C.B^T (K2 recompute) on the lower-triangular tile pairs, waves 0..9 ----
+  if (w < NPAIR) {
+    int rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= w) ++rt;
+    const int rs_ = w - rt * (rt + 1) / 2;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NT; ++kb)
+      mma(acc, ld_colk(Cs, LDN, 16 * rt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * rs_, 16 * kb, lane));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) CBs[(16 * rt + 4 * q + j) * LDC + 16 * rs_ + r16] = acc[j];
+  }
+
+  // ---- fixed roles ----
+  const bool blue = w < NT;             // phase A product: BLUE (dC) or K3 (dB)
+  const int nt_own = blue ? w : w - NT;
+  const int pair = W16 - 1 - w;          // ORANGE pair of waves 15..6
+  const bool has_pair = pair >= 0 && pair < NPAIR;
+  int prt = 0;
+  while (has_pair && (prt + 1) * (prt + 2) / 2 <= pair) ++prt;
+  const int prs = has_pair ? pair - prt * (prt + 1) / 2 : 0;
+  const int ipt = w / RB, irb = w % RB;  // phase B item
+  f32x4 xacc[RB];                        // dC (BLUE waves) or dB (K3 waves), transposed, summed over heads
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) xacc[rb] = zero4();
+  f32x4 dcbacc = zero4();                // d_cb of this wave's pair, summed over heads
+
+  // d_cumA from its sources, the K1 suffix sum and the chain to d_dt (RAW:
+  // d_da) for one head, from the partial sums in pb; lane = step
+  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float {
+    float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
+    if (lane < LM16) {
+      const int rbl = lane >> 4, rl = lane & 15;
+      float bl = 0.f, orow = 0.f, ocol = 0.f, dec = 0.f;
+#pragma unroll
+      for (int k = 0; k < NT; ++k) bl += pb[PB_BLUE + k * 64 + lane];
+      for (int k = 0; k <= rbl; ++k) orow += pb[PB_OROW + pair_of(rbl, k) * 16 + rl];
+      for (int k = rbl; k < RB; ++k) ocol += pb[PB_OCOL + pair_of(k, rbl) * 16 + rl];
+#pragma unroll
+      for (int k = 0; k < PT; ++k) {
+        dec += pb[PB_DEC + k * 64 + lane];
+        dvx += pb[PB_DVX + k * 64 + lane];
+      }
+      qv = dec * exp_hw(cs.end - cs.cum);
+      dc = bl + orow - ocol - qv;
+    }
+    const float qsum = wave_sum(qv);
+    float dendt = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) dendt += pb[PB_DEND + k];
+    dendt *= exp_hw(cs.end);
+    if (lane == Lc - 1) dc += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
+    const float dda = wave_incl_suffix(lane < Lc ? dc : 0.0f, lane);
+    return a.raw ? dda : (dvx + dda * Ah) * cs.sig;
+  };
+  const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
+  i64 prev_h = 0;
+  ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
+  float prev_Ah = 0.0f;
+
+  for (i64 hh = 0; hh < a.hph; ++hh) {
+    const i64 h = hbase + hh;
+    float* pb = pbase + (hh & 1) * PB_SET;
+    const ChunkScalars cs = finish_scalars(rcs);
+    const float Ah = rA;
+    const brsrc bdx = make_rsrc(dxg + (int)h * P16, xbytes);
+
+    __syncthreads();  // the previous head is done with xs / dys / Ss / dSs / the scalars (and CB on entry)
+    *(u32x4*)((xy_sel ? dys : xs) + xy_r * LDP + xy_col) = rxy;
+    *(u32x4*)(Ss + tid * 8) = rs;
+    *(u32x4*)(dSs + tid * 8) = rd;
+    if (w == 0) {
+      cumL[lane] = cs.cum;
+      delL[lane] = cs.delta;
+    }
+    issue(hh + 1 < a.hph ? h + 1 : h);  // unconditional: the last head reloads its own rows
+    __syncthreads();
+
+    // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
+    {
+      const bool on = hh > 0 && w == (int)((hh - 1) & 3);
+      float v = 0.0f;
+      if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_SET);
+      bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + prev_h) * 4) : BUF_OOB, v);
+    }
+
+    // ---- phase A (1): ORANGE on this wave's tile pair ----
+    if (has_pair) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < PT; ++kb)
+        mma(acc, ld_colk(dys, LDP, 16 * prt, 16 * kb, lane), ld_colk(xs, LDP, 16 * prs, 16 * kb, lane));
+      const int s_ = 16 * prs + r16;
+      const float cs_s = cumL[s_], dls = delL[s_];
+      const f32x4 ct = *(const f32x4*)(cumL + 16 * prt + 4 * q);  // rows t = 16 prt + 4q + j
+      float orow[4], ocol = 0.0f, wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * prt + 4 * q + j;
+        const float dec = (s_ <= t && t < Lc) ? exp_hw(ct[j] - cs_s) : 0.0f;
+        const float dcb = acc[j] * dls * dec;  // d_w = dy . v^T with v = delta x (delta = 1 for RAW)
+        dcbacc[j] += dcb;
+        const float cb = CBs[t * LDC + s_];
+        const float dd = dcb * cb;
+        orow[j] = dd;
+        ocol += dd;
+        wv[j] = cb * dec;  // w = CB * decay: the d_v_orange operand
+      }
+      store4(Wt + pair * 256 + 4 * lane, f32x4{wv[0], wv[1], wv[2], wv[3]});
+#pragma unroll
+      for (int j = 0; j < 4; ++j) orow[j] = sum16(orow[j]);
+      ocol = sum4q(ocol);
+      if (r16 == 0) *(f32x4*)(pb + PB_OROW + pair * 16 + 4 * q) = f32x4{orow[0], orow[1], orow[2], orow[3]};
+      if (q == 0) pb[PB_OCOL + pair * 16 + r16] = ocol;
+    }
+
+    // ---- phase A (2): BLUE (dC) or K3 (dB) on this wave's n tile, computed
+    // transposed (rows n, columns the chunk's rows r) ----
+    {
+      float fcol[RB];  // per-lane column factor of row r = 16 rb + r16
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float cl = cumL[16 * rb + r16];
+        fcol[rb] = blue ? exp_hw(cl) : delL[16 * rb + r16] * exp_hw(cs.end - cl);
+      }
+      const bf16* opA = blue ? Ss : dSs;  // A: rows n, k = p (native tiles)
+      const bf16* opB = blue ? dys : xs;  // B: k = p, columns r
+      f32x4 acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = zero4();
+      float dend = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < PT; ++kb) {
+        const Frag<bf16> fa = ld_ntv(opA + tile_off(kb, nt_own), lane);
+        Frag<bf16> fb[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) fb[rb] = ld_colk(opB, LDP, 16 * rb, 16 * kb, lane);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mma(acc[rb], fa, fb[rb]);
+        if (!blue) {  // d_end partial: S_c (.) dS_{c+1} over this n tile
+          float vS[4], vdS[4];
+          frag_get(ld_ntv(Ss + tile_off(kb, nt_own), lane), vS);
+          frag_get(fa, vdS);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dend = fmaf(vS[j], vdS[j], dend);
+        }
+      }
+      if (blue) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float cv[4];
+          frag_get(ld_colk(Cs, LDN, 16 * rb, 16 * nt_own, lane), cv);  // C[r][n .. n+3], n = 16 nt + 4q
+          float bsum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float val = acc[rb][j] * fcol[rb];
+            xacc[rb][j] += val;
+            bsum = fmaf(cv[j], val, bsum);
+          }
+          bsum = sum4q(bsum);
+          if (q == 0) pb[PB_BLUE + nt_own * 64 + 16 * rb + r16] = bsum;
+        }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
+        dend = wave_sum(dend);
+        if (lane == 0) pb[PB_DEND + nt_own] = dend;
+      }
+    }
+
+    __syncthreads();  // w tiles complete
+
+    // ---- phase B: K3 d_dv^T = dS_{c+1} . B^T and ORANGE d_v_or^T = dy^T . w for
+    // the item (p tile ipt, row block irb); dx; K3 decay and dvx row sums ----
+    {
+      f32x4 acc3 = zero4(), acc5 = zero4();
+      // A: rows p, k = n (transposed native read); B: k = n, columns r -- in two batches of 4 n tiles
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        Frag<bf16> f3a[NT / 2], f3b[NT / 2];
+#pragma unroll
+        for (int k = 0; k < NT / 2; ++k) {
+          const int kb = half * (NT / 2) + k;
+          f3a[k] = ld_ntv_t(dSs + tile_off(ipt, kb), lane);
+          f3b[k] = ld_colk(Bs, LDN, 16 * irb, 16 * kb, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < NT / 2; ++k) mma(acc3, f3a[k], f3b[k]);
+      }
+      {  // A: rows p, k = t (transpose read of dy rows); B: k = t, columns s
+        Frag<bf16> f5a[RB], f5b[RB];
+#pragma unroll
+        for (int kb = 0; kb < RB; ++kb) {
+          if (kb < irb) continue;
+          f5a[kb] = ld_rowk(dys, LDP, 16 * kb, 16 * ipt, lane);
+          f5b[kb] = ld_ntv(Wt + pair_of(kb, irb) * 256, lane);
+        }
+#pragma unroll
+        for (int kb = 0; kb < RB; ++kb) {
+          if (kb < irb) continue;
+          mma(acc5, f5a[kb], f5b[kb]);
+        }
+      }
+      const int r = 16 * irb + r16;  // this lane's column
+      const float dl = delL[r];
+      const float edec = exp_hw(cs.end - cumL[r]);
+      float xv[4];
+      frag_get(ld_colk(xs, LDP, 16 * irb, 16 * ipt, lane), xv);  // x[r][p .. p+3], p = 16 pt + 4q
+      float dvo[4], s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float dv = fmaf(acc3[j], edec, acc5[j]);  // d_v = d_v_k3 + d_v_orange
+        dvo[j] = a.raw ? dv : dv * dl;
+        s1 = fmaf(acc3[j], xv[j], s1);  // d_decay / delta = sum_p d_decayed_v . x
+        s2 = fmaf(dv, xv[j], s2);
+      }
+      // rows past the end of the sequence fall outside the resource and are dropped
+      bstore4(bdx, (unsigned)(r * xrs + 16 * ipt + 4 * q) * 2, f32x4{dvo[0], dvo[1], dvo[2], dvo[3]},
+              (const bf16*)0);
+      s1 = sum4q(s1) * dl;
+      s2 = sum4q(s2);
+      if (q == 0) {
+        pb[PB_DEC + ipt * 64 + r] = s1;
+        pb[PB_DVX + ipt * 64 + r] = s2;
+      }
+    }
+    __syncthreads();  // partial sums complete
+    prev_h = h;
+    prev_cs = cs;
+    prev_Ah = Ah;
+  }
+  if (a.hph > 0) {
+    const bool on = w == (int)((a.hph - 1) & 3);
+    float v = 0.0f;
+    if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_SET);
+    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + prev_h) * 4) : BUF_OOB, v);
+  }
+
+  // ---- K2 backward on the head-summed d_cb: dC_k2 = d_cb . B, dB_k2 = d_cb^T . C ----
+  __syncthreads();
+  if (has_pair) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) CBs[(16 * prt + 4 * q + j) * LDC + 16 * prs + r16] = dcbacc[j];
+  }
+  __syncthreads();
+  const i64 stride = a.b * a.T * a.G * a.N;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // transposed: rows n, columns r
+    f32x4 acc = xacc[rb];
+    if (blue) {
+      for (int kb = 0; kb <= rb; ++kb)  // dC_k2^T = B^T . d_cb^T
+        mma(acc, ld_rowk(Bs, LDN, 16 * kb, 16 * nt_own, lane), frag_make<bf16>(ld_colk(CBs, LDC, 16 * rb, 16 * kb, lane).v));
+    } else {
+      for (int kb = rb; kb < RB; ++kb)  // dB_k2^T = C^T . d_cb
+        mma(acc, ld_rowk(Cs, LDN, 16 * kb, 16 * nt_own, lane), frag_make<bf16>(ld_rowk(CBs, LDC, 16 * kb, 16 * rb, lane).v));
+    }
+    const int r = 16 * rb + r16;
+    if (r >= Lc) continue;
+    const int o = r * brs + 16 * nt_own + 4 * q;  // [r][n .. n+3], offset from boff0
+    if (a.hsplit == 1)
+      store4((bf16*)(blue ? a.dC : a.dB) + boff0 + o, acc);
+    else
+      store4(a.part + ((blue ? a.hsplit : 0) + hs) * stride + boff0 + o, acc);
+  }
+}
+
+}  // namespace
+
+void launch_ssd_chunk16(const SsdArgs& a, hipStream_t stream) {
+  const i64 grid = a.b * a.nc * a.G * a.hsplit;
+  hipLaunchKernelGGL(ssd_chunk16_kernel<0>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+}
+
+}  // namespace ssmvjp

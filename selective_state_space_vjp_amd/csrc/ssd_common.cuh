@@ -147,6 +147,10 @@ __device__ __forceinline__ ChunkScalars load_scalars(const SsdArgs& a, i64 bi, i
   return finish_scalars(issue_scalars(a, bi, c, h, lane));
 }
 
+// per-chunk backward with 16 waves for bf16 at P = 64, N = 128 and 64-step
+// rank-1 chunks, defined in ssd_chunk16.hip
+void launch_ssd_chunk16(const SsdArgs& a, hipStream_t stream);
+
 // row-blocked chunk backward (L*M > 64), defined in ssd_blocked.hip
 bool ssd_blocked_supported(const ssmvjp_ssd_desc& d);
 void launch_ssd_blocked_grads(const SsdArgs& a, bool is_bf16, hipStream_t stream);
