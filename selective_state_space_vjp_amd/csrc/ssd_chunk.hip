@@ -149,28 +149,35 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   };
   const int oc_row = P / E16, bc_row = NB / E16;
   const unsigned esz = sizeof(T);
-  const i64 nsteps = a.nc * NSUB;
-  auto chunk_of = [&](i64 step) { const i64 ci = step / NSUB; return dir == 0 ? ci : a.nc - 1 - ci; };
-  auto issue = [&](Pre& pr, i64 step) {
-    const i64 c = chunk_of(step);
-    const int R0 = (int)(step % NSUB) * SB;  // first fused row of this step
-    const i64 t0 = c * L;
-    const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
+  const int nsteps = (int)(a.nc * NSUB);
+  // loop-invariant bases of this (batch, head, n block); per-step offsets
+  // inside one batch element are 32-bit (the shape check bounds them)
+  const int rs_op = (int)(a.H * P), rs_bc = (int)(a.G * a.N);  // fused-row strides of x/dy and B/C
+  const T* op_b = op + ix_xv(a, bi, 0, 0, h, 0);
+  const T* bc_b = bc + ix_bc(a, bi, 0, 0, g, n0);
+  const float* csv_b = a.csv + (bi * a.nc * a.H + h) * 3 * 64;
+  T* out_b = out + (bi * a.nc * a.H + h) * (i64)P * N;
+  const int T32 = (int)a.T, nc32 = (int)a.nc, H32 = (int)a.H;
+  auto chunk_of = [&](int step) { const int ci = step / NSUB; return dir == 0 ? ci : nc32 - 1 - ci; };
+  auto issue = [&](Pre& pr, int step) {
+    const int c = chunk_of(step);
+    const int R0 = (step % NSUB) * SB;  // first fused row of this step
+    const int t0 = c * L;
+    const int Lc = T32 - t0 < L ? T32 - t0 : L;
     const int rows = Lc * M - R0;  // valid fused rows of this step (may be <= 0)
-    const brsrc rcs = make_rsrc(csv_at(a, bi, c, h), 3 * 64 * 4);
+    const int R = t0 * M + R0;     // first fused row in the batch element
+    const brsrc rcs = make_rsrc(csv_b + c * H32 * 3 * 64, 3 * 64 * 4);
     pr.cum = bload_f32(rcs, (unsigned)lane * 4u);
     pr.delta = bload_f32(rcs, (unsigned)(64 + lane) * 4u);
-    const brsrc ro = make_rsrc(op + ix_xv(a, bi, t0, 0, h, 0) + (i64)R0 * a.H * P,
-                               rows > 0 ? (unsigned)(((rows - 1) * a.H * P + P) * esz) : 0u);
-    const brsrc rb = make_rsrc(bc + ix_bc(a, bi, t0, 0, g, n0) + (i64)R0 * a.G * a.N,
-                               rows > 0 ? (unsigned)(((rows - 1) * a.G * a.N + NB) * esz) : 0u);
+    const brsrc ro = make_rsrc(op_b + R * rs_op, rows > 0 ? (unsigned)(((rows - 1) * rs_op + P) * esz) : 0u);
+    const brsrc rb = make_rsrc(bc_b + R * rs_bc, rows > 0 ? (unsigned)(((rows - 1) * rs_bc + NB) * esz) : 0u);
 #pragma unroll
     for (int it = 0; it < MAXC; ++it) {
       const int idx = tid + it * SCAN_NTH;
       const int r1 = idx / oc_row, c1 = (idx % oc_row) * E16;
       const int r2 = idx / bc_row, c2 = (idx % bc_row) * E16;
-      pr.o[it] = bload16(ro, idx < SB * oc_row ? (unsigned)((r1 * a.H * P + c1) * esz) : BUF_OOB);
-      pr.b[it] = bload16(rb, idx < SB * bc_row ? (unsigned)((r2 * a.G * a.N + c2) * esz) : BUF_OOB);
+      pr.o[it] = bload16(ro, idx < SB * oc_row ? (unsigned)((r1 * rs_op + c1) * esz) : BUF_OOB);
+      pr.b[it] = bload16(rb, idx < SB * bc_row ? (unsigned)((r2 * rs_bc + c2) * esz) : BUF_OOB);
     }
   };
   // per-chunk scalars, set on the chunk's first step
@@ -179,9 +186,9 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
   // refill of pr with step + DEPTH (clamped to the last step: loads that are never
   // used keep the issue unconditional), one barrier, then the state tiles; the
   // chunk's last step stores S_c (or dS_{c+1}) and applies the state update
-  auto process = [&](Pre& pr, i64 step, T* sb) {
-    const i64 c = chunk_of(step);
-    const int ks = (int)(step % NSUB);
+  auto process = [&](Pre& pr, int step, T* sb) {
+    const int c = chunk_of(step);
+    const int ks = step % NSUB;
     const bool last = ks == NSUB - 1;
     if (ks == 0) {
       const float end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr.cum), 63));
@@ -202,7 +209,7 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
     __syncthreads();
     // state block of this chunk and head; the store is dropped except on the
     // chunk's last step (a range check, so that no store sits in a branch)
-    const brsrc rout = make_rsrc(out + ((bi * a.nc + c) * a.H + h) * (i64)P * N, (unsigned)(P * N) * esz);
+    const brsrc rout = make_rsrc(out_b + c * H32 * P * N, (unsigned)(P * N) * esz);
     auto update = [&](int k) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -252,11 +259,11 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
 
   T* sb0 = (T*)smem_raw;
   T* sb1 = sb0 + BUF;
-  i64 step = 0;
+  int step = 0;
   if (nsteps > 0) {  // T = 0 has no chunk to prefetch
     // each process() ends with SCAN_MAXT state stores after its refill
     const brsrc pad = make_rsrc(out, 0u);
-    auto first = [&](Pre& pr, i64 s) {
+    auto first = [&](Pre& pr, int s) {
       issue(pr, s < nsteps ? s : nsteps - 1);
       vmem_pad_stores<SCAN_MAXT>(pad);
     };
@@ -825,9 +832,13 @@ bool ssd_shape_supported(const ssmvjp_ssd_desc& d) {
   if (d.headdim % 16 || d.dstate % 16 || d.headdim > 128 || d.dstate > 16 * CH_NW) return false;
   const i64 LM = d.chunk_len * d.mimo_rank;
   if (LM % 16) return false;
-  // byte offsets inside one chunk are 32-bit (buffer loads, int row offsets)
-  const i64 esz = d.dtype == SSMVJP_BF16 ? 2 : 4;
-  if (LM * d.nheads * d.headdim * esz >= (1ll << 31) || LM * d.ngroups * d.dstate * esz >= (1ll << 31)) return false;
+  // byte offsets inside one batch element are 32-bit (buffer loads, int row
+  // offsets): rows of x/dy and B/C, the stored states
+  const i64 esz = d.dtype == SSMVJP_BF16 ? 2 : 4, nc = cdiv(d.seqlen, d.chunk_len);
+  if (d.seqlen * d.mimo_rank * d.nheads * d.headdim * esz >= (1ll << 31) ||
+      d.seqlen * d.mimo_rank * d.ngroups * d.dstate * esz >= (1ll << 31) ||
+      nc * d.nheads * d.headdim * d.dstate * esz >= (1ll << 31) || nc * d.nheads * 3 * 64 * 4 >= (1ll << 31))
+    return false;
   if ((d.headdim / 16) * (scan_nb(d) / 16) > SCAN_TILES) return false;
   if (LM > SCAN_SB) return ssd_blocked_supported(d);  // long fused chunks: row-blocked kernels
   return LM <= MAXRB * 16 && grads_lds_bytes(d) <= 160 * 1024;
