@@ -54,7 +54,8 @@ def algorithmic_bytes(w, elem=2, state_elem=2):
     return {"state_scans": scans, "chunk_grads": grads, "path": path}
 
 
-KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/ssd_common.cuh",
+KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/ssd_chunk16.hip",
+                  "selective_state_space_vjp_amd/csrc/ssd_blocked.hip", "selective_state_space_vjp_amd/csrc/ssd_common.cuh",
                   "selective_state_space_vjp_amd/csrc/common.cuh")
 
 
@@ -246,7 +247,13 @@ def main():
     s0, dsf = dt_(c["s0"]), dt_(c["ds_final"])
     call = binding.SsdCall(xv, dtda, A, B, C, s0, dy, dsf, chunk_len=w["L"])
     del inp
-    grads_kernel = "ssd_blocked_bwd_kernel" if w["L"] * w["M"] > 64 else "ssd_chunk_bwd_kernel"
+    # the kernel the library dispatches the per-chunk backward to at this shape
+    if w["L"] * w["M"] > 64:
+        grads_kernel = "ssd_blocked_bwd_kernel"
+    elif (w["P"], w["N"], w["L"], w["M"]) == (64, 128, 64, 1):
+        grads_kernel = "ssd_chunk16_kernel"  # bf16, 16 waves
+    else:
+        grads_kernel = "ssd_chunk_bwd_kernel"
 
     for _ in range(args.warmup):
         call.states()
