@@ -19,19 +19,19 @@
 // MI355X organisation (three launches):
 //  * Columns of S are independent in the recurrence (r[v] and the update of
 //    column v read column v only), so V is cut into 32-column slices and every
-//    kernel runs one workgroup (4 waves) per (batch, value head, slice).  A
-//    thread owns a 4 x 4 block of its slice (rows 4kq..4kq+3, columns
-//    4vq..4vq+3); the 32 threads that share a column block sit in one half
-//    wave, so the per-column sums over k (k^T S_dec, dS^T a) are DPP row sums
-//    plus one permlane16 swap, with no LDS traffic and no barrier.
+//    kernel runs one workgroup (8 waves, two per SIMD) per (batch, value head,
+//    slice).  A thread owns a 4 x 2 block of its slice (rows 4kq..4kq+3,
+//    columns 2vq, 2vq+1); the 32 threads that share a column block sit in one
+//    half wave, so the per-column sums over k (k^T S_dec, dS^T a) are DPP row
+//    sums plus one permlane16 swap, with no LDS traffic and no barrier.
 //  * delta_fwd_ckpt_kernel walks the sequence forward and stores the state
 //    at the start of every NS-step sub-segment (the checkpoints).
 //  * delta_bwd_kernel walks the sub-segments in reverse: it recomputes the
 //    NS states of a sub-segment from its checkpoint into registers, then runs
 //    the NS backward steps.  dv is a per-column output and is stored
 //    directly.  The per-row outputs (dq_e, da, S_dec dr, dg: sums over v)
-//    never feed back into the recurrence; each thread folds its 4 columns,
-//    half waves are paired with one permlane32 swap, and the 4 waves are
+//    never feed back into the recurrence; each thread folds its 2 columns,
+//    half waves are paired with one permlane32 swap, and the 8 waves are
 //    summed through LDS once per sub-segment into the slice's partial sums.
 //  * delta_reduce_kernel adds the slice partials in slice order, applies the
 //    GVA sum over the value heads of each qk head (ascending), and forms dq,
@@ -46,9 +46,11 @@ namespace ssmvjp {
 namespace {
 
 constexpr int DK = 128;          // key dimension: rows of the state
-constexpr int NW = 4;            // waves per workgroup
+constexpr int NW = 8;            // waves per workgroup
 constexpr int NTH = 64 * NW;
-constexpr int VS = 32;           // columns of the state per workgroup (8 column blocks of 4)
+constexpr int VT = 2;            // state columns per thread
+constexpr int NE = 4 * VT;       // state elements per thread (4 rows x VT columns)
+constexpr int VS = NW * 2 * VT;  // columns of the state per workgroup (16 column blocks of 2)
 constexpr int NS = 8;            // steps per sub-segment = checkpoint interval
 constexpr int NQ = 4;            // per-row outputs: dq_e, da, S_dec dr, dg
 
@@ -57,7 +59,7 @@ struct DeltaArgs {
   float scale;
   const float *q, *k, *v, *beta, *g, *S0, *d_o, *dSf;
   float *dq, *dk, *dv, *dg, *dbeta, *dS0;
-  float* ck;    // [b][HV][nvs][nck][4][NTH] float4: state at the start of each sub-segment
+  float* ck;    // [b][HV][nvs][nck][NE/4][NTH] float4: state at the start of each sub-segment
   float* part;  // [b][T][HV][nvs][NQ][DK] per-slice partial sums of the per-row outputs
 };
 
@@ -98,28 +100,34 @@ __device__ __forceinline__ Slot slot_of(const DeltaArgs& a) {
   return s;
 }
 
-// One forward step on this thread's 4x4 block (S[4i+c]: row 4kq+i, column
-// 4vq+c): sd = exp(g) (.) S, r = v - k^T sd (column sums over the half wave),
-// S = sd + (beta k) (x) r.
-__device__ __forceinline__ void fwd_step(float S[16], float sd[16], f32x4 eg, f32x4 kk, float beta, f32x4 vv,
-                                         float r[4]) {
+// One forward step on this thread's 4 x VT block (S[VT*i+c]: row 4kq+i,
+// column VT*vq+c): sd = exp(g) (.) S, r = v - k^T sd (column sums over the
+// half wave), S = sd + (beta k) (x) r.
+__device__ __forceinline__ void fwd_step(float S[NE], float sd[NE], f32x4 eg, f32x4 kk, float beta, const float vv[VT],
+                                         float r[VT]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sd[4 * i + c] = eg[i] * S[4 * i + c];
+    for (int c = 0; c < VT; ++c) sd[VT * i + c] = eg[i] * S[VT * i + c];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < VT; ++c) {
     float p = kk[0] * sd[c];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) p = fmaf(kk[i], sd[4 * i + c], p);
+    for (int i = 1; i < 4; ++i) p = fmaf(kk[i], sd[VT * i + c], p);
     r[c] = vv[c] - sum32(p);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float ai = beta * kk[i];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S[4 * i + c] = fmaf(ai, r[c], sd[4 * i + c]);
+    for (int c = 0; c < VT; ++c) S[VT * i + c] = fmaf(ai, r[c], sd[VT * i + c]);
   }
+}
+
+__device__ __forceinline__ void ld_cols(const float* p, float o[VT]) {
+  const float2 u = *(const float2*)p;
+  o[0] = u.x;
+  o[1] = u.y;
 }
 
 // byte size of the valid rows of one sub-segment in a [.., T, heads, width] tensor
@@ -130,6 +138,18 @@ __device__ __forceinline__ unsigned seg_bytes(int ns, i64 row_stride, int width)
 // ===========================================================================
 // forward walk: checkpoints at the start of every sub-segment
 // ===========================================================================
+// this thread's 4 x VT block of a [K x V] state (row stride V), through a
+// range-checked resource (NULL base: zeros)
+__device__ __forceinline__ void load_block(float S[NE], const float* base, i64 V, int kq, int vq) {
+  const brsrc r0 = make_rsrc(base ? base : (const float*)nullptr, base ? (unsigned)(((DK - 1) * V + VS) * 4) : 0u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r0, (int)(((4 * kq + i) * V + VT * vq) * 4), 0, 0);
+    S[VT * i] = __uint_as_float(u[0]);
+    S[VT * i + 1] = __uint_as_float(u[1]);
+  }
+}
+
 __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
   __shared__ __align__(16) float sk[NS][DK];
   __shared__ __align__(16) float se[NS][DK];
@@ -140,22 +160,14 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
   const Slot sl = slot_of(a);
   const i64 T = a.T, V = a.V;
 
-  float S[16];
-  {
-    const brsrc r0 = make_rsrc(a.S0 ? a.S0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : a.dq,
-                               a.S0 ? (unsigned)(((DK - 1) * V + VS) * 4) : 0u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x = as_f4(bload16(r0, (unsigned)(((4 * kq + i) * V + 4 * vq) * 4)));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S[4 * i + c] = x[c];
-    }
-  }
-  // register prefetch of one sub-segment: k and g rows (one float4 each per
-  // thread), the slice of v (threads 0..63), beta (threads 0..NS-1)
+  float S[NE];
+  load_block(S, a.S0 ? a.S0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : nullptr, V, kq, vq);
+  // register prefetch of one sub-segment (threads 0..255): k and g rows (one
+  // float4 each), the slice of v (threads 0..63), beta (threads 0..NS-1)
   u32x4 pk, pg, pv;
   float pb;
-  const int srow = tid >> 5, scol = 4 * (tid & 31);
+  const int srow = (tid & 255) >> 5, scol = 4 * (tid & 31);
+  const bool stager = tid < 256;
   auto issue = [&](i64 j) {
     const i64 t0 = j * NS;
     const int ns = (int)(T - t0 < NS ? T - t0 : NS);
@@ -163,34 +175,35 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
     const brsrc rg = make_rsrc(a.g + ((sl.bi * T + t0) * a.HV + sl.hv) * DK, seg_bytes(ns, a.HV * DK, DK));
     const brsrc rv = make_rsrc(a.v + ((sl.bi * T + t0) * a.HV + sl.hv) * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
     const brsrc rb = make_rsrc(a.beta + (sl.bi * T + t0) * a.HV + sl.hv, seg_bytes(ns, a.HV, 1));
-    pk = bload16(rk, (unsigned)((srow * a.H * DK + scol) * 4));
-    pg = bload16(rg, (unsigned)((srow * a.HV * DK + scol) * 4));
+    pk = bload16(rk, stager ? (unsigned)((srow * a.H * DK + scol) * 4) : BUF_OOB);
+    pg = bload16(rg, stager ? (unsigned)((srow * a.HV * DK + scol) * 4) : BUF_OOB);
     pv = bload16(rv, tid < NS * VS / 4 ? (unsigned)(((tid >> 3) * a.HV * V + 4 * (tid & 7)) * 4) : BUF_OOB);
     pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
   };
-  float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (4 * NTH * 4);
+  float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (NE * NTH);
   if (a.nck > 0) issue(0);
   for (i64 j = 0; j < a.nck; ++j) {
     const int ns = (int)(T - j * NS < NS ? T - j * NS : NS);
     // checkpoint j: the state before step j*NS
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(f32x4*)(ckb + (j * 4 + i) * NTH * 4 + tid * 4) = f32x4{S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]};
+    for (int i = 0; i < NE / 4; ++i)
+      *(f32x4*)(ckb + (j * (NE / 4) + i) * NTH * 4 + tid * 4) = f32x4{S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]};
     __syncthreads();  // the previous sub-segment is done with the staged rows
-    {
+    if (stager) {
       *(f32x4*)&sk[srow][scol] = as_f4(pk);
       const f32x4 gg = as_f4(pg);
       *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
-      if (tid < NS * VS / 4) *(f32x4*)&sv[tid >> 3][4 * (tid & 7)] = as_f4(pv);
-      if (tid < NS) sb[tid] = pb;
     }
+    if (tid < NS * VS / 4) *(f32x4*)&sv[tid >> 3][4 * (tid & 7)] = as_f4(pv);
+    if (tid < NS) sb[tid] = pb;
     if (j + 1 < a.nck) issue(j + 1);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s >= ns) break;
-      float sd[16], r[4];
-      fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], lds4(&sv[s][4 * vq]), r);
+      float sd[NE], r[VT], vv[VT];
+      ld_cols(&sv[s][VT * vq], vv);
+      fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], vv, r);
     }
   }
 }
@@ -212,26 +225,18 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
   const Slot sl = slot_of(a);
   const i64 T = a.T, V = a.V;
 
-  float dS[16];
-  {
-    const brsrc r0 = make_rsrc(a.dSf ? a.dSf + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : a.dq,
-                               a.dSf ? (unsigned)(((DK - 1) * V + VS) * 4) : 0u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x = as_f4(bload16(r0, (unsigned)(((4 * kq + i) * V + 4 * vq) * 4)));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) dS[4 * i + c] = x[c];
-    }
-  }
+  float dS[NE];
+  load_block(dS, a.dSf ? a.dSf + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : nullptr, V, kq, vq);
 
-  // register prefetch of one sub-segment: q, k, g rows (one float4 each per
-  // thread), the slices of v (threads 0..63) and do (threads 64..127), beta
-  // (threads 0..NS-1) and this thread's part of the checkpoint
-  u32x4 pq, pk, pg, pv, pd, pc[4];
+  // register prefetch of one sub-segment: q, k, g rows (threads 0..255, one
+  // float4 each), the slices of v (threads 0..63) and do (threads 64..127),
+  // beta (threads 0..NS-1), and every thread's part of the checkpoint
+  u32x4 pq, pk, pg, pv, pd, pc[NE / 4];
   float pb;
-  const int srow = tid >> 5, scol = 4 * (tid & 31);
+  const int srow = (tid & 255) >> 5, scol = 4 * (tid & 31);
+  const bool stager = tid < 256;
   const int vrow = (tid & 63) >> 3, vcol = 4 * (tid & 7);
-  const float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (4 * NTH * 4);
+  const float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (NE * NTH);
   auto issue = [&](i64 j) {
     const i64 t0 = j * NS;
     const int ns = (int)(T - t0 < NS ? T - t0 : NS);
@@ -242,53 +247,55 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     const brsrc rv = make_rsrc(a.v + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
     const brsrc rd = make_rsrc(a.d_o + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
     const brsrc rb = make_rsrc(a.beta + hv0, seg_bytes(ns, a.HV, 1));
-    const brsrc rc = make_rsrc(ckb + j * 4 * NTH * 4, 4 * NTH * 16);
-    const unsigned qoff = (unsigned)((srow * a.H * DK + scol) * 4);
+    const brsrc rc = make_rsrc(ckb + j * NE * NTH, NE * NTH * 4);
+    const unsigned qoff = stager ? (unsigned)((srow * a.H * DK + scol) * 4) : BUF_OOB;
     const unsigned voff = (unsigned)((vrow * a.HV * V + vcol) * 4);
     pq = bload16(rq, qoff);
     pk = bload16(rk, qoff);
-    pg = bload16(rg, (unsigned)((srow * a.HV * DK + scol) * 4));
+    pg = bload16(rg, stager ? (unsigned)((srow * a.HV * DK + scol) * 4) : BUF_OOB);
     pv = bload16(rv, tid < 64 ? voff : BUF_OOB);
     pd = bload16(rd, tid >= 64 && tid < 128 ? voff : BUF_OOB);
     pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pc[i] = bload16(rc, (unsigned)((i * NTH + tid) * 16));
+    for (int i = 0; i < NE / 4; ++i) pc[i] = bload16(rc, (unsigned)((i * NTH + tid) * 16));
   };
 
-  float* partb = a.part;
   if (a.nck > 0) issue(a.nck - 1);
   for (i64 j = a.nck - 1; j >= 0; --j) {
     const i64 t0 = j * NS;
     const int ns = (int)(T - t0 < NS ? T - t0 : NS);
     // stage this sub-segment (the previous one finished reading the staged
     // rows before its last barrier)
-    float S[16];
+    float S[NE];
     {
-      const f32x4 qq = as_f4(pq), gg = as_f4(pg);
-      *(f32x4*)&sq[srow][scol] = f32x4{a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]};
-      *(f32x4*)&sk[srow][scol] = as_f4(pk);
-      *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
+      if (stager) {
+        const f32x4 qq = as_f4(pq), gg = as_f4(pg);
+        *(f32x4*)&sq[srow][scol] = f32x4{a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]};
+        *(f32x4*)&sk[srow][scol] = as_f4(pk);
+        *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
+      }
       if (tid < 64) *(f32x4*)&sv[vrow][vcol] = as_f4(pv);
       if (tid >= 64 && tid < 128) *(f32x4*)&sdo[vrow][vcol] = as_f4(pd);
       if (tid < NS) sb[tid] = pb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NE / 4; ++i) {
         const f32x4 x = as_f4(pc[i]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) S[4 * i + c] = x[c];
+        for (int e = 0; e < 4; ++e) S[4 * i + e] = x[e];
       }
     }
     if (j > 0) issue(j - 1);
     __syncthreads();  // staged rows visible; the previous reduction is done with red
 
     // recompute the sub-segment's S_dec (registers) and r (LDS, per column)
-    float sd[NS][16];
+    float sd[NS][NE];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s >= ns) break;
-      float r[4];
-      fwd_step(S, sd[s], lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], lds4(&sv[s][4 * vq]), r);
-      if (kq == 0) *(f32x4*)&sr[s][4 * vq] = f32x4{r[0], r[1], r[2], r[3]};
+      float r[VT], vv[VT];
+      ld_cols(&sv[s][VT * vq], vv);
+      fwd_step(S, sd[s], lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], vv, r);
+      if (kq == 0) *(float2*)&sr[s][VT * vq] = make_float2(r[0], r[1]);
     }
     // sr is written and read by the same wave (a column block lives in one
     // half wave), and LDS operations of a wave complete in order
@@ -298,17 +305,19 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     for (int s = NS - 1; s >= 0; --s) {
       if (s >= ns) continue;
       const f32x4 qq = lds4(&sq[s][4 * kq]), kk = lds4(&sk[s][4 * kq]), eg = lds4(&se[s][4 * kq]);
-      const f32x4 dd = lds4(&sdo[s][4 * vq]), rr = lds4(&sr[s][4 * vq]);
+      float dd[VT], rr[VT];
+      ld_cols(&sdo[s][VT * vq], dd);
+      ld_cols(&sr[s][VT * vq], rr);
       const float beta = sb[s];
       float o[16];  // per-row outputs: o[4*qd + i], qd = dq_e, da, S_dec dr, dg
-      float drp[4];
+      float drp[VT];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = beta * kk[i];
         float dq_e = 0.0f, da = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * i + c;
+        for (int c = 0; c < VT; ++c) {
+          const int e = VT * i + c;
           dS[e] = fmaf(qq[i], dd[c], dS[e]);                     // step 1: dS += (scale q) (x) do
           dq_e = fmaf(fmaf(ai, rr[c], sd[s][e]), dd[c], dq_e);  //         dq_e = S_t do
           da = fmaf(rr[c], dS[e], da);                          // step 2: da = dS r
@@ -317,15 +326,15 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
         o[i] = dq_e;
         o[4 + i] = da;
       }
-      float dr[4];
+      float dr[VT];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dr[c] = sum32(drp[c]);
+      for (int c = 0; c < VT; ++c) dr[c] = sum32(drp[c]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float sdr = 0.0f, dg = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * i + c;
+        for (int c = 0; c < VT; ++c) {
+          const int e = VT * i + c;
           sdr = fmaf(sd[s][e], dr[c], sdr);     // step 4: S_dec dr
           dS[e] = fmaf(-kk[i], dr[c], dS[e]);   // step 5: dS_dec = dS - k (x) dr
           dg = fmaf(sd[s][e], dS[e], dg);       //         dg = rowsum(S_dec (.) dS_dec)
@@ -334,34 +343,34 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
         o[8 + i] = sdr;
         o[12 + i] = dg;
       }
-      // dv = dr: this column block's four values, from one lane per half wave
+      // dv = dr: this column block's values, from one lane per half wave
       if (kq == 0) {
-        float* dvp = a.dv + ((sl.bi * T + t0 + s) * a.HV + sl.hv) * V + sl.vs * VS + 4 * vq;
-        *(f32x4*)dvp = f32x4{dr[0], dr[1], dr[2], dr[3]};
+        float* dvp = a.dv + ((sl.bi * T + t0 + s) * a.HV + sl.hv) * V + sl.vs * VS + VT * vq;
+        *(float2*)dvp = make_float2(dr[0], dr[1]);
       }
-      // per-row outputs: pair the half waves (same rows, other 4 columns)
+      // per-row outputs: pair the half waves (same rows, other columns)
 #pragma unroll
       for (int jv = 0; jv < 8; ++jv) red[s][w][8 * half + jv][kq] = pair_halves(o[jv], o[8 + jv]);
     }
     __syncthreads();  // red complete
-    // sum the 4 waves; thread -> row k, (step, output) pairs half, half+2, ...
+    // sum the waves; thread -> row k, (step, output) pairs hsel, hsel+4, ...
     {
       const int kr = tid & (DK - 1), hsel = tid >> 7;
 #pragma unroll
-      for (int m = 0; m < 2 * NS; ++m) {
-        const int pidx = hsel + 2 * m, s = pidx >> 2, qd = pidx & 3;
+      for (int m = 0; m < NS * NQ / (NTH / DK); ++m) {
+        const int pidx = hsel + (NTH / DK) * m, s = pidx >> 2, qd = pidx & 3;
         if (s >= ns) continue;
         float acc = red[s][0][4 * qd + (kr & 3)][kr >> 2];
 #pragma unroll
         for (int ww = 1; ww < NW; ++ww) acc += red[s][ww][4 * qd + (kr & 3)][kr >> 2];
-        partb[((((sl.bi * T + t0 + s) * a.HV + sl.hv) * a.nvs + sl.vs) * NQ + qd) * DK + kr] = acc;
+        a.part[((((sl.bi * T + t0 + s) * a.HV + sl.hv) * a.nvs + sl.vs) * NQ + qd) * DK + kr] = acc;
       }
     }
   }
   if (a.dS0) {
-    float* o = a.dS0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS + 4 * vq;
+    float* o = a.dS0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS + VT * vq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(f32x4*)(o + (4 * kq + i) * V) = f32x4{dS[4 * i], dS[4 * i + 1], dS[4 * i + 2], dS[4 * i + 3]};
+    for (int i = 0; i < 4; ++i) *(float2*)(o + (4 * kq + i) * V) = make_float2(dS[VT * i], dS[VT * i + 1]);
   }
 }
 
@@ -424,7 +433,7 @@ DeltaPlan delta_plan(const ssmvjp_delta_desc& d) {
     off += (bytes + 255) / 256 * 256;
     return o;
   };
-  p.off_ck = carve(d.batch * d.nv_heads * p.nck * DK * d.dv * 4);
+  p.off_ck = carve(d.batch * d.nv_heads * p.nck * DK * d.dv * 4);  // NE * NTH floats per (slice, checkpoint)
   p.off_part = carve(d.batch * d.seqlen * d.nv_heads * p.vsplit * NQ * DK * 4);
   p.bytes = (size_t)off;
   return p;
