@@ -144,3 +144,28 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         bd.ssm_scan_bwd(x, torch.zeros(1, 4, 2), torch.zeros(2), torch.zeros(1, 4, 1, 8), torch.zeros(1, 4, 1, 8),
                         None, x, None)
+
+
+def test_delta_rejects_bad_arguments_without_launching():
+    # every case returns before anything is enqueued, so no GPU is needed
+    L = bd.lib()
+    d = bd.DeltaDesc(batch=1, seqlen=16, nqk_heads=1, nv_heads=2, dk=128, dv=32, scale=0.25, reserved=0)
+    nulls = [None] * 14
+    assert L.delta_rule_bwd(ctypes.byref(d), *nulls, None, 0, None) == bd.EINVAL
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(14)]
+    assert L.delta_rule_bwd(ctypes.byref(d), *fake, None, 0, None) == bd.EWORKSPACE
+    mis = list(fake)
+    mis[2] = ctypes.c_void_p(4096 * 3 + 8)  # v only 8-byte aligned
+    assert L.delta_rule_bwd(ctypes.byref(d), *mis, ctypes.c_void_p(1 << 20), 1 << 34, None) == bd.EINVAL
+    # the staged entry point validates its stage mask the same way
+    ws = ctypes.c_void_p(1 << 20)
+    for bad in (0, 8, -1):
+        assert L.delta_rule_bwd_stages(ctypes.byref(d), bad, *fake, ws, 1 << 34, None) == bd.EINVAL
+
+
+def test_ssd_stage_entry_points_validate_like_the_full_call():
+    L = bd.lib()
+    d = _ssd()
+    # NULL inputs (ten pointers incl. the workspace; eleven for the grads stage)
+    assert L.ssd_chunk_bwd_states(ctypes.byref(d), *([None] * 10), 0, None) == bd.EINVAL
+    assert L.ssd_chunk_bwd_grads(ctypes.byref(d), *([None] * 11), 0, None) == bd.EINVAL
