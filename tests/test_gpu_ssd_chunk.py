@@ -150,3 +150,33 @@ def test_deterministic_across_runs():
     b = _gpu_m2(inp, "bf16", 64)
     for k in M2_OUTS:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("path,dtype", [("chunked", "f32"), ("chunked", "bf16"), ("sequential", "f32")])
+def test_micro_batch_chaining_matches_one_call(path, dtype):
+    """Backward over [0, T) equals two chained calls: [T1, T) with s0 = the
+    state after step T1-1, then [0, T1) seeded with the first call's d_s0 as
+    its final-state gradient (the seed is exactly the state part of the packed
+    upstream gradient, so the chain is lossless)."""
+    b, T, T1, H, P, N, G, L = 1, 192, 128, 4, 64, 128, 1, 64
+    announce(f"chaining {path} {dtype} T={T} split at {T1}")
+    inp = synth.mamba_inputs(b, T, H, P, N, G, False, seed=77)
+    c = synth.as_dtype(inp, dtype, "mamba")
+    ref = oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"])
+    # state after step T1-1, from the float64 forward of the first part
+    _, s_mid = oracle.mamba_seq_fwd(c["x"][:, :T1], c["dt"][:, :T1], c["A"], c["B"][:, :T1], c["C"][:, :T1], c["s0"])
+
+    def run(part, s0, dsf):
+        if path == "chunked":
+            return _gpu_m2({**part, "s0": s0, "ds_final": dsf}, dtype, L)
+        return _gpu_seq({**part, "s0": s0, "ds_final": dsf}, dtype)
+
+    tail = {k: inp[k][:, T1:] for k in ("x", "dt", "B", "C", "dy")}
+    tail["A"] = inp["A"]
+    head = {k: inp[k][:, :T1] for k in ("x", "dt", "B", "C", "dy")}
+    head["A"] = inp["A"]
+    g2 = run(tail, s_mid, inp["ds_final"])
+    g1 = run(head, inp["s0"], g2["d_s0"])
+    chained = {k: np.concatenate([g1[k], g2[k]], axis=1) for k in ("dx", "d_dt", "dB", "dC")}
+    chained["d_s0"] = g1["d_s0"]
+    _compare(chained, ref, M2_OUTS, TOL[dtype])
