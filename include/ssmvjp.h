@@ -162,6 +162,31 @@ ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* ssd_chunk_fwd: chunked SSD forward (the step before the backward)         */
+/* ------------------------------------------------------------------------ */
+
+/* The forward scan in the chunked SSD form of burn-mamba's chunked forward
+ * (K1 chunk cumsum, K2 C.B^T, K3 intra-chunk state, K4 state passing, K5
+ * output = BLUE inter-chunk term + ORANGE causal intra-chunk term): returns
+ * y and the final state s_{T-1} (s0 when T = 0).
+ *   Inputs as for ssd_chunk_bwd (FORM_MAMBA2: x, dt, A; FORM_RAW: v, da).
+ *   y like x_or_v ([b,T,H,P] or [b,T,M,H,P], dtype); s_final [b,H,P,N] f32
+ *   (NULL: not written); s0 NULL = zeros.
+ * The running state of each (batch, head) stays on chip; with bf16 the
+ * workspace holds the scores C.B^T of every chunk (from ssd_chunk_fwd_workspace;
+ * none with float32).  The kernel walks chunks of chunk_len steps when
+ * chunk_len * M <= 64, else of 64 / M steps; the results do not depend on the
+ * chunk length apart from rounding.
+ * Constraints (SSMVJP_EUNSUPPORTED otherwise): P % 16 == 0, N % 16 == 0,
+ * N <= 128, M <= 64.  x_or_v, B, C and y 16-byte aligned. */
+ssmvjp_status ssd_chunk_fwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes);
+ssmvjp_status ssd_chunk_fwd(const ssmvjp_ssd_desc* desc,
+                            const void* x_or_v, const float* dt_or_da, const float* A,
+                            const void* B, const void* C, const float* s0,
+                            void* y, float* s_final,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* delta_rule_bwd: KDA gated delta rule backward                             */
 /* ------------------------------------------------------------------------ */
 

@@ -20,9 +20,10 @@ DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
 FORM_MAMBA2, FORM_RAW = 0, 1
 DELTA_CKPT, DELTA_BWD, DELTA_REDUCE, DELTA_ALL = 1, 2, 4, 7
 
-EXPORTS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-           "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd",
-           "delta_rule_bwd_stages", "ssmvjp_status_str", "ssmvjp_version")
+_STATUS_FNS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
+               "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "ssd_chunk_fwd_workspace", "ssd_chunk_fwd",
+               "delta_rule_bwd_workspace", "delta_rule_bwd", "delta_rule_bwd_stages")
+EXPORTS = _STATUS_FNS + ("ssmvjp_status_str", "ssmvjp_version")
 
 
 class ScanDesc(ctypes.Structure):
@@ -68,12 +69,12 @@ def lib():
         L.ssd_chunk_bwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 14 + [sz, vp]
         L.ssd_chunk_bwd_states.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 10 + [sz, vp]
         L.ssd_chunk_bwd_grads.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11 + [sz, vp]
+        L.ssd_chunk_fwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
+        L.ssd_chunk_fwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 9 + [sz, vp]
         L.delta_rule_bwd_workspace.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.POINTER(sz)]
         L.delta_rule_bwd.argtypes = [ctypes.POINTER(DeltaDesc)] + [vp] * 15 + [sz, vp]
         L.delta_rule_bwd_stages.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.c_int32] + [vp] * 15 + [sz, vp]
-        for name in ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-                     "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "delta_rule_bwd_workspace", "delta_rule_bwd",
-                     "delta_rule_bwd_stages"):
+        for name in _STATUS_FNS:
             getattr(L, name).restype = ctypes.c_int
         L.ssmvjp_status_str.argtypes = [ctypes.c_int]
         L.ssmvjp_status_str.restype = ctypes.c_char_p
@@ -230,6 +231,43 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, w
                              _ptr(dy), _ptr(ds_final), _ptr(out[names[0]]), _ptr(out[names[1]]), _ptr(out["dB"]),
                              _ptr(out["dC"]), _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
     _check("ssd_chunk_bwd", st)
+    return out
+
+
+def ssd_chunk_fwd_workspace(desc):
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_fwd_workspace", lib().ssd_chunk_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ssd_chunk_fwd(xv, dtda, A, B, C, s0=None, *, chunk_len=64, out=None, want_final=True, workspace=None,
+                  stream=None):
+    """Chunked SSD forward.  Returns dict y (like xv) and s_final [b,H,P,N] float32.
+
+    Mamba-2 form (A given): xv = x [b,T,H,P], dtda = dt [b,T,H] (raw), B, C [b,T,G,N].
+    RAW form (A None): xv = v [b,T,M,H,P], dtda = da [b,T,H], B, C [b,T,M,G,N].
+    s0 None = zeros; want_final=False leaves s_final out (None).
+    """
+    form = FORM_MAMBA2 if A is not None else FORM_RAW
+    desc = ssd_desc(xv, B, chunk_len, form)
+    b, T, H, P, N = desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate
+    dev, big = xv.device, xv.dtype
+    _need(xv, "x/v", big, tuple(xv.shape), dev)
+    _need(B, "B", big, tuple(B.shape), dev)
+    _need(C, "C", big, tuple(B.shape), dev)
+    _need(dtda, "dt/da", torch.float32, (b, T, H), dev)
+    if A is not None:
+        _need(A, "A", torch.float32, (H,), dev)
+    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
+    if out is None:
+        out = {"y": torch.empty_like(xv),
+               "s_final": torch.empty((b, H, P, N), dtype=torch.float32, device=dev) if want_final else None}
+    _need(out["y"], "y", big, tuple(xv.shape), dev)
+    _need(out["s_final"], "s_final", torch.float32, (b, H, P, N), dev)
+    ws, wsb = _workspace(ssd_chunk_fwd_workspace(desc), dev, workspace)
+    st = lib().ssd_chunk_fwd(ctypes.byref(desc), _ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0),
+                             _ptr(out["y"]), _ptr(out["s_final"]), _ptr(ws), wsb, _stream(stream))
+    _check("ssd_chunk_fwd", st)
     return out
 
 

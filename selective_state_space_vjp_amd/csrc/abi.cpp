@@ -171,6 +171,54 @@ ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc, const void* x_or_
                  workspace, workspace_bytes, stream, SSD_STAGE_GRADS);
 }
 
+// ------------------------------- ssd_chunk_fwd ------------------------------
+
+namespace {
+ssmvjp_status ssd_fwd_check(const ssmvjp_ssd_desc* desc) {
+  if (!desc) return SSMVJP_EINVAL;
+  const ssmvjp_ssd_desc& d = *desc;
+  if (d.batch < 0 || d.seqlen < 0 || d.nheads <= 0 || d.headdim <= 0 || d.dstate <= 0 || d.ngroups <= 0 ||
+      d.mimo_rank <= 0 || d.chunk_len <= 0)
+    return SSMVJP_EINVAL;
+  if (d.nheads % d.ngroups) return SSMVJP_EINVAL;
+  if (d.form != SSMVJP_FORM_MAMBA2 && d.form != SSMVJP_FORM_RAW) return SSMVJP_EINVAL;
+  if (d.form == SSMVJP_FORM_MAMBA2 && d.mimo_rank != 1) return SSMVJP_EINVAL;
+  if (!valid_dtype(d.dtype)) return SSMVJP_EINVAL;
+  if (!ssd_fwd_shape_supported(d)) return SSMVJP_EUNSUPPORTED;
+  return SSMVJP_OK;
+}
+}  // namespace
+
+ssmvjp_status ssd_chunk_fwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes) {
+  if (!bytes) return SSMVJP_EINVAL;
+  ssmvjp_status s = ssd_fwd_check(desc);
+  if (s != SSMVJP_OK) return s;
+  *bytes = ssd_fwd_workspace_bytes(*desc);
+  return SSMVJP_OK;
+}
+
+ssmvjp_status ssd_chunk_fwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
+                            const float* A, const void* B, const void* C, const float* s0, void* y,
+                            float* s_final, void* workspace, size_t workspace_bytes, void* stream) {
+  ssmvjp_status s = ssd_fwd_check(desc);
+  if (s != SSMVJP_OK) return s;
+  const ssmvjp_ssd_desc& d = *desc;
+  const bool has_tokens = d.batch * d.seqlen > 0;
+  if (has_tokens && (!x_or_v || !dt_or_da || !B || !C || !y)) return SSMVJP_EINVAL;
+  if (d.form == SSMVJP_FORM_MAMBA2 && has_tokens && !A) return SSMVJP_EINVAL;
+  const void* pa[] = {x_or_v, B, C, y};
+  for (const void* p : pa)
+    if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
+  const void* pf[] = {dt_or_da, A, s0, s_final};
+  for (const void* p : pf)
+    if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
+  const size_t need = ssd_fwd_workspace_bytes(d);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
+  if (d.batch == 0) return SSMVJP_OK;
+  SsdFwdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, y, s_final, workspace};
+  return hip_status(launch_ssd_fwd(d, ptr, (hipStream_t)stream));
+}
+
 // ------------------------------- delta_rule_bwd -----------------------------
 
 ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* bytes) {

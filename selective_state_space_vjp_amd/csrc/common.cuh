@@ -94,6 +94,18 @@ __device__ __forceinline__ float wave_sum(float v) { return sum4q(sum16(v)); }
 // exp(x) through the hardware exp2 (v_exp_f32, relative error a few 1e-8)
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// softplus(z) = log(1 + e^z) through the hardware exp2 / log2, with the log1p
+// correction of Goldberg, "What every computer scientist should know about
+// floating-point arithmetic" (Theorem 4): with u = 1 + e rounded,
+// log1p(e) = e * log(u) / (u - 1) to a few ulps, and e itself when u rounds to 1.
+__device__ __forceinline__ float softplus_hw(float z) {
+  const float e = exp_hw(z);
+  const float u = 1.0f + e;
+  const float l = __builtin_amdgcn_logf(u) * 0.6931471805599453f;
+  const float sp = u == 1.0f ? e : l * (e * __builtin_amdgcn_rcpf(u - 1.0f));
+  return z > 20.0f ? z : sp;
+}
+
 // inclusive prefix sum over the 64 lanes, all in DPP: Hillis-Steele inside
 // each 16-lane row (row_shr 1, 2, 4, 8 with zero fill), then the row totals
 // carried across rows with row_bcast:15 (rows 1 and 3) and row_bcast:31

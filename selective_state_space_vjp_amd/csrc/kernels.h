@@ -75,6 +75,22 @@ enum { SSD_STAGE_STATES = 1, SSD_STAGE_GRADS = 2, SSD_STAGE_ALL = 3 };
 hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const SsdPointers& ptr,
                           hipStream_t stream, int stages);
 
+struct SsdFwdPointers {
+  const void* xv;
+  const float* dtda;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* s0;
+  void* y;
+  float* s_final;
+  void* workspace;
+};
+
+bool ssd_fwd_shape_supported(const ssmvjp_ssd_desc& d);
+size_t ssd_fwd_workspace_bytes(const ssmvjp_ssd_desc& d);
+hipError_t launch_ssd_fwd(const ssmvjp_ssd_desc& d, const SsdFwdPointers& ptr, hipStream_t stream);
+
 // ------------------------------ delta rule ---------------------------------
 struct DeltaPlan {
   int64_t CK;          // checkpoint interval (steps)

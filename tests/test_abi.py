@@ -169,3 +169,46 @@ def test_ssd_stage_entry_points_validate_like_the_full_call():
     # NULL inputs (ten pointers incl. the workspace; eleven for the grads stage)
     assert L.ssd_chunk_bwd_states(ctypes.byref(d), *([None] * 10), 0, None) == bd.EINVAL
     assert L.ssd_chunk_bwd_grads(ctypes.byref(d), *([None] * 11), 0, None) == bd.EINVAL
+
+
+@pytest.mark.parametrize("kw,desc_status,call_status", [
+    # supported descriptors reach the NULL-pointer check of the call
+    (dict(), bd.OK, bd.EINVAL),
+    (dict(form=1, mimo_rank=4), bd.OK, bd.EINVAL),
+    (dict(form=1, mimo_rank=3, chunk_len=16), bd.OK, bd.EINVAL),  # steps straddle 16-row tiles
+    (dict(headdim=48, dstate=96, dtype=0), bd.OK, bd.EINVAL),
+    (dict(headdim=20), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
+    (dict(dstate=40), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
+    (dict(dstate=256), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
+    (dict(form=1, mimo_rank=65), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
+    (dict(nheads=3, ngroups=2), bd.EINVAL, bd.EINVAL),
+    (dict(form=0, mimo_rank=2), bd.EINVAL, bd.EINVAL),
+    (dict(chunk_len=0), bd.EINVAL, bd.EINVAL),
+    (dict(batch=0), bd.OK, bd.OK),  # nothing to do: no pointer is read
+])
+def test_ssd_fwd_validates_before_launching(kw, desc_status, call_status):
+    L = bd.lib()
+    d = _ssd(**kw)
+    n = ctypes.c_size_t(0)
+    assert L.ssd_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == desc_status
+    assert L.ssd_chunk_fwd(ctypes.byref(d), *([None] * 8), None, 0, None) == call_status
+
+
+def test_ssd_fwd_rejects_misaligned_big_tensors():
+    L = bd.lib()
+    d = _ssd()
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]
+    mis = list(fake)
+    mis[0] = ctypes.c_void_p(4096 + 8)  # x only 8-byte aligned
+    ws = ctypes.c_void_p(1 << 20)
+    assert L.ssd_chunk_fwd(ctypes.byref(d), *mis, ws, 1 << 30, None) == bd.EINVAL
+    mis = list(fake)
+    mis[7] = ctypes.c_void_p(4096 * 8 + 2)  # s_final misaligned for float32
+    assert L.ssd_chunk_fwd(ctypes.byref(d), *mis, ws, 1 << 30, None) == bd.EINVAL
+    # bf16 needs the scores workspace; float32 needs none
+    assert L.ssd_chunk_fwd(ctypes.byref(d), *fake, None, 0, None) == bd.EWORKSPACE
+    n = ctypes.c_size_t(0)
+    assert L.ssd_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == bd.OK
+    assert n.value == 1 * 2 * 1 * 16 * 256 * 4  # b * chunks * groups score blocks
+    d32 = _ssd(dtype=0)
+    assert L.ssd_chunk_fwd_workspace(ctypes.byref(d32), ctypes.byref(n)) == bd.OK and n.value == 0
