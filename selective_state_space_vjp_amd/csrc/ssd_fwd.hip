@@ -406,15 +406,18 @@ __global__ void __launch_bounds__(64 * CB_NW) ssd_fwd_scores_kernel(FwdArgs a, f
 }
 
 // kernel F2: the walk over the chunks of one (batch, head, p block), software
-// pipelined so that each chunk costs one barrier.  Interval c (c = 0 .. nc):
-//   stage    B, x (scaled for the state update) of chunk c+1 and C, x and the
-//            per-row cumA and delta of chunk c into their LDS buffers (parity
-//            of the chunk), from registers loaded one interval ahead (loading
-//            two intervals ahead measured no faster);
-//   phase 1  chunk c: the state as the operand type -> LDS, then the state
-//            update on MFMA;
-//   phase 2  chunk c-1: the decay mask applied to its score tiles (registers),
-//            ORANGE and BLUE on MFMA, y stored;
+// pipelined so that each chunk costs one barrier, with two wave roles that
+// share each SIMD: waves 0-3 produce the outputs (one 16-row block of y each,
+// all p columns of the block), waves 4-7 hold the running state and update it.
+// Interval c (c = 0 .. nc):
+//   stage    (all waves) B, x (scaled for the state update) of chunk c+1 and
+//            C, x and the per-row cumA and delta of chunk c into their LDS
+//            buffers (parity of the chunk), from registers loaded one interval
+//            ahead; wave 0 also stages dt of chunk c+2;
+//   phase 1  (state waves) chunk c: the state as the operand type -> LDS, then
+//            the state update on MFMA;
+//   phase 2  (output waves) chunk c-1: the decay mask applied to its score
+//            tiles (registers), ORANGE and BLUE on MFMA, y stored;
 //   barrier.
 // Everything an interval reads was written before the previous barrier, and
 // every buffer it writes was last read before it.
@@ -424,8 +427,8 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
   constexpr int N = 16 * NT, PB = 16 * PTB;
   constexpr int PPB = pitch_down(N), PPC = pitch_along(N), PPX = pitch_down(PB);
   constexpr int SB = 64 * PPB, SC = 64 * PPC, SX = 64 * PPX;
-  constexpr int NST = NT * PTB, MAXST = (NST + FW_NW - 1) / FW_NW;
-  constexpr int NOUT = 4 * PTB;  // output tiles: one per wave (at most 8)
+  constexpr int NST = NT * PTB;
+  constexpr int NTW = (NT + 3) / 4;  // n tiles per state wave (all PTB p tiles of each)
   constexpr int CROW_B = N / 8, CROW_X = PB / 8;
   constexpr int MAXCB = (64 * CROW_B + FW_NTH - 1) / FW_NTH, MAXCX = (64 * CROW_X + FW_NTH - 1) / FW_NTH;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -436,6 +439,7 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
   T* const Ss = Xd + 2 * SX;   // [2][NST * 256]
   float* const crow = (float*)(Ss + 2 * NST * 256);  // [2][64] cumA per fused row
   float* const drow = crow + 2 * 64;                 // [2][64] delta per fused row
+  float* const zrow = drow + 2 * 64;                 // [2][64] dt (or da) per step
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             c16 = lane & 15;
@@ -450,18 +454,23 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
   const int rs_x = (int)(a.H * a.P), rs_bc = (int)(a.G * a.N);
   const float Ah = a.raw ? 0.0f : a.A[h];
 
-  f32x4 S[MAXST];
+  // roles: output wave rt = w (w < 4); state wave sw = w - 4 holding the
+  // tiles (n_t, p_t) with n_t = NTW * sw + i (i < NTW, n_t < NT), all p_t
+  const bool out_wave = w < 4;
+  const int ort = w, sw = w - 4, nt0 = NTW * sw;
+  f32x4 S[NTW][PTB];
   const i64 sbase = (bi * a.H + h) * a.P * a.N;
 #pragma unroll
-  for (int k = 0; k < MAXST; ++k) {
-    const int kk = w + FW_NW * k;
-    S[k] = zero4();
-    if (kk < NST && a.s0) {
-      const int nt = kk / PTB, pt = kk % PTB;
+  for (int i = 0; i < NTW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[k][j] = a.s0[sbase + (i64)(p0 + 16 * pt + c16) * N + 16 * nt + 4 * q + j];
+    for (int pt = 0; pt < PTB; ++pt) {
+      S[i][pt] = zero4();
+      if (!out_wave && nt0 + i < NT && a.s0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          S[i][pt][j] = a.s0[sbase + (i64)(p0 + 16 * pt + c16) * N + 16 * (nt0 + i) + 4 * q + j];
+      }
     }
-  }
 
   const T* x_b = (const T*)a.xv + ((bi * a.T) * a.M * a.H + h) * a.P + p0;
   const T* B_b = (const T*)a.B + ((bi * a.T) * a.M * a.G + g) * a.N;
@@ -470,9 +479,6 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
   const float* dt_b = a.dtda + bi * a.T * a.H + h;
   const float* cb_b = cbt + (bi * a.nc * a.G + g) * 16 * 256;  // chunk c at + c * G * 16 * 256
 
-  // this wave's output tile (phase 2): (pt, rt) = (w % PTB, w / PTB)
-  const bool has_out = w < NOUT;
-  const int opt = w % PTB, ort = w / PTB;
   // loop-invariant row -> step maps: the last fused row of this lane's output
   // row's step (the causal mask is s <= last), the step of each staged x row
   // and of this lane's row (lane = fused row)
@@ -482,9 +488,9 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
   for (int it = 0; it < MAXCX; ++it) lx[it] = (((tid + it * FW_NTH) / CROW_X) & 63) / M;
   const int lrow = lane / M;
 
-  auto rows_of = [&](int ch) {
+  auto steps_of = [&](int ch) {
     const int t0 = ch * Lf;
-    return (T32 - t0 < Lf ? T32 - t0 : Lf) * M;
+    return T32 - t0 < Lf ? T32 - t0 : Lf;
   };
   struct Set {
     float z;
@@ -492,19 +498,22 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
     f32x4 cb[4];
   };
   auto clampc = [&](int ch) { return ch < 0 ? 0 : (ch >= nc ? nc - 1 : ch); };
-  // loads for one interval: B, x, dt of chunk cb_ (B rows for the state update),
-  // C of chunk cc, scores of chunk cs
+  auto load_dt = [&](int ch) {
+    const int t0 = ch * Lf, Lc = steps_of(ch);
+    return bload_f32(make_rsrc(dt_b + (i64)t0 * H32, (unsigned)(((Lc - 1) * H32 + 1) * 4)),
+                     lane < Lc ? (unsigned)(lane * H32 * 4) : BUF_OOB);
+  };
+  // loads for one interval: B and x of chunk cb_ (the state update), dt of
+  // chunk cb_ + 1 (wave 0), C of chunk cc, scores of chunk cs (output waves)
   auto issue = [&](Set& s, int cb_, int cc, int cs) {
+    const int cz = clampc(cb_ + 1);
     cb_ = clampc(cb_);
     cc = clampc(cc);
     cs = clampc(cs);
+    if (w == 0) s.z = load_dt(cz);
     {
-      const int t0 = cb_ * Lf;
-      const int Lc = T32 - t0 < Lf ? T32 - t0 : Lf;
-      const int rows = Lc * M;
-      s.z = bload_f32(make_rsrc(dt_b + (i64)t0 * H32, (unsigned)(((Lc - 1) * H32 + 1) * 4)),
-                      lane < Lc ? (unsigned)(lane * H32 * 4) : BUF_OOB);
-      const i64 R0 = (i64)t0 * M;
+      const int rows = steps_of(cb_) * M;
+      const i64 R0 = (i64)cb_ * Lf * M;
       const brsrc rb = make_rsrc(B_b + R0 * rs_bc, (unsigned)(((rows - 1) * rs_bc + N) * 2));
       const brsrc rx = make_rsrc(x_b + R0 * rs_x, (unsigned)(((rows - 1) * rs_x + PB) * 2));
 #pragma unroll
@@ -521,7 +530,7 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
       }
     }
     {
-      const int rows = rows_of(cc);
+      const int rows = steps_of(cc) * M;
       const brsrc rc = make_rsrc(C_b + (i64)cc * Lf * M * rs_bc, (unsigned)(((rows - 1) * rs_bc + N) * 2));
 #pragma unroll
       for (int it = 0; it < MAXCB; ++it) {
@@ -530,22 +539,20 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
                                   ? (unsigned)(((idx / CROW_B) * rs_bc + (idx % CROW_B) * 8) * 2) : BUF_OOB);
       }
     }
-    {
+    if (out_wave) {
       const brsrc rs = make_rsrc(cb_b + (i64)cs * a.G * 16 * 256, 16 * 256 * 4);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bool live = has_out && (st <= ort || !a.causal);
+        const bool live = st <= ort || !a.causal;
         const u32x4 u = bload16(rs, live ? (unsigned)(((st * 4 + ort) * 64 + lane) * 16) : BUF_OOB);
         s.cb[st] = __builtin_bit_cast(f32x4, u);
       }
     }
   };
 
-  // step scalars of the chunk whose B / x a set holds (lane = step)
-  auto scalars_of = [&](const Set& s, int ch) {
-    const int t0 = ch * Lf;
-    const int Lc = T32 - t0 < Lf ? T32 - t0 : Lf;
-    return fwd_scalars_hw(a.raw, s.z, lane < Lc, Ah, lane);
+  // step scalars of chunk ch from the dt staged in zrow slot `slot` (lane = step)
+  auto scalars_of = [&](int slot, int ch) {
+    return fwd_scalars_hw(a.raw, zrow[slot * 64 + lane], lane < steps_of(ch), Ah, lane);
   };
   // B and x of chunk ch (scalars sc) -> the state-update buffers of its parity
   auto stage_state = [&](const Set& s, const FwdScalars& sc, int ch) {
@@ -584,27 +591,41 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
       drow[(ch & 1) * 64 + lane] = dr;
     }
   };
+  // all of a wave's LDS fragments are read before its first MFMA waits on them
   auto phase1 = [&](const FwdScalars& sc, int ch) {
+    if (out_wave) return;
     const T* bs = Bs + (ch & 1) * SB;
     const T* xw = Xw + (ch & 1) * SX;
     T* const ss = Ss + (ch & 1) * NST * 256;
     const float e_end = exp_hw(sc.end);
 #pragma unroll
-    for (int k = 0; k < MAXST; ++k) {
-      const int kk = w + FW_NW * k;
-      if (kk >= NST) continue;
-      const int nt = kk / PTB, pt = kk % PTB;
-      store4(ss + kk * 256 + lane * 4, S[k]);
-      f32x4 acc;
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = e_end * S[k][j];
+      for (int pt = 0; pt < PTB; ++pt)
+        if (nt0 + i < NT) store4(ss + ((nt0 + i) * PTB + pt) * 256 + lane * 4, S[i][pt]);
+    Frag<T> fb[NTW][4], fx[PTB][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(acc, ld_rowk(bs, PPB, 16 * kb, 16 * nt, lane), ld_rowk(xw, PPX, 16 * kb, 16 * pt, lane));
-      S[k] = acc;
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) fb[i][kb] = ld_rowk(bs, PPB, 16 * kb, 16 * (nt0 + i < NT ? nt0 + i : 0), lane);
+#pragma unroll
+      for (int pt = 0; pt < PTB; ++pt) fx[pt][kb] = ld_rowk(xw, PPX, 16 * kb, 16 * pt, lane);
     }
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int pt = 0; pt < PTB; ++pt) {
+        if (nt0 + i >= NT) continue;
+        f32x4 acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = e_end * S[i][pt][j];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(acc, fb[i][kb], fx[pt][kb]);
+        S[i][pt] = acc;
+      }
   };
   auto phase2 = [&](const Set& s, int ch) {
-    if (!has_out) return;
+    if (!out_wave) return;
     const T* xd = Xd + (ch & 1) * SX;
     const T* cs = Cs + (ch & 1) * SC;
     const T* ss = Ss + (ch & 1) * NST * 256;
@@ -612,43 +633,82 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
     const float* dr_ = drow + (ch & 1) * 64;
     const int r = 16 * ort + c16;
     const float cr = cr_[r];
-    f32x4 ao = zero4(), ab = zero4();
+    f32x4 ao[PTB], ab[PTB];
+#pragma unroll
+    for (int pt = 0; pt < PTB; ++pt) ao[pt] = ab[pt] = zero4();
     // ORANGE: G^T[s][r] = (B_s . C_r) delta_s exp(cumA_r - cumA_s) for s <= the last row of r's step
+    float4 cs4[4], ds4[4];
+    Frag<T> xf[4][PTB];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       if (st > ort && a.causal) continue;
-      const float4 cs4 = *(const float4*)(cr_ + 16 * st + 4 * q);
-      const float4 ds4 = *(const float4*)(dr_ + 16 * st + 4 * q);
-      const float csj[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dsj[4] = {ds4.x, ds4.y, ds4.z, ds4.w};
+      cs4[st] = *(const float4*)(cr_ + 16 * st + 4 * q);
+      ds4[st] = *(const float4*)(dr_ + 16 * st + 4 * q);
+#pragma unroll
+      for (int pt = 0; pt < PTB; ++pt) xf[st][pt] = ld_rowk(xd, PPX, 16 * st, 16 * pt, lane);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st > ort && a.causal) continue;
+      const float csj[4] = {cs4[st].x, cs4[st].y, cs4[st].z, cs4[st].w};
+      const float dsj[4] = {ds4[st].x, ds4[st].y, ds4[st].z, ds4[st].w};
       float gv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         gv[j] = 16 * st + 4 * q + j <= last_r ? s.cb[st][j] * dsj[j] * exp_hw(cr - csj[j]) : 0.0f;
-      mma(ao, ld_rowk(xd, PPX, 16 * st, 16 * opt, lane), frag_make<T>(gv));
+      const Frag<T> gf = frag_make<T>(gv);
+#pragma unroll
+      for (int pt = 0; pt < PTB; ++pt) mma(ao[pt], xf[st][pt], gf);
     }
+    // BLUE: sum_n S[p][n] C[r][n], fragments read four n tiles at a time
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) mma(ab, ld_ntv(ss + (nt * PTB + opt) * 256, lane), ld_colk(cs, PPC, 16 * ort, 16 * nt, lane));
+    for (int n0 = 0; n0 < NT; n0 += 4) {
+      Frag<T> cf[4], sf[4][PTB];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (n0 + u >= NT) continue;
+        cf[u] = ld_colk(cs, PPC, 16 * ort, 16 * (n0 + u), lane);
+#pragma unroll
+        for (int pt = 0; pt < PTB; ++pt) sf[u][pt] = ld_ntv(ss + ((n0 + u) * PTB + pt) * 256, lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (n0 + u >= NT) continue;
+#pragma unroll
+        for (int pt = 0; pt < PTB; ++pt) mma(ab[pt], sf[u][pt], cf[u]);
+      }
+    }
     const float er = exp_hw(cr);
-    f32x4 yv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) yv[j] = ao[j] + er * ab[j];
-    const int rows = rows_of(ch);
+    const int rows = steps_of(ch) * M;
     const brsrc ry = make_rsrc(y_b + (i64)ch * Lf * M * rs_x, (unsigned)(((rows - 1) * rs_x + PB) * 2));
-    bstore4(ry, r < rows ? (unsigned)((r * rs_x + 16 * opt + 4 * q) * 2) : BUF_OOB, yv, (const T*)0);
+#pragma unroll
+    for (int pt = 0; pt < PTB; ++pt) {
+      f32x4 yv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yv[j] = ao[pt][j] + er * ab[pt][j];
+      bstore4(ry, r < rows ? (unsigned)((r * rs_x + 16 * pt + 4 * q) * 2) : BUF_OOB, yv, (const T*)0);
+    }
   };
 
   if (nc > 0) {
     Set sa, sb;
-    // prologue: B and x of chunk 0 into the state-update buffers; the loads of interval 0
+    // prologue: dt of chunks 0 and 1 into zrow, B and x of chunk 0 into the
+    // state-update buffers, the loads of interval 0
     issue(sb, 0, 0, 0);
-    FwdScalars sc_cur = scalars_of(sb, 0);
+    if (w == 0) {
+      zrow[lane] = load_dt(0);
+      zrow[64 + lane] = sb.z;
+    }
+    __syncthreads();
+    FwdScalars sc_cur = scalars_of(0, 0);
     stage_state(sb, sc_cur, 0);
     issue(sa, 1, 0, 0);
     __syncthreads();
     auto interval = [&](Set& s, Set& o, int c) {
-      // s: B, x, dt of chunk c+1, C of chunk c, scores of chunk c-1;
+      // s: B, x of chunk c+1, dt of chunk c+2, C of chunk c, scores of chunk c-1;
       // o: x of chunk c, refilled here for interval c+1
-      const FwdScalars sc_next = scalars_of(s, clampc(c + 1));
+      const FwdScalars sc_next = scalars_of((c + 1) & 1, clampc(c + 1));
+      if (w == 0) zrow[(c & 1) * 64 + lane] = s.z;
       stage_state(s, sc_next, c + 1);
       stage_out(s, o, sc_cur, c);
       issue(o, c + 2, c + 1, c);
@@ -663,15 +723,16 @@ __global__ void __launch_bounds__(FW_NTH) ssd_fwd_walk_kernel(FwdArgs a, const f
     }
   }
 
-  if (a.s_final) {
+  if (a.s_final && !out_wave) {
 #pragma unroll
-    for (int k = 0; k < MAXST; ++k) {
-      const int kk = w + FW_NW * k;
-      if (kk >= NST) continue;
-      const int nt = kk / PTB, pt = kk % PTB;
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a.s_final[sbase + (i64)(p0 + 16 * pt + c16) * N + 16 * nt + 4 * q + j] = S[k][j];
-    }
+      for (int pt = 0; pt < PTB; ++pt) {
+        if (nt0 + i >= NT) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a.s_final[sbase + (i64)(p0 + 16 * pt + c16) * N + 16 * (nt0 + i) + 4 * q + j] = S[i][pt][j];
+      }
   }
 }
 
@@ -679,7 +740,7 @@ template <int NT, int PTB>
 size_t walk_lds() {
   constexpr int N = 16 * NT, PB = 16 * PTB;
   return 2 * (64 * (size_t)(pitch_down(N) + pitch_along(N) + 2 * pitch_down(PB)) + (size_t)NT * PTB * 256) * 2 +
-         2 * 2 * 64 * 4;
+         3 * 2 * 64 * 4;
 }
 
 template <int NT, int PTB>
