@@ -191,15 +191,87 @@ def bench_kda(args, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_fwd(args, dev):
+    """The chunked forward (ssd_chunk_fwd: y and the final state) at the Mamba-2
+    chunked workload shape: one step is one forward over the batch."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_vjp_amd import binding, synth
+
+    w = dict(synth.WORKLOADS["mamba2_chunk"])
+    inp = synth.workload_inputs("mamba2_chunk")
+    c = synth.as_dtype(inp, "bf16", "mamba")
+    del inp
+
+    def dt_(a, dtype=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(dtype).to(dev).contiguous()
+
+    bf = torch.bfloat16
+    x, B, C = dt_(c["x"], bf), dt_(c["B"], bf), dt_(c["C"], bf)
+    dt, A, s0 = dt_(c["dt"]), dt_(c["A"]), dt_(c["s0"])
+    desc = binding.ssd_desc(x, B, w["L"], binding.FORM_MAMBA2)
+    ws = torch.empty(max(binding.ssd_chunk_fwd_workspace(desc), 1), dtype=torch.uint8, device=dev)
+    out = {"y": torch.empty_like(x), "s_final": torch.empty_like(s0)}
+
+    def step():
+        binding.ssd_chunk_fwd(x, dt, A, B, C, s0, chunk_len=w["L"], out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    b, T, H, P, N, G = w["b"], w["T"], w["H"], w["P"], w["N"], w["G"]
+    # compulsory HBM bytes: x, B, C, dt read and y written once, s0 read and s_final written
+    fwd_bytes = 2 * b * T * H * P * 2 + 2 * b * T * G * N * 2 + b * T * H * 4 + 2 * b * H * P * N * 4
+    gbps = fwd_bytes / (call_ms * 1e6)
+    line = {
+        "metric": "scan-forward tokens/s (B·T/s) at Mamba-2 bf16 shape; % of HBM roofline", "value":
+        round(b * T / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mamba2_fwd", "batch": b, "seqlen": T, "heads": H, "headdim": P, "dstate": N,
+                   "ngroups": G, "chunk_len": w["L"], "form": "mamba2", "accumulate": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "ssd_fwd_scores_kernel + ssd_fwd_walk_kernel (one ssd_chunk_fwd call)",
+                     "algorithmic_bytes_per_launch": fwd_bytes, "avg_launch_ms": round(call_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.default_threads()
+        c0 = {k: (v[:1] if hasattr(v, "ndim") and v.ndim >= 3 else v) for k, v in c.items()}
+        t0 = time.perf_counter()
+        oracle.mamba_seq_fwd(c0["x"], c0["dt"], c0["A"], c0["B"], c0["C"], c0["s0"], nthreads=threads)
+        sec = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": T / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                "sample": f"1 of {b} sequences (T={T}, all {H} heads), float64 sequential "
+                                          f"forward recurrence, {sec:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk", "kda"),
-                    help="mamba2_chunk (default, the headline line), mimo_chunk (rank-4 MIMO, RAW form) or "
-                         "kda (gated delta rule, b=2 T=4096 H=16 HV=32 K=V=128, fp32)")
+    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk", "kda", "mamba2_fwd"),
+                    help="mamba2_chunk (default, the headline line), mimo_chunk (rank-4 MIMO, RAW form), "
+                         "kda (gated delta rule, b=2 T=4096 H=16 HV=32 K=V=128, fp32) or mamba2_fwd (the "
+                         "chunked forward at the mamba2_chunk shape)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -228,6 +300,8 @@ def main():
         return
     if args.workload == "kda":
         return bench_kda(args, dev)
+    if args.workload == "mamba2_fwd":
+        return bench_fwd(args, dev)
     w = dict(synth.WORKLOADS[args.workload])
     w.setdefault("M", 1)
     inp = synth.workload_inputs(args.workload)
