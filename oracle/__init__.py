@@ -13,7 +13,10 @@ Functions and the passages they follow:
   store-all reverse recurrence seeded with the final-state gradient
   (llama.cpp PR "S1-31: SSM_SCAN_BACK", the op description and the
   "grad is the WHOLE packed gradient" / store-all paragraphs).  Mamba-2
-  (one decay per head) and Mamba-1 (one decay per state).
+  (one decay per head) and Mamba-1 (one decay per state).  Besides the page's
+  five gradients the backward returns dA, the gradient of the decay
+  coefficients (burn-mamba's combined_backward returns the decay gradient
+  d_da; dA = sum over batch and time of d_da * delta).
 * ``raw_seq_fwd`` / ``raw_seq_bwd`` -- the same recurrence in the pre-scaled
   (v, da) form with a rank-M input per step: the sequential computation that the
   chunked kernels re-associate (burn-mamba "combined_backward.rs", the K3/K4/K5
@@ -86,7 +89,7 @@ def _load():
         lib = ctypes.CDLL(str(_LIB))
         i64, dp, ci, cd = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.orc_mamba_seq_fwd.argtypes = [i64] * 6 + [ci] + [dp] * 8 + [ci]
-        lib.orc_mamba_seq_bwd.argtypes = [i64] * 6 + [ci] + [dp] * 13 + [ci, ci]
+        lib.orc_mamba_seq_bwd.argtypes = [i64] * 6 + [ci] + [dp] * 14 + [ci, ci]
         lib.orc_raw_seq_fwd.argtypes = [i64] * 7 + [dp] * 7 + [ci]
         lib.orc_raw_seq_bwd.argtypes = [i64] * 7 + [dp] * 12 + [ci]
         lib.orc_ssd_chunk_fwd.argtypes = [i64] * 8 + [dp] * 7 + [ci]
@@ -155,14 +158,15 @@ def mamba_seq_fwd(x, dt, A, B, C, s0=None, nthreads=0):
 
 
 def mamba_seq_bwd(x, dt, A, B, C, s0, dy, ds_final, mutation=MUT_NONE, nthreads=0):
-    """Return dict dx, d_dt, dB, dC, d_s0 (same shapes as x, dt, B, C, s0)."""
+    """Return dict dx, d_dt, dB, dC, d_s0 (same shapes as x, dt, B, C, s0) and
+    dA (same shape as A)."""
     x, dt, A, B, C, s0, dy, dsf = map(_f64, (x, dt, A, B, C, s0, dy, ds_final))
     b, T, H, P, N, G, ps = _mamba_dims(x, B, A)
     out = dict(dx=np.zeros_like(x), d_dt=np.zeros_like(dt), dB=np.zeros_like(B),
-               dC=np.zeros_like(C), d_s0=np.zeros((b, H, P, N)))
+               dC=np.zeros_like(C), d_s0=np.zeros((b, H, P, N)), dA=np.zeros_like(A))
     _check(_load().orc_mamba_seq_bwd(b, T, H, P, N, G, ps, _p(x), _p(dt), _p(A), _p(B), _p(C),
                                      _p(s0), _p(dy), _p(dsf), _p(out["dx"]), _p(out["d_dt"]),
-                                     _p(out["dB"]), _p(out["dC"]), _p(out["d_s0"]),
+                                     _p(out["dB"]), _p(out["dC"]), _p(out["d_s0"]), _p(out["dA"]),
                                      int(mutation), _threads(nthreads)), "mamba_seq_bwd")
     return out
 

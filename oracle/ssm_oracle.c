@@ -131,18 +131,25 @@ int orc_mamba_seq_fwd(i64 b, i64 T, i64 H, i64 P, i64 N, i64 G, int per_state,
 
 /* Store-all reverse recurrence (P3: seeded with ds_final at t = T, walking t
  * from T-1 down to 0, all T+1 states recomputed and kept). */
+/* dA (optional, NULL = not computed): the gradient of the decay coefficients,
+ * [H] (per head) or [H,N] (per state).  a_t = exp(delta_t A) gives
+ * d s_t / d A = delta_t a_t s_{t-1} elementwise, so
+ * dA[h,n] = sum_{b,t} delta_t a_t[n] sum_p dS_t[p,n] s_{t-1}[p,n]
+ * (summed over n as well for a per-head A), with dS_t the gradient of s_t. */
 int orc_mamba_seq_bwd(i64 b, i64 T, i64 H, i64 P, i64 N, i64 G, int per_state,
                       const double* x, const double* dt, const double* A,
                       const double* B, const double* C, const double* s0,
                       const double* dy, const double* ds_final,
-                      double* dx, double* d_dt, double* dB, double* dC, double* d_s0,
+                      double* dx, double* d_dt, double* dB, double* dC, double* d_s0, double* dA,
                       int mutation, int nthreads) {
   if (b < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G) return 1;
   const i64 hpg = H / G;
   /* per-head partials of dB and dC, summed over the group after the join */
   double* dBh = (double*)calloc((size_t)(b * T * H * N) + 1, sizeof(double));
   double* dCh = (double*)calloc((size_t)(b * T * H * N) + 1, sizeof(double));
-  if (!dBh || !dCh) { free(dBh); free(dCh); return 2; }
+  /* per-(batch, head) partials of dA, summed over the batch after the join */
+  double* dAb = (double*)calloc((size_t)(b * H * N) + 1, sizeof(double));
+  if (!dBh || !dCh || !dAb) { free(dBh); free(dCh); free(dAb); return 2; }
   set_threads(nthreads);
   int fail = 0;
 #pragma omp parallel for schedule(dynamic)
@@ -210,6 +217,8 @@ int orc_mamba_seq_bwd(i64 b, i64 T, i64 H, i64 P, i64 N, i64 G, int per_state,
           double term = xt[p] * Bt[n];
           if (mutation != MUT_DROP_DA_PATH) term += An * a * s_prev[p * N + n];
           ddelta += dS[p * N + n] * term;
+          /* dA: d s_t / d A = delta a s_{t-1} */
+          dAb[(bi * H + h) * N + n] += dS[p * N + n] * d * a * s_prev[p * N + n];
         }
       d_dt[(bi * T + t) * H + h] = (mutation == MUT_DROP_SOFTPLUS) ? ddelta : ddelta * sigmoid(zt);
       /* carry the gradient to s_{t-1} */
@@ -234,8 +243,19 @@ int orc_mamba_seq_bwd(i64 b, i64 T, i64 H, i64 P, i64 N, i64 G, int per_state,
           dB[IX4(bi, t, g, n, T, G, N)] = sb;
           dC[IX4(bi, t, g, n, T, G, N)] = sc;
         }
+  /* dA: sum over the batch (and over n for a per-head A), ascending */
+  if (dA) {
+    for (i64 h = 0; h < H; ++h)
+      for (i64 n = 0; n < (per_state ? N : 1); ++n) {
+        double acc = 0.0;
+        for (i64 bi = 0; bi < b; ++bi)
+          for (i64 nn = (per_state ? n : 0); nn < (per_state ? n + 1 : N); ++nn) acc += dAb[(bi * H + h) * N + nn];
+        dA[per_state ? h * N + n : h] = acc;
+      }
+  }
   free(dBh);
   free(dCh);
+  free(dAb);
   return fail ? 2 : 0;
 }
 
