@@ -99,6 +99,22 @@ ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc,
                            void* dx, float* d_dt, void* dB, void* dC, float* d_s0,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssm_scan_bwd plus dA, the gradient of the decay coefficients A: dA [H]
+ * (per-head decay) or [H,N] (per-state decay), float32, written (not
+ * accumulated).  With a_t = exp(delta_t A) the state update gives
+ * d s_t / d A = delta_t a_t s_{t-1}, so dA = sum over the batch and time of
+ * delta_t a_t <dS_t, s_{t-1}> (per state: per column n).  burn-mamba's
+ * combined_backward returns the decay gradient d_da; dA is its sum
+ * sum_{b,t} d_da * delta, the gradient training needs for A.  The other
+ * arguments and outputs are exactly those of ssm_scan_bwd; dA must not be NULL
+ * when batch > 0.  The sums over the batch run in a fixed order (deterministic). */
+ssmvjp_status ssm_scan_bwd_dA(const ssmvjp_scan_desc* desc,
+                              const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* s0,
+                              const void* dy, const float* ds_final,
+                              void* dx, float* d_dt, void* dB, void* dC, float* d_s0, float* dA,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* ssd_chunk_bwd: chunked SSD backward (Mamba-2 and Mamba-3 MIMO)            */
 /* ------------------------------------------------------------------------ */
@@ -137,6 +153,20 @@ ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
                             const void* dy, const float* ds_final,
                             void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC, float* d_s0,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_chunk_bwd plus dA [H] (FORM_MAMBA2 only, SSMVJP_EINVAL otherwise):
+ * dA_h = sum over the batch and time of d_da * delta for head h, with d_da the
+ * decay gradient the chunked backward forms on the way to d_dt (burn-mamba
+ * combined_backward's d_da).  Each chunk's per-head sum is formed in the
+ * chunk kernel, and the sums over (batch, chunk) run in a fixed order.  The
+ * other arguments and outputs are exactly those of ssd_chunk_bwd (same
+ * workspace size); dA must not be NULL when batch > 0. */
+ssmvjp_status ssd_chunk_bwd_dA(const ssmvjp_ssd_desc* desc,
+                               const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* s0,
+                               const void* dy, const float* ds_final,
+                               void* dx, float* d_dt, void* dB, void* dC, float* d_s0, float* dA,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two stages of ssd_chunk_bwd as separate calls, for callers that want to
  * schedule or time them apart.  ssd_chunk_bwd_states followed by

@@ -20,9 +20,10 @@ DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
 FORM_MAMBA2, FORM_RAW = 0, 1
 DELTA_CKPT, DELTA_BWD, DELTA_REDUCE, DELTA_ALL = 1, 2, 4, 7
 
-_STATUS_FNS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssd_chunk_bwd_workspace", "ssd_chunk_bwd",
-               "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "ssd_chunk_fwd_workspace", "ssd_chunk_fwd",
-               "delta_rule_bwd_workspace", "delta_rule_bwd", "delta_rule_bwd_stages")
+_STATUS_FNS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssm_scan_bwd_dA", "ssd_chunk_bwd_workspace",
+               "ssd_chunk_bwd", "ssd_chunk_bwd_dA", "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads",
+               "ssd_chunk_fwd_workspace", "ssd_chunk_fwd", "delta_rule_bwd_workspace", "delta_rule_bwd",
+               "delta_rule_bwd_stages")
 EXPORTS = _STATUS_FNS + ("ssmvjp_status_str", "ssmvjp_version")
 
 
@@ -65,8 +66,10 @@ def lib():
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.ssm_scan_bwd_workspace.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(sz)]
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 14 + [sz, vp]
+        L.ssm_scan_bwd_dA.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 15 + [sz, vp]
         L.ssd_chunk_bwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
         L.ssd_chunk_bwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 14 + [sz, vp]
+        L.ssd_chunk_bwd_dA.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 15 + [sz, vp]
         L.ssd_chunk_bwd_states.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 10 + [sz, vp]
         L.ssd_chunk_bwd_grads.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11 + [sz, vp]
         L.ssd_chunk_fwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
@@ -153,8 +156,10 @@ def ssm_scan_bwd_workspace(desc):
     return n.value
 
 
-def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, out=None, workspace=None, stream=None):
-    """Sequential selective-scan backward.  Returns dict dx, d_dt, dB, dC, d_s0.
+def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, want_dA=False, out=None, workspace=None,
+                 stream=None):
+    """Sequential selective-scan backward.  Returns dict dx, d_dt, dB, dC, d_s0
+    (and dA, shaped like A, with want_dA=True).
 
     x, dy [b,T,H,P] and B, C [b,T,G,N] are float32 or bfloat16 (all the same);
     dt [b,T,H], A [H] (Mamba-2) or [H,N] (Mamba-1), s0, ds_final [b,H,P,N] float32
@@ -176,10 +181,17 @@ def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, out=None, wo
         out = dict(dx=torch.empty_like(x), d_dt=torch.empty_like(dt), dB=torch.empty_like(B),
                    dC=torch.empty_like(C), d_s0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
     ws, wsb = _workspace(ssm_scan_bwd_workspace(desc), dev, workspace)
-    st = lib().ssm_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy),
-                            _ptr(ds_final), _ptr(out["dx"]), _ptr(out["d_dt"]), _ptr(out["dB"]), _ptr(out["dC"]),
-                            _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
-    _check("ssm_scan_bwd", st)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy), _ptr(ds_final), _ptr(out["dx"]),
+            _ptr(out["d_dt"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["d_s0"]))
+    if want_dA:
+        if "dA" not in out:
+            out["dA"] = torch.empty_like(A)
+        _need(out["dA"], "dA", torch.float32, tuple(A.shape), dev)
+        st = lib().ssm_scan_bwd_dA(ctypes.byref(desc), *args, _ptr(out["dA"]), _ptr(ws), wsb, _stream(stream))
+        _check("ssm_scan_bwd_dA", st)
+    else:
+        st = lib().ssm_scan_bwd(ctypes.byref(desc), *args, _ptr(ws), wsb, _stream(stream))
+        _check("ssm_scan_bwd", st)
     return out
 
 
@@ -201,11 +213,13 @@ def ssd_chunk_bwd_workspace(desc):
     return n.value
 
 
-def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, workspace=None, stream=None):
+def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, want_dA=False, out=None, workspace=None,
+                  stream=None):
     """Chunked SSD backward.
 
     Mamba-2 form (A given): xv = x [b,T,H,P], dtda = dt [b,T,H] (raw),
-    B, C [b,T,G,N]; returns dict dx, d_dt, dB, dC, d_s0.
+    B, C [b,T,G,N]; returns dict dx, d_dt, dB, dC, d_s0 (and dA [H] with
+    want_dA=True).
     RAW form (A None): xv = v [b,T,M,H,P], dtda = da [b,T,H], B, C [b,T,M,G,N];
     returns dict dv, d_da, dB, dC, d_s0.
     """
@@ -227,10 +241,19 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, w
         out = {names[0]: torch.empty_like(xv), names[1]: torch.empty_like(dtda), "dB": torch.empty_like(B),
                "dC": torch.empty_like(C), "d_s0": torch.empty((b, H, P, N), dtype=torch.float32, device=dev)}
     ws, wsb = _workspace(ssd_chunk_bwd_workspace(desc), dev, workspace)
-    st = lib().ssd_chunk_bwd(ctypes.byref(desc), _ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0),
-                             _ptr(dy), _ptr(ds_final), _ptr(out[names[0]]), _ptr(out[names[1]]), _ptr(out["dB"]),
-                             _ptr(out["dC"]), _ptr(out["d_s0"]), _ptr(ws), wsb, _stream(stream))
-    _check("ssd_chunk_bwd", st)
+    args = (_ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy), _ptr(ds_final),
+            _ptr(out[names[0]]), _ptr(out[names[1]]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["d_s0"]))
+    if want_dA:
+        if form != FORM_MAMBA2:
+            raise ValueError("dA needs the Mamba-2 (x, dt, A) form")
+        if "dA" not in out:
+            out["dA"] = torch.empty_like(A)
+        _need(out["dA"], "dA", torch.float32, (H,), dev)
+        st = lib().ssd_chunk_bwd_dA(ctypes.byref(desc), *args, _ptr(out["dA"]), _ptr(ws), wsb, _stream(stream))
+        _check("ssd_chunk_bwd_dA", st)
+    else:
+        st = lib().ssd_chunk_bwd(ctypes.byref(desc), *args, _ptr(ws), wsb, _stream(stream))
+        _check("ssd_chunk_bwd", st)
     return out
 
 

@@ -82,10 +82,10 @@ ssmvjp_status ssm_scan_bwd_workspace(const ssmvjp_scan_desc* desc, size_t* bytes
   return SSMVJP_OK;
 }
 
-ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
-                           const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
-                           void* dx, float* d_dt, void* dB, void* dC, float* d_s0, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+static ssmvjp_status scan_run(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
+                              void* dx, float* d_dt, void* dB, void* dC, float* d_s0, float* dA, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   ssmvjp_status s = scan_check(desc);
   if (s != SSMVJP_OK) return s;
   const ssmvjp_scan_desc& d = *desc;
@@ -97,15 +97,32 @@ ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc, const void* x, const fl
   const void* pa[] = {x, B, C, dy, dx, dB, dC};
   for (const void* p : pa)
     if (p && !aligned(p, be)) return SSMVJP_EINVAL;
-  const void* pf[] = {dt, A, s0, ds_final, d_dt, d_s0};
+  const void* pf[] = {dt, A, s0, ds_final, d_dt, d_s0, dA};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
   const SeqPlan plan = seq_plan(d);
   if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
     return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
-  SeqPointers ptr{x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, workspace};
+  SeqPointers ptr{x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, workspace, dA};
   return hip_status(launch_seq_bwd(d, plan, ptr, (hipStream_t)stream));
+}
+
+ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
+                           void* dx, float* d_dt, void* dB, void* dC, float* d_s0, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return scan_run(desc, x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+ssmvjp_status ssm_scan_bwd_dA(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
+                              void* dx, float* d_dt, void* dB, void* dC, float* d_s0, float* dA, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (desc && desc->batch > 0 && !dA) return SSMVJP_EINVAL;
+  return scan_run(desc, x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, dA, workspace, workspace_bytes,
+                  stream);
 }
 
 // ------------------------------- ssd_chunk_bwd ------------------------------
@@ -121,7 +138,8 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
 static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
                              const float* A, const void* B, const void* C, const float* s0, const void* dy,
                              const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
-                             float* d_s0, void* workspace, size_t workspace_bytes, void* stream, int stages) {
+                             float* d_s0, float* dA, void* workspace, size_t workspace_bytes, void* stream,
+                             int stages) {
   ssmvjp_status s = ssd_check(desc);
   if (s != SSMVJP_OK) return s;
   const ssmvjp_ssd_desc& d = *desc;
@@ -136,14 +154,14 @@ static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, co
   const void* pa[] = {x_or_v, B, C, dy, dx_or_dv, dB, dC};
   for (const void* p : pa)
     if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
-  const void* pf[] = {dt_or_da, A, s0, ds_final, d_dt_or_dda, d_s0};
+  const void* pf[] = {dt_or_da, A, s0, ds_final, d_dt_or_dda, d_s0, dA};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
   const SsdPlan plan = ssd_plan(d);
   if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
     return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
-  SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace};
+  SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace, dA};
   return hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream, stages));
 }
 
@@ -151,8 +169,18 @@ ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, con
                             const float* A, const void* B, const void* C, const float* s0, const void* dy,
                             const float* ds_final, void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
                             float* d_s0, void* workspace, size_t workspace_bytes, void* stream) {
-  return ssd_run(desc, x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace,
-                 workspace_bytes, stream, SSD_STAGE_ALL);
+  return ssd_run(desc, x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, nullptr,
+                 workspace, workspace_bytes, stream, SSD_STAGE_ALL);
+}
+
+ssmvjp_status ssd_chunk_bwd_dA(const ssmvjp_ssd_desc* desc, const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* s0, const void* dy, const float* ds_final,
+                               void* dx, float* d_dt, void* dB, void* dC, float* d_s0, float* dA, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (desc && desc->form != SSMVJP_FORM_MAMBA2) return SSMVJP_EINVAL;  // dA needs the (x, dt, A) form
+  if (desc && desc->batch > 0 && !dA) return SSMVJP_EINVAL;
+  return ssd_run(desc, x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, dA, workspace, workspace_bytes,
+                 stream, SSD_STAGE_ALL);
 }
 
 ssmvjp_status ssd_chunk_bwd_states(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
@@ -160,7 +188,7 @@ ssmvjp_status ssd_chunk_bwd_states(const ssmvjp_ssd_desc* desc, const void* x_or
                                    const float* ds_final, float* d_s0, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   return ssd_run(desc, x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, nullptr, nullptr, nullptr, nullptr, d_s0,
-                 workspace, workspace_bytes, stream, SSD_STAGE_STATES);
+                 nullptr, workspace, workspace_bytes, stream, SSD_STAGE_STATES);
 }
 
 ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
@@ -168,7 +196,7 @@ ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc, const void* x_or_
                                   float* d_dt_or_dda, void* dB, void* dC, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   return ssd_run(desc, x_or_v, dt_or_da, A, B, C, nullptr, dy, nullptr, dx_or_dv, d_dt_or_dda, dB, dC, nullptr,
-                 workspace, workspace_bytes, stream, SSD_STAGE_GRADS);
+                 nullptr, workspace, workspace_bytes, stream, SSD_STAGE_GRADS);
 }
 
 // ------------------------------- ssd_chunk_fwd ------------------------------

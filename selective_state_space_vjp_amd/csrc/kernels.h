@@ -15,6 +15,7 @@ struct SeqPlan {
   int64_t K, J;       // checkpoint interval and count
   int PPT, NPG;       // p values per thread, p groups per workgroup
   int64_t off_delta, off_sig, off_ck, off_seg, off_dBh, off_dCh;
+  int64_t off_dA;  // per-(batch, head[, state]) partial sums of dA
   size_t bytes;
 };
 
@@ -33,12 +34,15 @@ struct SeqPointers {
   void* dC;
   float* d_s0;
   void* workspace;
+  float* dA;  // NULL: not computed
 };
 
 SeqPlan seq_plan(const ssmvjp_scan_desc& d);
 size_t seq_lds_bytes(const ssmvjp_scan_desc& d, const SeqPlan& plan);
 hipError_t launch_seq_bwd(const ssmvjp_scan_desc& d, const SeqPlan& plan, const SeqPointers& ptr,
                           hipStream_t stream);
+// dA[j] = sum over i < R of part[i * J + j], ascending i (one thread per j)
+void launch_dA_reduce(const float* part, int64_t R, int64_t J, float* dA, hipStream_t stream);
 
 // ------------------------------ chunked SSD --------------------------------
 struct SsdPlan {
@@ -49,6 +53,7 @@ struct SsdPlan {
   int64_t off_S, off_dS, off_part;
   int64_t off_rowv, off_dend;  // row-blocked path (L*M > 64): per-row partial sums, d_end
   int64_t off_csv;             // per-chunk step scalars (cumA, delta, sigmoid(dt))
+  int64_t off_dA;              // per-(batch, chunk, head) partial sums of dA
   size_t bytes;
 };
 
@@ -67,6 +72,7 @@ struct SsdPointers {
   void* dC;
   float* d_s0;
   void* workspace;
+  float* dA;  // NULL: not computed (FORM_MAMBA2 only)
 };
 
 bool ssd_shape_supported(const ssmvjp_ssd_desc& d);

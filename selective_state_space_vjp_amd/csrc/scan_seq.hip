@@ -48,6 +48,7 @@ struct SeqArgs {
   float* seg;    // [b*H][K][P*N]
   float* dBh;    // [b,T,H,N]
   float* dCh;    // [b,T,H,N]
+  float* dA_part;  // [b,H,N] (per state) or [b,H] (per head) partial sums of dA, or NULL
 };
 
 __global__ void seq_prologue_kernel(const float* __restrict__ dt, i64 n, float* __restrict__ delta,
@@ -122,6 +123,9 @@ __global__ void __launch_bounds__(1024) seq_bwd_kernel(SeqArgs a, int PPT, int N
     const int p = pg * PPT + k;
     dS[k] = (k < PPT && p < P && a.dsf) ? a.dsf[ebase + (i64)p * N + n] : 0.0f;
   }
+  // dA: d s_t / d A = delta a s_{t-1}, summed over this thread's p range and
+  // over t (reverse order) in one register
+  float dAacc = 0.0f;
 
   for (i64 j = a.J - 1; j >= 0; --j) {
     const i64 t0 = j * a.K;
@@ -144,7 +148,7 @@ __global__ void __launch_bounds__(1024) seq_bwd_kernel(SeqArgs a, int PPT, int N
       const float av = expf(__fmul_rn(d, acoef));
       const float Bn = ld(B, ((bi * a.T + t) * a.G + g) * a.N + n);
       const float Cn = ld(C, ((bi * a.T + t) * a.G + g) * a.N + n);
-      float dbn = 0.0f, dcn = 0.0f, dd = 0.0f;
+      float dbn = 0.0f, dcn = 0.0f, dd = 0.0f, dAs = 0.0f;
       __syncthreads();  // previous step's readers of red/colB/colC/ddw are done
 #pragma unroll
       for (int k = 0; k < MAXPPT; ++k) {
@@ -158,8 +162,10 @@ __global__ void __launch_bounds__(1024) seq_bwd_kernel(SeqArgs a, int PPT, int N
         dcn += dyp * s_t;                          // dC_t uses s_t
         dbn += dS[k] * xp;                         // dB_t (before the delta factor)
         dd += dS[k] * (xp * Bn + acoef * av * s_prev);  // input path + decay path
+        dAs += dS[k] * s_prev;
         red[p * (N + 1) + n] = dS[k] * Bn;
       }
+      dAacc += d * av * dAs;
       if (active) {
         colB[pg * N + n] = dbn;
         colC[pg * N + n] = dcn;
@@ -195,6 +201,27 @@ __global__ void __launch_bounds__(1024) seq_bwd_kernel(SeqArgs a, int PPT, int N
     const int p = pg * PPT + k;
     if (k < PPT && p < P) a.d_s0[ebase + (i64)p * N + n] = dS[k];
   }
+  if (a.dA_part) {  // uniform: fixed-order sums over the p groups (per state) or all threads (per head)
+    __syncthreads();  // the last step's readers of colB and ddw are done
+    if (a.per_state) {
+      if (active) colB[pg * N + n] = dAacc;
+      __syncthreads();
+      if (tid < N) {
+        float s = 0.0f;
+        for (int q = 0; q < NPG; ++q) s += colB[q * N + tid];
+        a.dA_part[bh * a.N + tid] = s;
+      }
+    } else {
+      const float v = wave_sum(active ? dAacc : 0.0f);
+      if ((tid & 63) == 0) ddw[tid >> 6] = v;
+      __syncthreads();
+      if (tid == 0) {
+        float s = 0.0f;
+        for (int w = 0; w < nw; ++w) s += ddw[w];
+        a.dA_part[bh] = s;
+      }
+    }
+  }
 }
 
 template <typename T>
@@ -213,7 +240,19 @@ __global__ void seq_group_sum_kernel(const float* __restrict__ dBh, const float*
   st(dC, i, sc);
 }
 
+__global__ void dA_reduce_kernel(const float* __restrict__ part, i64 R, i64 J, float* __restrict__ dA) {
+  const i64 j = (i64)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= J) return;
+  float s = 0.0f;
+  for (i64 i = 0; i < R; ++i) s += part[i * J + j];
+  dA[j] = s;
+}
+
 static inline i64 cdiv(i64 a, i64 b) { return (a + b - 1) / b; }
+
+void launch_dA_reduce(const float* part, i64 R, i64 J, float* dA, hipStream_t stream) {
+  if (J > 0) hipLaunchKernelGGL(dA_reduce_kernel, dim3((unsigned)cdiv(J, 256)), dim3(256), 0, stream, part, R, J, dA);
+}
 
 SeqPlan seq_plan(const ssmvjp_scan_desc& d) {
   SeqPlan p{};
@@ -237,6 +276,7 @@ SeqPlan seq_plan(const ssmvjp_scan_desc& d) {
   p.off_seg = carve(d.batch * d.nheads * p.K * d.headdim * d.dstate);
   p.off_dBh = carve(bTH * d.dstate);
   p.off_dCh = carve(bTH * d.dstate);
+  p.off_dA = carve(d.batch * d.nheads * d.dstate);
   p.bytes = (size_t)off;
   return p;
 }
@@ -262,6 +302,7 @@ static hipError_t launch_seq_t(const ssmvjp_scan_desc& d, const SeqPlan& plan, c
   a.seg = (float*)(ws + plan.off_seg);
   a.dBh = (float*)(ws + plan.off_dBh);
   a.dCh = (float*)(ws + plan.off_dCh);
+  a.dA_part = ptr.dA ? (float*)(ws + plan.off_dA) : nullptr;
 
   const i64 bTH = a.b * a.T * a.H;
   if (bTH > 0) {
@@ -280,6 +321,7 @@ static hipError_t launch_seq_t(const ssmvjp_scan_desc& d, const SeqPlan& plan, c
     hipLaunchKernelGGL(seq_group_sum_kernel<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, a.dBh, a.dCh,
                        a.b * a.T, a.H, a.G, a.N, (T*)a.dB, (T*)a.dC);
   }
+  if (ptr.dA) launch_dA_reduce(a.dA_part, a.b, a.per_state ? a.H * a.N : a.H, ptr.dA, stream);
   return hipGetLastError();
 }
 

@@ -329,7 +329,9 @@ __device__ __forceinline__ Frag<T> cvt_rowk(const float* tile, int pitch, int k0
   return frag_make<T>(f.v);
 }
 
-template <typename T, int CP, int CN, int CL, int CM>
+// DA: also the per-chunk dA partial sums (a separate instantiation, so that
+// the plain backward keeps its registers)
+template <typename T, int CP, int CN, int CL, int CM, bool DA>
 __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   constexpr int E16 = 16 / sizeof(T);
   constexpr bool FIXED = CP && CN && CL && CM;
@@ -431,9 +433,9 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   };
   if (BF) {
     issue(hbase);
-    // a head issues the next head's loads, then one d_dt store and one dx
-    // store per (p tile, row block) item of this wave
-    if constexpr (FIXED) vmem_pad_stores<1 + (CP / 16) * (CL * CM / 16) / CH_NW>(make_rsrc(a.dxv, 0u));
+    // a head issues the next head's loads, then the d_dt (and dA) stores and
+    // one dx store per (p tile, row block) item of this wave
+    if constexpr (FIXED) vmem_pad_stores<(DA ? 2 : 1) + (CP / 16) * (CL * CM / 16) / CH_NW>(make_rsrc(a.dxv, 0u));
   }
   __syncthreads();  // B, C staged
 
@@ -468,8 +470,9 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
 
   // d_cumA from its four sources, the K1 suffix sum and the chain to d_dt for
   // one head, from the partial row sums in pb; run by a single wave, which gets
-  // the d_dt (RAW: d_da) value of step `lane` back.
-  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float {
+  // the d_dt (RAW: d_da) value of step `lane` back, and the head's dA partial
+  // sum over the chunk, sum_l d_da_l * delta_l, in every lane.
+  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float2 {
     auto cum_of = [&](int l) { return __shfl(cs.cum, l, 64); };
     float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
     const float c_row = cum_of((lane / M) & 63);  // every lane takes part in the shuffle
@@ -503,13 +506,14 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     }
     if (lane == Lc - 1) dcl += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
     const float dda = wave_incl_suffix(lane < Lc ? dcl : 0.0f, lane);
-    return a.raw ? dda : (dvxl + dda * Ah) * cs.sig;
+    return make_float2(a.raw ? dda : (dvxl + dda * Ah) * cs.sig, DA ? wave_sum(dda * cs.delta) : 0.0f);
   };
   // every wave stores (dropped unless `on` and lane < Lc): no store sits in a
   // branch, which keeps the compiler's count of outstanding loads exact
   const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
-  auto epi_store = [&](bool on, i64 h, float v) {
-    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v);
+  auto epi_store = [&](bool on, i64 h, float2 v) {
+    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v.x);
+    if constexpr (DA) bstore_f32(dA_rsrc(a, bi, c), on && lane == 0 ? (unsigned)(h * 4) : BUF_OOB, v.y);
   };
   i64 prev_h = 0;
   ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
@@ -551,7 +555,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     // rotating wave while the other waves start on this head
     if (BF) {
       const bool on = hh > 0 && w == (int)((hh - 1) % CH_NW);
-      float v = 0.0f;
+      float2 v = make_float2(0.0f, 0.0f);
       if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_N * 8 * 64);
       epi_store(on, prev_h, v);
     }
@@ -731,7 +735,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
     // ---- d_cumA assembly: this head now (float32) or one head later (bf16) ----
     if (!BF) {
       __syncthreads();  // partial row sums complete
-      float v = 0.0f;
+      float2 v = make_float2(0.0f, 0.0f);
       if (w == 0) v = epilogue(cs, Ah, pbase);
       epi_store(w == 0, h, v);
     } else {
@@ -743,7 +747,7 @@ __global__ void __launch_bounds__(CH_NTH) ssd_chunk_bwd_kernel(SsdArgs a) {
   if (BF && a.hph > 0) {
     __syncthreads();
     const bool on = w == (int)((a.hph - 1) % CH_NW);
-    float v = 0.0f;
+    float2 v = make_float2(0.0f, 0.0f);
     if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_N * 8 * 64);
     epi_store(on, prev_h, v);
   }
@@ -864,6 +868,7 @@ SsdPlan ssd_plan(const ssmvjp_ssd_desc& d) {
   p.off_rowv = carve(blocked ? d.batch * p.nc * d.nheads * RV_N * p.LM * 4 : 0);
   p.off_dend = carve(blocked ? d.batch * p.nc * d.nheads * 4 : 0);
   p.off_csv = carve(d.batch * p.nc * d.nheads * 3 * 64 * 4);
+  p.off_dA = carve(d.batch * p.nc * d.nheads * 4);
   p.bytes = (size_t)off;
   return p;
 }
@@ -884,6 +889,7 @@ static SsdArgs make_args(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const Ss
   a.rowv = (float*)(ws + plan.off_rowv);
   a.dend = (float*)(ws + plan.off_dend);
   a.csv = (float*)(ws + plan.off_csv);
+  a.dA_part = ptr.dA && !a.raw ? (float*)(ws + plan.off_dA) : nullptr;
   return a;
 }
 
@@ -935,12 +941,18 @@ static void launch_grads_t(const SsdArgs& a, hipStream_t stream) {
   const i64 grid2 = a.b * a.nc * a.G * a.hsplit;
   if (sizeof(T) == 2 && workload_shape(a))
     launch_ssd_chunk16(a, stream);  // 16 waves, bf16 at P = 64, N = 128, L = 64, M = 1
+  else if (workload_shape(a) && a.dA_part)
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1, true>), dim3((unsigned)grid2), dim3(CH_NTH),
+                       grads_lds<T>(a), stream, a);
   else if (workload_shape(a))
-    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1>), dim3((unsigned)grid2), dim3(CH_NTH),
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 64, 128, 64, 1, false>), dim3((unsigned)grid2), dim3(CH_NTH),
+                       grads_lds<T>(a), stream, a);
+  else if (a.dA_part)
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 0, 0, 0, 0, true>), dim3((unsigned)grid2), dim3(CH_NTH),
                        grads_lds<T>(a), stream, a);
   else
-    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 0, 0, 0, 0>), dim3((unsigned)grid2), dim3(CH_NTH), grads_lds<T>(a),
-                       stream, a);
+    hipLaunchKernelGGL((ssd_chunk_bwd_kernel<T, 0, 0, 0, 0, false>), dim3((unsigned)grid2), dim3(CH_NTH),
+                       grads_lds<T>(a), stream, a);
   if (a.hsplit > 1) {
     const i64 n = a.b * a.T * a.M * a.G * a.N;
     hipLaunchKernelGGL(ssd_head_sum_kernel<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, a.part, n,
@@ -960,6 +972,8 @@ hipError_t launch_ssd_bwd(const ssmvjp_ssd_desc& d, const SsdPlan& plan, const S
     if (stages & SSD_STAGE_STATES) launch_states_t<float>(a, stream, NB);
     if (stages & SSD_STAGE_GRADS) launch_grads_t<float>(a, stream);
   }
+  if ((stages & SSD_STAGE_GRADS) && ptr.dA && d.form == SSMVJP_FORM_MAMBA2)
+    launch_dA_reduce((const float*)((char*)ptr.workspace + plan.off_dA), d.batch * plan.nc, d.nheads, ptr.dA, stream);
   return hipGetLastError();
 }
 

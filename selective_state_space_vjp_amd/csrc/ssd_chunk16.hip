@@ -64,7 +64,9 @@ constexpr int L_TOTAL = L_W + NPAIR * 256 * 2;
 __device__ __forceinline__ int pair_of(int rt, int rs) { return rt * (rt + 1) / 2 + rs; }
 __device__ __forceinline__ int tile_off(int pt, int nt) { return (pt * NT + nt) * 256; }
 
-template <int UNUSED>
+// DA: also the per-chunk dA partial sums (a separate instantiation, so that
+// the plain backward keeps its registers)
+template <bool DA>
 __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* CBs = (float*)(smem_raw + L_CB);
@@ -128,8 +130,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     rd = bload16(make_rsrc((const bf16*)a.dS + so, PN * 2), (unsigned)tid * 16u);
   };
   issue(hbase);
-  // each head issues the next head's loads, then the d_dt store and one dx store
-  vmem_pad_stores<2>(make_rsrc(a.dxv, 0u));
+  // each head issues the next head's loads, then the d_dt (and dA) stores and one dx store
+  vmem_pad_stores<DA ? 3 : 2>(make_rsrc(a.dxv, 0u));
   __syncthreads();  // B, C staged
 
   // ---- C.B^T (K2 recompute) on the lower-triangular tile pairs, waves 0..9 ----
@@ -160,8 +162,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   f32x4 dcbacc = zero4();                // d_cb of this wave's pair, summed over heads
 
   // d_cumA from its sources, the K1 suffix sum and the chain to d_dt (RAW:
-  // d_da) for one head, from the partial sums in pb; lane = step
-  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float {
+  // d_da) for one head, from the partial sums in pb; lane = step.  Also the
+  // head's dA partial sum over the chunk, sum_l d_da_l * delta_l (the same in
+  // every lane).
+  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float2 {
     float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
     if (lane < LM16) {
       const int rbl = lane >> 4, rl = lane & 15;
@@ -185,9 +189,14 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     dendt *= exp_hw(cs.end);
     if (lane == Lc - 1) dc += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
     const float dda = wave_incl_suffix(lane < Lc ? dc : 0.0f, lane);
-    return a.raw ? dda : (dvx + dda * Ah) * cs.sig;
+    return make_float2(a.raw ? dda : (dvx + dda * Ah) * cs.sig, DA ? wave_sum(dda * cs.delta) : 0.0f);
   };
   const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
+  // every wave stores (dropped unless `on`): no store sits in a branch
+  auto epi_store = [&](bool on, i64 h, float2 v) {
+    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v.x);
+    if constexpr (DA) bstore_f32(dA_rsrc(a, bi, c), on && lane == 0 ? (unsigned)(h * 4) : BUF_OOB, v.y);
+  };
   i64 prev_h = 0;
   ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
   float prev_Ah = 0.0f;
@@ -213,9 +222,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
     {
       const bool on = hh > 0 && w == (int)((hh - 1) & 3);
-      float v = 0.0f;
+      float2 v = make_float2(0.0f, 0.0f);
       if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_SET);
-      bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + prev_h) * 4) : BUF_OOB, v);
+      epi_store(on, prev_h, v);
     }
 
     // ---- phase A (1): ORANGE on this wave's tile pair ----
@@ -367,9 +376,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   }
   if (a.hph > 0) {
     const bool on = w == (int)((a.hph - 1) & 3);
-    float v = 0.0f;
+    float2 v = make_float2(0.0f, 0.0f);
     if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_SET);
-    bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + prev_h) * 4) : BUF_OOB, v);
+    epi_store(on, prev_h, v);
   }
 
   // ---- K2 backward on the head-summed d_cb: dC_k2 = d_cb . B, dB_k2 = d_cb^T . C ----
@@ -405,7 +414,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
 void launch_ssd_chunk16(const SsdArgs& a, hipStream_t stream) {
   const i64 grid = a.b * a.nc * a.G * a.hsplit;
-  hipLaunchKernelGGL(ssd_chunk16_kernel<0>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+  if (a.dA_part)
+    hipLaunchKernelGGL(ssd_chunk16_kernel<true>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+  else
+    hipLaunchKernelGGL(ssd_chunk16_kernel<false>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
 }
 
 }  // namespace ssmvjp

@@ -33,7 +33,16 @@ struct SsdArgs {
   // row-blocked path (L*M > 64) only:
   float* rowv;  // [b][nc][H][RV_N][LM] per-row partial sums of d_cumA terms
   float* dend;  // [b][nc][H] sum over (p, n) of S_c * dS_{c+1}
+  // dA (Mamba-2 form, when requested): [b][nc][H] sums over the chunk's steps
+  // of d_da * delta, else NULL
+  float* dA_part;
 };
+
+// resource over the dA partial sums of chunk c (empty when dA is not requested:
+// every store through it is dropped)
+__device__ __forceinline__ brsrc dA_rsrc(const SsdArgs& a, i64 bi, i64 c) {
+  return a.dA_part ? make_rsrc(a.dA_part + (bi * a.nc + c) * a.H, (unsigned)(a.H * 4)) : make_rsrc(a.d_dtda, 0u);
+}
 
 // per-row partial sums kept by the row-blocked path, in this order
 enum { RV_BLUE = 0, RV_OROW, RV_OCOL, RV_DEC, RV_DVX, RV_N };

@@ -212,3 +212,23 @@ def test_ssd_fwd_rejects_misaligned_big_tensors():
     assert n.value == 1 * 2 * 1 * 16 * 256 * 4  # b * chunks * groups score blocks
     d32 = _ssd(dtype=0)
     assert L.ssd_chunk_fwd_workspace(ctypes.byref(d32), ctypes.byref(n)) == bd.OK and n.value == 0
+
+
+def test_dA_entry_points_validate_before_launching():
+    L = bd.lib()
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(13)]
+    ws = ctypes.c_void_p(1 << 20)
+    # chunked: dA needs the Mamba-2 form and a dA pointer
+    d = _ssd()
+    assert L.ssd_chunk_bwd_dA(ctypes.byref(d), *fake, None, ws, 1 << 34, None) == bd.EINVAL
+    raw = _ssd(form=1, mimo_rank=2)
+    assert L.ssd_chunk_bwd_dA(ctypes.byref(raw), *fake, ctypes.c_void_p(1 << 21), ws, 1 << 34, None) == bd.EINVAL
+    assert L.ssd_chunk_bwd_dA(ctypes.byref(d), *([None] * 14), None, 0, None) == bd.EINVAL
+    mis = ctypes.c_void_p((1 << 21) + 2)  # dA misaligned for float32
+    assert L.ssd_chunk_bwd_dA(ctypes.byref(d), *fake, mis, ws, 1 << 34, None) == bd.EINVAL
+    # sequential
+    s = _scan()
+    assert L.ssm_scan_bwd_dA(ctypes.byref(s), *fake, None, ws, 1 << 34, None) == bd.EINVAL
+    assert L.ssm_scan_bwd_dA(ctypes.byref(s), *fake, mis, ws, 1 << 34, None) == bd.EINVAL
+    # an empty batch has nothing to write
+    assert L.ssm_scan_bwd_dA(ctypes.byref(_scan(batch=0)), *([None] * 14), None, 0, None) == bd.OK
