@@ -293,14 +293,13 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         for (int rb = 0; rb < RB; ++rb) {
           float cv[4];
           frag_get(ld_colk(Cs, LDN, 16 * rb, 16 * nt_own, lane), cv);  // C[r][n .. n+3], n = 16 nt + 4q
-          float bsum = 0.0f;
+          float bsum = 0.0f;  // sum_n C dC_blue = fcol * sum_n C acc
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float val = acc[rb][j] * fcol[rb];
-            xacc[rb][j] += val;
-            bsum = fmaf(cv[j], val, bsum);
+            xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
+            bsum = fmaf(cv[j], acc[rb][j], bsum);
           }
-          bsum = sum4q(bsum);
+          bsum = sum4q(bsum) * fcol[rb];
           if (q == 0) pb[PB_BLUE + nt_own * 64 + 16 * rb + r16] = bsum;
         }
       } else {
