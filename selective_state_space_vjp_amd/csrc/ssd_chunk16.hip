@@ -35,8 +35,11 @@ constexpr int P16 = 64, N16 = 128, LM16 = 64;
 constexpr int PT = P16 / 16, NT = N16 / 16, RB = LM16 / 16;
 constexpr int NPAIR = RB * (RB + 1) / 2;  // lower-triangular (t, s) tile pairs
 constexpr int LDC = LM16 + 4;             // CB pitch (float)
-constexpr int LDN = N16 + 8;              // B / C pitch (bf16)
-constexpr int LDP = P16 + 8;              // x / dy pitch (bf16)
+// row pitches of the staged tiles: rows 2 dwords apart modulo the 32 LDS
+// banks, so the fragment reads along a row (16 lanes, 8 bytes each, one per
+// row) hit 32 distinct banks
+constexpr int LDN = N16 + 4;              // B / C pitch (bf16)
+constexpr int LDP = P16 + 4;              // x / dy pitch (bf16)
 constexpr int PN = P16 * N16;
 
 // partial row sums of one head (float offsets inside one set)
@@ -62,6 +65,28 @@ constexpr int L_W = L_S + PN * 2;                        // bf16 [NPAIR][256] w 
 constexpr int L_TOTAL = L_W + NPAIR * 256 * 2;
 
 __device__ __forceinline__ int pair_of(int rt, int rs) { return rt * (rt + 1) / 2 + rs; }
+
+// The S_c and dS_{c+1} tiles sit in LDS in MFMA output order with each
+// 128-byte quarter of a 512-byte tile rotated by 32 bytes per quarter: the
+// transposed read gathers 8 bytes from each of the four quarters at the same
+// offset, which without the rotation all fall in the same banks.
+__device__ __forceinline__ int swz(int byte) { return (byte & ~127) | ((byte + 32 * ((byte >> 7) & 3)) & 127); }
+__device__ __forceinline__ Frag<bf16> ld_ntv_s(const bf16* t, int lane) {
+  Frag<bf16> f;
+  f.v = *(const s16x4*)((const char*)t + swz(8 * lane));
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> ld_ntv_t_s(const bf16* t, int lane) {
+  const int m = lane & 15;
+  return lds_tr_b16((const bf16*)((const char*)t + swz(8 * ((m & 3) * 16 + 4 * (lane >> 4) + (m >> 2)))));
+}
+// two 8-byte LDS stores of a 16-byte chunk (rows of the staged tiles are 8-byte aligned)
+__device__ __forceinline__ void st16_as8(bf16* p, const u32x4& u) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 lo = {u[0], u[1]}, hi = {u[2], u[3]};
+  *(u32x2*)p = lo;
+  *(u32x2*)(p + 4) = hi;
+}
 __device__ __forceinline__ int tile_off(int pt, int nt) { return (pt * NT + nt) * 256; }
 
 // DA: also the per-chunk dA partial sums (a separate instantiation, so that
@@ -106,8 +131,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     const unsigned bcbytes = (unsigned)(((i64)(Lc - 1) * brs + N16) * 2);
     const brsrc rb_ = make_rsrc(Bg, bcbytes), rc_ = make_rsrc(Cg, bcbytes);
     const int r = tid >> 4, col = (tid & 15) * 8;  // 64 rows x 16 chunks of 16 bytes
-    *(u32x4*)(Bs + r * LDN + col) = bload16(rb_, (unsigned)(r * brs + col) * 2);
-    *(u32x4*)(Cs + r * LDN + col) = bload16(rc_, (unsigned)(r * brs + col) * 2);
+    st16_as8(Bs + r * LDN + col, bload16(rb_, (unsigned)(r * brs + col) * 2));
+    st16_as8(Cs + r * LDN + col, bload16(rc_, (unsigned)(r * brs + col) * 2));
   }
 
   // ---- register prefetch of one head: step scalars, A, x or dy rows, S_c and dS_{c+1} ----
@@ -209,9 +234,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     const brsrc bdx = make_rsrc(dxg + (int)h * P16, xbytes);
 
     __syncthreads();  // the previous head is done with xs / dys / Ss / dSs / the scalars (and CB on entry)
-    *(u32x4*)((xy_sel ? dys : xs) + xy_r * LDP + xy_col) = rxy;
-    *(u32x4*)(Ss + tid * 8) = rs;
-    *(u32x4*)(dSs + tid * 8) = rd;
+    st16_as8((xy_sel ? dys : xs) + xy_r * LDP + xy_col, rxy);
+    *(u32x4*)((char*)Ss + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rs;
+    *(u32x4*)((char*)dSs + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rd;
     if (w == 0) {
       cumL[lane] = cs.cum;
       delL[lane] = cs.delta;
@@ -274,7 +299,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       float dend = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < PT; ++kb) {
-        const Frag<bf16> fa = ld_ntv(opA + tile_off(kb, nt_own), lane);
+        const Frag<bf16> fa = ld_ntv_s(opA + tile_off(kb, nt_own), lane);
         Frag<bf16> fb[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) fb[rb] = ld_colk(opB, LDP, 16 * rb, 16 * kb, lane);
@@ -282,7 +307,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         for (int rb = 0; rb < RB; ++rb) mma(acc[rb], fa, fb[rb]);
         if (!blue) {  // d_end partial: S_c (.) dS_{c+1} over this n tile
           float vS[4], vdS[4];
-          frag_get(ld_ntv(Ss + tile_off(kb, nt_own), lane), vS);
+          frag_get(ld_ntv_s(Ss + tile_off(kb, nt_own), lane), vS);
           frag_get(fa, vdS);
 #pragma unroll
           for (int j = 0; j < 4; ++j) dend = fmaf(vS[j], vdS[j], dend);
@@ -325,7 +350,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 #pragma unroll
         for (int k = 0; k < NT / 2; ++k) {
           const int kb = half * (NT / 2) + k;
-          f3a[k] = ld_ntv_t(dSs + tile_off(ipt, kb), lane);
+          f3a[k] = ld_ntv_t_s(dSs + tile_off(ipt, kb), lane);
           f3b[k] = ld_colk(Bs, LDN, 16 * irb, 16 * kb, lane);
         }
 #pragma unroll
