@@ -40,9 +40,82 @@ constexpr int BK_NTH = 64 * BK_NW;
 constexpr int BK_R = 64;             // fused rows per block
 constexpr int BK_TMAX = 8;           // P / 16 and N / 16 at most
 
+// Swizzled LDS layouts (bf16 tiles whose rows are whole 128-byte segments, the
+// workload shapes).  Rows of the staged input tiles have no padding; within each
+// 128-byte segment of a row the 8-byte unit u is stored at u ^ f(row),
+// f(row) = 4 (row % 4) + (row / 4) % 4.  A fragment read along the rows (16
+// consecutive rows from a multiple of 16, one unit each) and a transposed read
+// (4 consecutive rows from a multiple of 4, 4 consecutive units each) then hit
+// 16 distinct 8-byte bank pairs.  The state tiles keep MFMA output order with
+// each 128-byte quarter of a 512-byte tile rotated by 32 bytes per quarter, so
+// that the transposed read, which takes 8 bytes at the same offset of every
+// quarter, hits distinct banks.
+__device__ __forceinline__ int bk_xsw(int row, int col) {  // element offset in the row of column col, col % 4 == 0
+  const int u = col >> 2;
+  return ((u & ~15) | ((u & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3)))) << 2;
+}
+__device__ __forceinline__ int bk_qsw(int byte) { return (byte & ~127) | ((byte + 32 * ((byte >> 7) & 3)) & 127); }
+
+template <bool SWZ, typename T>
+__device__ __forceinline__ Frag<T> bk_colk(const T* t, int pitch, int c0, int k0, int lane) {
+  if constexpr (SWZ) {
+    const int row = c0 + (lane & 15);
+    Frag<T> f;
+    f.v = *(const s16x4*)(t + row * pitch + bk_xsw(row, k0 + 4 * (lane >> 4)));
+    return f;
+  } else {
+    return ld_colk(t, pitch, c0, k0, lane);
+  }
+}
+template <bool SWZ, typename T>
+__device__ __forceinline__ Frag<T> bk_rowk(const T* t, int pitch, int k0, int c0, int lane) {
+  if constexpr (SWZ) {
+    const int m = lane & 15, row = k0 + 4 * (lane >> 4) + (m >> 2);
+    return lds_tr_b16(t + row * pitch + bk_xsw(row, c0 + 4 * (m & 3)));
+  } else {
+    return ld_rowk(t, pitch, k0, c0, lane);
+  }
+}
+template <bool SWZ, typename T>
+__device__ __forceinline__ Frag<T> bk_ntv(const T* t, int lane) {
+  if constexpr (SWZ) {
+    Frag<T> f;
+    f.v = *(const s16x4*)((const char*)t + bk_qsw(8 * lane));
+    return f;
+  } else {
+    return ld_ntv(t, lane);
+  }
+}
+template <bool SWZ, typename T>
+__device__ __forceinline__ Frag<T> bk_ntv_t(const T* t, int lane) {
+  if constexpr (SWZ) {
+    const int m = lane & 15;
+    return lds_tr_b16((const T*)((const char*)t + bk_qsw(8 * ((m & 3) * 16 + 4 * (lane >> 4) + (m >> 2)))));
+  } else {
+    return ld_ntv_t(t, lane);
+  }
+}
+// a 16-byte chunk (columns col .. col+E16-1 of row `row`) into a staged tile
+template <bool SWZ, typename T>
+__device__ __forceinline__ void bk_put16(T* dst, int pitch, int row, int col, const u32x4& u) {
+  if constexpr (SWZ) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 lo = {u[0], u[1]}, hi = {u[2], u[3]};
+    *(u32x2*)(dst + row * pitch + bk_xsw(row, col)) = lo;
+    *(u32x2*)(dst + row * pitch + bk_xsw(row, col + 4)) = hi;
+  } else {
+    *(u32x4*)(dst + row * pitch + col) = u;
+  }
+}
+// byte offset of the 16-byte chunk idx of a state in its staged layout
+template <bool SWZ>
+__device__ __forceinline__ int bk_state_off(int idx) {
+  return SWZ ? (idx >> 5) * 512 + bk_qsw((idx & 31) * 16) : idx * 16;
+}
+
 // 64 rows of a [rows][stride] tensor (ncol columns from src) into LDS rows of
 // `pitch` elements; rows at or past `valid` read zeros (range-checked loads)
-template <typename T>
+template <bool SWZ, typename T>
 __device__ __forceinline__ void bk_stage_rows(T* dst, int pitch, const T* src, i64 stride, int ncol, int valid,
                                               int tid) {
   constexpr int E16 = 16 / sizeof(T);
@@ -50,21 +123,24 @@ __device__ __forceinline__ void bk_stage_rows(T* dst, int pitch, const T* src, i
   const brsrc r = make_rsrc(src, valid > 0 ? (unsigned)(((valid - 1) * stride + ncol) * sizeof(T)) : 0u);
   for (int idx = tid; idx < BK_R * cpr; idx += BK_NTH) {
     const int row = idx / cpr, col = (idx % cpr) * E16;
-    *(u32x4*)(dst + row * pitch + col) = bload16(r, (unsigned)((row * stride + col) * sizeof(T)));
+    bk_put16<SWZ>(dst, pitch, row, col, bload16(r, (unsigned)((row * stride + col) * sizeof(T))));
   }
 }
-// one [P x N] state in native tile order (contiguous)
-template <typename T>
+// one [P x N] state in native tile order
+template <bool SWZ, typename T>
 __device__ __forceinline__ void bk_stage_state(T* dst, const T* src, int PN, int tid) {
   constexpr int E16 = 16 / sizeof(T);
   const brsrc r = make_rsrc(src, (unsigned)(PN * sizeof(T)));
-  for (int idx = tid; idx < PN / E16; idx += BK_NTH) *(u32x4*)(dst + idx * E16) = bload16(r, (unsigned)idx * 16u);
+  for (int idx = tid; idx < PN / E16; idx += BK_NTH)
+    *(u32x4*)((char*)dst + bk_state_off<SWZ>(idx)) = bload16(r, (unsigned)idx * 16u);
 }
 
+// bf16: two workgroups per CU, at most 256 registers (VGPR + AGPR) per lane
 template <typename T, int CP, int CN>
-__global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
+__global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) ssd_blocked_bwd_kernel(SsdArgs a) {
   constexpr bool BF = sizeof(T) == 2;
-  constexpr int PAD = BF ? 8 : 4;
+  constexpr bool SWZ = BF && CP && CN && CP % 64 == 0 && CN % 64 == 0;  // swizzled, unpadded tiles
+  constexpr int PAD = SWZ ? 0 : (BF ? 8 : 4);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int P = CP ? CP : (int)a.P, N = CN ? CN : (int)a.N, M = (int)a.M, L = (int)a.L;
   const int PT = P / 16, NT = N / 16, LM = (int)a.LM, nblk = LM / BK_R;
@@ -133,12 +209,12 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
 #pragma unroll
     for (int it = 0; it < MAXN; ++it) {
       const int idx = tid + it * BK_NTH;
-      if (idx < BK_R * cpn) *(u32x4*)(dstN + (idx / cpn) * LDN + (idx % cpn) * E16) = pn[it];
+      if (idx < BK_R * cpn) bk_put16<SWZ>(dstN, LDN, idx / cpn, (idx % cpn) * E16, pn[it]);
     }
 #pragma unroll
     for (int it = 0; it < MAXP; ++it) {
       const int idx = tid + it * BK_NTH;
-      if (idx < BK_R * cpp) *(u32x4*)(dstP + (idx / cpp) * LDP + (idx % cpp) * E16) = pp[it];
+      if (idx < BK_R * cpp) bk_put16<SWZ>(dstP, LDP, idx / cpp, (idx % cpp) * E16, pp[it]);
     }
   };
 
@@ -158,7 +234,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
     f32x4 dvT[BK_TMAX];  // d_v^T tiles (rows p, columns s) of the current head
     float s1 = 0.0f, ocol = 0.0f, cum_s = 0.0f, delta_s = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
-    bk_stage_rows(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    bk_stage_rows<SWZ>(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
     issue_step(0);
     for (i64 k = 0; k < nsteps; ++k) {
       const i64 hh = k / nT, h = g * a.hpg + hh;
@@ -170,8 +246,8 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
         delta_s = __shfl(cs.delta, l_col & 63, 64);
         const float edec = exp_hw(cs.end - cum_s), xcol = delta_s * edec;
         __syncthreads();  // the previous head is done with xs / STs
-        bk_stage_rows(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-        bk_stage_state(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+        bk_stage_rows<SWZ>(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+        bk_stage_state<SWZ>(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
         __syncthreads();
         // K3: d_dv^T = dS_{c+1}.B^T (rows p, columns s); dB_k3^T += dS^T . (xcol v)^T
         s1 = 0.0f;
@@ -182,9 +258,9 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
           if (pt >= PT) continue;
           f32x4 acc = zero4();
           for (int kb = 0; kb < NT; ++kb)
-            mma(acc, ld_ntv_t(STs + tile_off(pt, kb), lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+            mma(acc, bk_ntv_t<SWZ>(STs + tile_off(pt, kb), lane), bk_colk<SWZ>(Bs, LDN, 16 * w, 16 * kb, lane));
           float xv[4];
-          frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);  // x[s][p .. p+3], p = 16 pt + 4q
+          frag_get(bk_colk<SWZ>(xs, LDP, 16 * w, 16 * pt, lane), xv);  // x[s][p .. p+3], p = 16 pt + 4q
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             s1 += acc[j] * xv[j];  // d_decay / delta = sum_p d_dv . x
@@ -196,7 +272,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
           if (nt >= NT) continue;
           f32x4 acc = zero4();
           for (int kb = 0; kb < PT; ++kb)
-            mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
+            mma(acc, bk_ntv<SWZ>(STs + tile_off(kb, nt), lane), bk_colk<SWZ>(xs, LDP, 16 * w, 16 * kb, lane));
 #pragma unroll
           for (int j = 0; j < 4; ++j) dBT[nt][j] += acc[j] * xcol;
         }
@@ -212,9 +288,9 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
       for (int tt = 0; tt < 4; ++tt) {
         f32x4 cb = zero4(), g1 = zero4();
         for (int kb = 0; kb < NT; ++kb)
-          mma(cb, ld_colk(Cs, LDN, 16 * tt, 16 * kb, lane), ld_colk(Bs, LDN, 16 * w, 16 * kb, lane));
+          mma(cb, bk_colk<SWZ>(Cs, LDN, 16 * tt, 16 * kb, lane), bk_colk<SWZ>(Bs, LDN, 16 * w, 16 * kb, lane));
         for (int kb = 0; kb < PT; ++kb)
-          mma(g1, ld_colk(dys, LDP, 16 * tt, 16 * kb, lane), ld_colk(xs, LDP, 16 * w, 16 * kb, lane));
+          mma(g1, bk_colk<SWZ>(dys, LDP, 16 * tt, 16 * kb, lane), bk_colk<SWZ>(xs, LDP, 16 * w, 16 * kb, lane));
         float wv[4], dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -233,13 +309,13 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
       for (int pt = 0; pt < BK_TMAX; ++pt) {  // d_v_or^T += dy^T . w
         if (pt >= PT) continue;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) mma(dvT[pt], ld_rowk(dys, LDP, 16 * tt, 16 * pt, lane), wf[tt]);
+        for (int tt = 0; tt < 4; ++tt) mma(dvT[pt], bk_rowk<SWZ>(dys, LDP, 16 * tt, 16 * pt, lane), wf[tt]);
       }
 #pragma unroll
       for (int nt = 0; nt < BK_TMAX; ++nt) {  // dB_k2^T += C^T . d_cb
         if (nt >= NT) continue;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], ld_rowk(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
+        for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], bk_rowk<SWZ>(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
       }
 
       if (tb == nblk - 1) {
@@ -251,7 +327,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
         for (int pt = 0; pt < BK_TMAX; ++pt) {
           if (pt >= PT) continue;
           float xv[4];
-          frag_get(ld_colk(xs, LDP, 16 * w, 16 * pt, lane), xv);
+          frag_get(bk_colk<SWZ>(xs, LDP, 16 * w, 16 * pt, lane), xv);
           f32x4 o;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -292,7 +368,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
     for (int i = 0; i < BK_TMAX; ++i) dCT[i] = zero4();
     float blue = 0.0f, orow = 0.0f, cum_t = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
-    bk_stage_rows(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    bk_stage_rows<SWZ>(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
     issue_step(0);
     for (i64 k = 0; k < nsteps; ++k) {
       const i64 hh = k / nS, h = g * a.hpg + hh;
@@ -303,15 +379,15 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
         cum_t = __shfl(cs.cum, l_col & 63, 64);
         const float ecol = exp_hw(cum_t);
         __syncthreads();  // the previous head is done with dys / STs
-        bk_stage_rows(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-        bk_stage_state(STs, (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+        bk_stage_rows<SWZ>(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
+        bk_stage_state<SWZ>(STs, (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
         __syncthreads();
         if (blk == 0) {  // d_end = sum_{p,n} S_c * dS_{c+1}, once per chunk and head
           const brsrc rdS = make_rsrc((const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, (unsigned)PN * esz);
           float part = 0.0f;
           for (int idx = tid; idx < PN / E16; idx += BK_NTH) {
             const u32x4 u = bload16(rdS, (unsigned)idx * 16u);
-            const u32x4 v = *(const u32x4*)(STs + idx * E16);
+            const u32x4 v = *(const u32x4*)((const char*)STs + bk_state_off<SWZ>(idx));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if constexpr (BF) {
@@ -339,9 +415,9 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
           if (nt >= NT) continue;
           f32x4 acc = zero4();
           for (int kb = 0; kb < PT; ++kb)  // A: rows n, k = p (native tile); B: k = p, columns t
-            mma(acc, ld_ntv(STs + tile_off(kb, nt), lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+            mma(acc, bk_ntv<SWZ>(STs + tile_off(kb, nt), lane), bk_colk<SWZ>(dys, LDP, 16 * w, 16 * kb, lane));
           float cv[4];
-          frag_get(ld_colk(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
+          frag_get(bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float val = acc[j] * ecol;
@@ -361,9 +437,9 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
       for (int ss = 0; ss < 4; ++ss) {
         f32x4 cb = zero4(), g1 = zero4();
         for (int kb = 0; kb < NT; ++kb)
-          mma(cb, ld_colk(Bs, LDN, 16 * ss, 16 * kb, lane), ld_colk(Cs, LDN, 16 * w, 16 * kb, lane));
+          mma(cb, bk_colk<SWZ>(Bs, LDN, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * kb, lane));
         for (int kb = 0; kb < PT; ++kb)
-          mma(g1, ld_colk(xs, LDP, 16 * ss, 16 * kb, lane), ld_colk(dys, LDP, 16 * w, 16 * kb, lane));
+          mma(g1, bk_colk<SWZ>(xs, LDP, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(dys, LDP, 16 * w, 16 * kb, lane));
         float dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -381,7 +457,7 @@ __global__ void __launch_bounds__(BK_NTH) ssd_blocked_bwd_kernel(SsdArgs a) {
       for (int nt = 0; nt < BK_TMAX; ++nt) {  // dC_k2^T += B^T . d_cb^T
         if (nt >= NT) continue;
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], ld_rowk(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
+        for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], bk_rowk<SWZ>(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
       }
 
       if (sb == blk) {  // the head's row sums
@@ -439,8 +515,9 @@ __global__ void __launch_bounds__(64) ssd_blocked_epilogue_kernel(SsdArgs a) {
 // ===========================================================================
 // host side
 // ===========================================================================
-static size_t blocked_lds_bytes(i64 P, i64 N, bool bf) {
-  const i64 e = bf ? 2 : 4, pad = bf ? 8 : 4;
+// swz: the bf16 instantiation for P = 64, N = 128, whose tiles are unpadded
+static size_t blocked_lds_bytes(i64 P, i64 N, bool bf, bool swz = false) {
+  const i64 e = bf ? 2 : 4, pad = swz ? 0 : (bf ? 8 : 4);
   return (size_t)(e * (2 * BK_R * (N + pad) + 2 * BK_R * (P + pad) + P * N) + 4 * BK_NW);
 }
 
@@ -456,9 +533,10 @@ bool ssd_blocked_supported(const ssmvjp_ssd_desc& d) {
 
 template <typename T>
 static void launch_blocked_t(const SsdArgs& a, hipStream_t stream) {
-  const size_t lds = blocked_lds_bytes(a.P, a.N, sizeof(T) == 2);
+  const bool fixed = a.P == 64 && a.N == 128;
+  const size_t lds = blocked_lds_bytes(a.P, a.N, sizeof(T) == 2, fixed && sizeof(T) == 2);
   const i64 grid = a.b * a.nc * a.G * 2 * (a.LM / BK_R);
-  if (a.P == 64 && a.N == 128)
+  if (fixed)
     hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
   else
     hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
