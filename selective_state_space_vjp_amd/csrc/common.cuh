@@ -154,6 +154,14 @@ __device__ __forceinline__ short bf16_bits(float f) {
   bf16 b = (bf16)f;
   return __builtin_bit_cast(short, b);
 }
+// two floats rounded to bf16 (nearest even, as bf16_bits) in one dword, lo in
+// bits 0..15: a single two-operand v_cvt_pk_bf16_f32
+__device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
+}
 
 __device__ __forceinline__ f32x4 zero4() {
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -196,9 +204,10 @@ __device__ __forceinline__ Frag<float> frag_make<float>(const float v[4]) {
 }
 template <>
 __device__ __forceinline__ Frag<bf16> frag_make<bf16>(const float v[4]) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t u = {pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])};
   Frag<bf16> f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.v[j] = bf16_bits(v[j]);
+  f.v = __builtin_bit_cast(s16x4, u);
   return f;
 }
 

@@ -63,9 +63,9 @@ __device__ __forceinline__ i64 native_off(int N, int pt, int nt, int lane, int j
 
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
 __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
-  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 u = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  *(bf16x4*)p = u;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 u = {pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])};
+  *(u32x2*)p = u;
 }
 
 // four float results stored as 4 consecutive elements of T through a resource
@@ -76,8 +76,7 @@ __device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, c
 }
 __device__ __forceinline__ void bstore4(brsrc r, unsigned off, const f32x4& v, const bf16*) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 u = {(unsigned)(unsigned short)bf16_bits(v[0]) | ((unsigned)(unsigned short)bf16_bits(v[1]) << 16),
-             (unsigned)(unsigned short)bf16_bits(v[2]) | ((unsigned)(unsigned short)bf16_bits(v[3]) << 16)};
+  const u32x2 u = {pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])};
   __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
 }
 
@@ -99,7 +98,7 @@ __device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float lo = __uint_as_float(u[e] << 16) * s, hi = __uint_as_float(u[e] & 0xffff0000u) * s;
-    o[e] = (unsigned)(unsigned short)bf16_bits(lo) | ((unsigned)(unsigned short)bf16_bits(hi) << 16);
+    o[e] = pk_bf16(lo, hi);
   }
   return o;
 }
