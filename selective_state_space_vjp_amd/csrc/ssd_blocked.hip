@@ -40,29 +40,17 @@ constexpr int BK_NTH = 64 * BK_NW;
 constexpr int BK_R = 64;             // fused rows per block
 constexpr int BK_TMAX = 8;           // P / 16 and N / 16 at most
 
-// Swizzled LDS layouts (bf16 tiles whose rows are whole 128-byte segments, the
-// workload shapes).  Rows of the staged input tiles have no padding; within each
-// 128-byte segment of a row the 8-byte unit u is stored at u ^ f(row),
-// f(row) = 4 (row % 4) + (row / 4) % 4.  A fragment read along the rows (16
-// consecutive rows from a multiple of 16, one unit each) and a transposed read
-// (4 consecutive rows from a multiple of 4, 4 consecutive units each) then hit
-// 16 distinct 8-byte bank pairs.  The state tiles keep MFMA output order with
-// each 128-byte quarter of a 512-byte tile rotated by 32 bytes per quarter, so
-// that the transposed read, which takes 8 bytes at the same offset of every
-// quarter, hits distinct banks.
-__device__ __forceinline__ int bk_xsw(int row, int col) {  // element offset in the row of column col, col % 4 == 0
-  const int u = col >> 2;
-  return ((u & ~15) | ((u & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3)))) << 2;
-}
+// Swizzled LDS layouts (the bf16 P = 64, N = 128 instantiation): the staged
+// input tiles are XOR-swizzled (xsw_off), and the state tiles keep MFMA output
+// order with each 128-byte quarter of a 512-byte tile rotated by 32 bytes per
+// quarter, so that the transposed read, which takes 8 bytes at the same offset
+// of every quarter, hits distinct banks.
 __device__ __forceinline__ int bk_qsw(int byte) { return (byte & ~127) | ((byte + 32 * ((byte >> 7) & 3)) & 127); }
 
 template <bool SWZ, typename T>
 __device__ __forceinline__ Frag<T> bk_colk(const T* t, int pitch, int c0, int k0, int lane) {
   if constexpr (SWZ) {
-    const int row = c0 + (lane & 15);
-    Frag<T> f;
-    f.v = *(const s16x4*)(t + row * pitch + bk_xsw(row, k0 + 4 * (lane >> 4)));
-    return f;
+    return ld_colk_xs(t, pitch, c0, k0, lane);
   } else {
     return ld_colk(t, pitch, c0, k0, lane);
   }
@@ -70,8 +58,7 @@ __device__ __forceinline__ Frag<T> bk_colk(const T* t, int pitch, int c0, int k0
 template <bool SWZ, typename T>
 __device__ __forceinline__ Frag<T> bk_rowk(const T* t, int pitch, int k0, int c0, int lane) {
   if constexpr (SWZ) {
-    const int m = lane & 15, row = k0 + 4 * (lane >> 4) + (m >> 2);
-    return lds_tr_b16(t + row * pitch + bk_xsw(row, c0 + 4 * (m & 3)));
+    return ld_rowk_xs(t, pitch, k0, c0, lane);
   } else {
     return ld_rowk(t, pitch, k0, c0, lane);
   }
@@ -99,10 +86,7 @@ __device__ __forceinline__ Frag<T> bk_ntv_t(const T* t, int lane) {
 template <bool SWZ, typename T>
 __device__ __forceinline__ void bk_put16(T* dst, int pitch, int row, int col, const u32x4& u) {
   if constexpr (SWZ) {
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 lo = {u[0], u[1]}, hi = {u[2], u[3]};
-    *(u32x2*)(dst + row * pitch + bk_xsw(row, col)) = lo;
-    *(u32x2*)(dst + row * pitch + bk_xsw(row, col + 4)) = hi;
+    st16_xs(dst, pitch, row, col, u);
   } else {
     *(u32x4*)(dst + row * pitch + col) = u;
   }

@@ -103,6 +103,35 @@ __device__ __forceinline__ u32x4 scale16(u32x4 u, float s, const bf16*) {
   return o;
 }
 
+// XOR-swizzled bf16 tiles: rows without padding whose length is a multiple of
+// 64 elements (whole 128-byte segments).  Within each 128-byte segment of a row
+// the 8-byte unit u is stored at u ^ f(row), f(row) = 4 (row % 4) + (row / 4) % 4.
+// A fragment read along the rows (16 consecutive rows from a multiple of 16,
+// one unit each: ld_colk_xs) and a transposed read (4 consecutive rows from a
+// multiple of 4, 4 consecutive units each: ld_rowk_xs) then hit 16 distinct
+// 8-byte bank pairs; no plain row pitch serves both.
+__device__ __forceinline__ int xsw_off(int row, int col) {  // element offset of column col (col % 4 == 0) in its row
+  const int u = col >> 2;
+  return ((u & ~15) | ((u & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3)))) << 2;
+}
+__device__ __forceinline__ Frag<bf16> ld_colk_xs(const bf16* t, int pitch, int c0, int k0, int lane) {
+  const int row = c0 + (lane & 15);
+  Frag<bf16> f;
+  f.v = *(const s16x4*)(t + row * pitch + xsw_off(row, k0 + 4 * (lane >> 4)));
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> ld_rowk_xs(const bf16* t, int pitch, int k0, int c0, int lane) {
+  const int m = lane & 15, row = k0 + 4 * (lane >> 4) + (m >> 2);
+  return lds_tr_b16(t + row * pitch + xsw_off(row, c0 + 4 * (m & 3)));
+}
+// a 16-byte chunk (columns col .. col+7 of row `row`) into a swizzled tile
+__device__ __forceinline__ void st16_xs(bf16* t, int pitch, int row, int col, const u32x4& u) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 lo = {u[0], u[1]}, hi = {u[2], u[3]};
+  *(u32x2*)(t + row * pitch + xsw_off(row, col)) = lo;
+  *(u32x2*)(t + row * pitch + xsw_off(row, col + 4)) = hi;
+}
+
 // Per-chunk step sizes for one head, one lane per step l < L (lanes >= L and
 // steps past T get zeros, which keeps cumA flat over a short last chunk).
 // z is this lane's dt (Mamba-2) or da (RAW) value, Ah the head's A (Mamba-2).
