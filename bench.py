@@ -191,6 +191,34 @@ def bench_kda(args, dev):
     print(json.dumps(line), flush=True)
 
 
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB infinity cache
+
+
+def cold_cache_steps(step_fns, n, dev):
+    """Per-step times with the infinity cache evicted before every step: a
+    512 MiB buffer is overwritten between steps (outside the timed events), so
+    each step starts with none of its inputs cached, as after other layers'
+    traffic.  step_fns are the step's stages; returns the median ms of each
+    stage and of the whole step."""
+    import torch
+
+    scratch = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    per = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(step_fns) + 1)]
+        evs[0].record()
+        for k, f in enumerate(step_fns):
+            f()
+            evs[k + 1].record()
+        torch.cuda.synchronize()
+        per.append([evs[k].elapsed_time(evs[k + 1]) for k in range(len(step_fns))])
+    del scratch
+    med = lambda v: sorted(v)[len(v) // 2]
+    stages = [med([p[k] for p in per]) for k in range(len(step_fns))]
+    return stages, med([sum(p) for p in per])
+
+
 def bench_fwd(args, dev):
     """The chunked forward (ssd_chunk_fwd: y and the final state) at the Mamba-2
     chunked workload shape: one step is one forward over the batch."""
@@ -248,6 +276,10 @@ def bench_fwd(args, dev):
                      "kernel": "ssd_fwd_scores_kernel + ssd_fwd_walk_kernel (one ssd_chunk_fwd call)",
                      "algorithmic_bytes_per_launch": fwd_bytes, "avg_launch_ms": round(call_ms, 4)},
     }
+    _, cold_ms = cold_cache_steps([step], min(K, 20), dev)
+    line["cold_cache"] = {"flush_bytes": MALL_FLUSH_BYTES, "ms_per_step": round(cold_ms, 4),
+                          "tokens_per_s": round(b * T / (cold_ms / 1e3), 1),
+                          "note": "median per-step event time, infinity cache evicted before each step"}
     if not args.no_cpu_baseline:
         import oracle
 
@@ -380,6 +412,11 @@ def main():
         "path_roofline": {"algorithmic_bytes": ab["path"], "achieved_GBps": round(ab["path"] / (ms_per_step * 1e6), 1),
                           "frac": round(ab["path"] / (ms_per_step * 1e6) / HBM_PEAK_GBS, 4)},
     }
+    (cold_scans, cold_grads), cold_ms = cold_cache_steps([call.states, call.grads], min(K, 20), dev)
+    line["cold_cache"] = {"flush_bytes": MALL_FLUSH_BYTES, "ms_per_step": round(cold_ms, 4),
+                          "tokens_per_s": round(tokens / (cold_ms / 1e3), 1),
+                          "state_scans_ms": round(cold_scans, 4), "chunk_grads_ms": round(cold_grads, 4),
+                          "note": "median per-step event times, infinity cache evicted before each step"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, w)
     print(json.dumps(line), flush=True)
