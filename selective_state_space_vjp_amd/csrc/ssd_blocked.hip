@@ -119,14 +119,18 @@ __device__ __forceinline__ void bk_stage_state(T* dst, const T* src, int PN, int
     *(u32x4*)((char*)dst + bk_state_off<SWZ>(idx)) = bload16(r, (unsigned)idx * 16u);
 }
 
-// bf16: two workgroups per CU, at most 256 registers (VGPR + AGPR) per lane
-template <typename T, int CP, int CN>
+// bf16: two workgroups per CU, at most 256 registers (VGPR + AGPR) per lane.
+// CP, CN, CM: compile-time P, N and rank M (0: from the arguments).
+template <typename T, int CP, int CN, int CM>
 __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) ssd_blocked_bwd_kernel(SsdArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr bool SWZ = BF && CP && CN && CP % 64 == 0 && CN % 64 == 0;  // swizzled, unpadded tiles
   constexpr int PAD = SWZ ? 0 : (BF ? 8 : 4);
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int P = CP ? CP : (int)a.P, N = CN ? CN : (int)a.N, M = (int)a.M, L = (int)a.L;
+  const int P = CP ? CP : (int)a.P, N = CN ? CN : (int)a.N, M = CM ? CM : (int)a.M, L = (int)a.L;
+  // with a compile-time rank that is a multiple of 4, the 4 rows a lane holds
+  // in a 16x16 tile (4q .. 4q+3) belong to one step: one decay per tile and lane
+  constexpr bool STEP4 = CM != 0 && CM % 4 == 0;
   const int PT = P / 16, NT = N / 16, LM = (int)a.LM, nblk = LM / BK_R;
   const int LDN = N + PAD, LDP = P + PAD, PN = P * N;
   T* Bs = (T*)smem_raw;    // [64][LDN] B rows of a source block
@@ -276,11 +280,20 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
         for (int kb = 0; kb < PT; ++kb)
           mma(g1, bk_colk<SWZ>(dys, LDP, 16 * tt, 16 * kb, lane), bk_colk<SWZ>(xs, LDP, 16 * w, 16 * kb, lane));
         float wv[4], dv[4];
+        float dec4 = 0.0f;
+        if constexpr (STEP4) {
+          const int lt = (tb * BK_R + 16 * tt + 4 * q) / CM;
+          const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
+          dec4 = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int lt = (tb * BK_R + 16 * tt + 4 * q + j) / M;
-          const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
-          const float dec = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
+          float dec = dec4;
+          if constexpr (!STEP4) {
+            const int lt = (tb * BK_R + 16 * tt + 4 * q + j) / M;
+            const float ct = __shfl(cs.cum, lt & 63, 64);  // every lane takes part in the shuffle
+            dec = (l_col <= lt && lt < Lc) ? exp_hw(ct - cum_s) : 0.0f;
+          }
           const float dcb = g1[j] * delta_s * dec;  // d_w = dy.v^T with v = delta x (delta = 1 for RAW)
           ocol += dcb * cb[j];
           wv[j] = cb[j] * dec;
@@ -425,13 +438,23 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
         for (int kb = 0; kb < PT; ++kb)
           mma(g1, bk_colk<SWZ>(xs, LDP, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(dys, LDP, 16 * w, 16 * kb, lane));
         float dv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ls = (sb * BK_R + 16 * ss + 4 * q + j) / M;
+        float dd4 = 0.0f;  // delta_s * decay
+        if constexpr (STEP4) {
+          const int ls = (sb * BK_R + 16 * ss + 4 * q) / CM;
           const float cs_s = __shfl(cs.cum, ls & 63, 64);  // every lane takes part in the shuffles
           const float d_s = __shfl(cs.delta, ls & 63, 64);
-          const float dec = (ls <= l_col && l_col < Lc) ? exp_hw(cum_t - cs_s) : 0.0f;
-          const float dcb = g1[j] * d_s * dec;
+          dd4 = (ls <= l_col && l_col < Lc) ? d_s * exp_hw(cum_t - cs_s) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float dd = dd4;
+          if constexpr (!STEP4) {
+            const int ls = (sb * BK_R + 16 * ss + 4 * q + j) / M;
+            const float cs_s = __shfl(cs.cum, ls & 63, 64);  // every lane takes part in the shuffles
+            const float d_s = __shfl(cs.delta, ls & 63, 64);
+            dd = (ls <= l_col && l_col < Lc) ? d_s * exp_hw(cum_t - cs_s) : 0.0f;
+          }
+          const float dcb = g1[j] * dd;
           orow += dcb * cb[j];
           dv[j] = dcb;
         }
@@ -520,10 +543,12 @@ static void launch_blocked_t(const SsdArgs& a, hipStream_t stream) {
   const bool fixed = a.P == 64 && a.N == 128;
   const size_t lds = blocked_lds_bytes(a.P, a.N, sizeof(T) == 2, fixed && sizeof(T) == 2);
   const i64 grid = a.b * a.nc * a.G * 2 * (a.LM / BK_R);
-  if (fixed)
-    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  if (fixed && a.M == 4)  // the rank-4 MIMO workload shape
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 4>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  else if (fixed)
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
   else
-    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
   hipLaunchKernelGGL(ssd_blocked_epilogue_kernel, dim3((unsigned)(a.b * a.nc * a.H)), dim3(64), 0, stream, a);
 }
 
