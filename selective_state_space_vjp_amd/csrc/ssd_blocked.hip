@@ -210,10 +210,9 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     // ======================= source block s = blk =========================
     // steps: (head hh, target block tb) for tb = blk .. nblk-1, heads in order
     const int nT = nblk - blk;
-    const i64 nsteps = a.hpg * nT;
-    auto issue_step = [&](i64 k) {
-      const i64 h = g * a.hpg + k / nT;
-      const int tb = blk + (int)(k % nT);
+    const int nsteps = (int)a.hpg * nT;
+    auto issue_step = [&](int hh, int tb) {
+      const i64 h = g * a.hpg + hh;
       issue(Cg + (i64)tb * BK_R * bstr, (const T*)a.dy + xrow0 + (i64)tb * BK_R * xstr + h * P, valid_in(tb));
     };
     f32x4 dBT[BK_TMAX];  // dB^T tiles (rows n, columns s), summed over the group's heads
@@ -223,10 +222,10 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     float s1 = 0.0f, ocol = 0.0f, cum_s = 0.0f, delta_s = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
     bk_stage_rows<SWZ>(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
-    issue_step(0);
-    for (i64 k = 0; k < nsteps; ++k) {
-      const i64 hh = k / nT, h = g * a.hpg + hh;
-      const int tb = blk + (int)(k % nT);
+    issue_step(0, blk);
+    // step k = (head hh, target block tb), counted without divisions
+    for (int k = 0, hh = 0, tb = blk; k < nsteps; ++k, tb = (tb + 1 == nblk) ? blk : tb + 1, hh += (tb == blk)) {
+      const i64 h = g * a.hpg + hh;
       if (tb == blk) {
         // ---- a new head: its scalars, x / v rows and dS_{c+1}; then the K3 backward ----
         cs = scalars(h);
@@ -269,7 +268,10 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
       // ---- ORANGE and K2 for the pair (t block tb, s block blk) ----
       __syncthreads();  // the previous pair is done with Cs / dys
       commit(Cs, dys);
-      issue_step(k + 1 < nsteps ? k + 1 : k);  // unconditional: the last step reloads its own rows
+      {  // the next step's rows; the last step reloads its own, which keeps the issue unconditional
+        const bool more = k + 1 < nsteps, wrap = tb + 1 == nblk;
+        issue_step(more && wrap ? hh + 1 : hh, more ? (wrap ? blk : tb + 1) : tb);
+      }
       __syncthreads();
       Frag<T> wf[4], df[4];  // w and d_cb tiles (rows t, columns s): operands with k = t
 #pragma unroll
@@ -354,10 +356,9 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     // ======================= target block t = blk =========================
     // steps: (head hh, source block sb) for sb = 0 .. blk, heads in order
     const int nS = blk + 1;
-    const i64 nsteps = a.hpg * nS;
-    auto issue_step = [&](i64 k) {
-      const i64 h = g * a.hpg + k / nS;
-      const int sb = (int)(k % nS);
+    const int nsteps = (int)a.hpg * nS;
+    auto issue_step = [&](int hh, int sb) {
+      const i64 h = g * a.hpg + hh;
       issue(Bg + (i64)sb * BK_R * bstr, (const T*)a.xv + xrow0 + (i64)sb * BK_R * xstr + h * P, valid_in(sb));
     };
     f32x4 dCT[BK_TMAX];  // dC^T tiles (rows n, columns t), summed over the group's heads
@@ -366,10 +367,10 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     float blue = 0.0f, orow = 0.0f, cum_t = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
     bk_stage_rows<SWZ>(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
-    issue_step(0);
-    for (i64 k = 0; k < nsteps; ++k) {
-      const i64 hh = k / nS, h = g * a.hpg + hh;
-      const int sb = (int)(k % nS);
+    issue_step(0, 0);
+    // step k = (head hh, source block sb), counted without divisions
+    for (int k = 0, hh = 0, sb = 0; k < nsteps; ++k, sb = (sb == blk) ? 0 : sb + 1, hh += (sb == 0)) {
+      const i64 h = g * a.hpg + hh;
       if (sb == 0) {
         // ---- a new head: its scalars, dy rows and S_c; d_end; BLUE ----
         cs = scalars(h);
@@ -427,7 +428,10 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
       // ---- ORANGE row sums and K2 for the pair (t block blk, s block sb), transposed tiles ----
       __syncthreads();  // the previous pair is done with Bs / xs
       commit(Bs, xs);
-      issue_step(k + 1 < nsteps ? k + 1 : k);  // unconditional: the last step reloads its own rows
+      {  // the next step's rows; the last step reloads its own, which keeps the issue unconditional
+        const bool more = k + 1 < nsteps, wrap = sb == blk;
+        issue_step(more && wrap ? hh + 1 : hh, more ? (wrap ? 0 : sb + 1) : sb);
+      }
       __syncthreads();
       Frag<T> df[4];  // d_cb^T tiles (rows s, columns t): operands with k = s
 #pragma unroll
