@@ -54,13 +54,17 @@ constexpr int PB_SET = PB_DEND + 16;
 // LDS layout (bytes)
 constexpr int L_CB = 0;                                  // float [64][LDC]
 constexpr int L_PB = L_CB + LM16 * LDC * 4;              // float [2][PB_SET]
-constexpr int L_SC = L_PB + 2 * PB_SET * 4;              // float [2][64]: cumA, delta of the current head
-constexpr int L_B = L_SC + 2 * 64 * 4;                   // bf16 [64][LDN]
+// x, dy, dS_{c+1} and the step scalars are double buffered by head parity: the
+// next head is staged during phase B of the current one, which reads them;
+// S_c, read only in phase A, is staged in place during phase B
+constexpr int SC_N = 5;                                  // per-step values: cumA, delta, and the factors below
+constexpr int L_SC = L_PB + 2 * PB_SET * 4;              // float [2][SC_N][64], by head parity
+constexpr int L_B = L_SC + 2 * SC_N * 64 * 4;            // bf16 [64][LDN]
 constexpr int L_C = L_B + LM16 * LDN * 2;                // bf16 [64][LDN]
-constexpr int L_X = L_C + LM16 * LDN * 2;                // bf16 [64][LDP]
-constexpr int L_DY = L_X + LM16 * LDP * 2;               // bf16 [64][LDP]
-constexpr int L_DS = L_DY + LM16 * LDP * 2;              // bf16 [P*N] dS_{c+1}, native tiles
-constexpr int L_S = L_DS + PN * 2;                       // bf16 [P*N] S_c, native tiles
+constexpr int L_X = L_C + LM16 * LDN * 2;                // bf16 [2][64][LDP]
+constexpr int L_DY = L_X + 2 * LM16 * LDP * 2;           // bf16 [2][64][LDP]
+constexpr int L_DS = L_DY + 2 * LM16 * LDP * 2;          // bf16 [2][P*N] dS_{c+1}, native tiles
+constexpr int L_S = L_DS + 2 * PN * 2;                   // bf16 [P*N] S_c, native tiles
 constexpr int L_W = L_S + PN * 2;                        // bf16 [NPAIR][256] w tiles in MFMA output order
 constexpr int L_TOTAL = L_W + NPAIR * 256 * 2;
 
@@ -96,13 +100,12 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* CBs = (float*)(smem_raw + L_CB);
   float* pbase = (float*)(smem_raw + L_PB);
-  float* cumL = (float*)(smem_raw + L_SC);
-  float* delL = cumL + 64;
+  float* scb = (float*)(smem_raw + L_SC);
   bf16* Bs = (bf16*)(smem_raw + L_B);
   bf16* Cs = (bf16*)(smem_raw + L_C);
-  bf16* xs = (bf16*)(smem_raw + L_X);
-  bf16* dys = (bf16*)(smem_raw + L_DY);
-  bf16* dSs = (bf16*)(smem_raw + L_DS);
+  bf16* xsb = (bf16*)(smem_raw + L_X);
+  bf16* dysb = (bf16*)(smem_raw + L_DY);
+  bf16* dSsb = (bf16*)(smem_raw + L_DS);
   bf16* Ss = (bf16*)(smem_raw + L_S);
   bf16* Wt = (bf16*)(smem_raw + L_W);
 
@@ -226,23 +229,47 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
   float prev_Ah = 0.0f;
 
+  // the prefetched head into the buffers of parity k (x, dy, dS_{c+1}, step
+  // scalars) and into Ss; returns its step scalars
+  ChunkScalars ncs = {0.f, 0.f, 0.f, 0.f};
+  float nA = 0.0f;
+  auto stage = [&](int k) {
+    ncs = finish_scalars(rcs);
+    nA = rA;
+    st16_as8((xy_sel ? dysb : xsb) + k * LM16 * LDP + xy_r * LDP + xy_col, rxy);
+    *(u32x4*)((char*)Ss + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rs;
+    *(u32x4*)((char*)(dSsb + k * PN) + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rd;
+    if (w == 0) {  // per step r: cumA, delta, e^cumA (BLUE), delta e^(end-cumA) (K3), e^(end-cumA)
+      float* sc = scb + k * SC_N * 64;
+      const float edec = exp_hw(ncs.end - ncs.cum);
+      sc[lane] = ncs.cum;
+      sc[64 + lane] = ncs.delta;
+      sc[128 + lane] = exp_hw(ncs.cum);
+      sc[192 + lane] = ncs.delta * edec;
+      sc[256 + lane] = edec;
+    }
+  };
+  stage(0);
+  issue(a.hph > 1 ? hbase + 1 : hbase);
+  vmem_pad_stores<1>(make_rsrc(a.dxv, 0u));  // as a head's dx store after its refill
+
   for (i64 hh = 0; hh < a.hph; ++hh) {
     const i64 h = hbase + hh;
-    float* pb = pbase + (hh & 1) * PB_SET;
-    const ChunkScalars cs = finish_scalars(rcs);
-    const float Ah = rA;
+    const int k = (int)(hh & 1);
+    float* pb = pbase + k * PB_SET;
+    const ChunkScalars cs = ncs;
+    const float Ah = nA;
     const brsrc bdx = make_rsrc(dxg + (int)h * P16, xbytes);
+    const float* cumL = scb + k * SC_N * 64;
+    const float* delL = cumL + 64;
+    const float* fbl = cumL + 128;  // e^cumA
+    const float* fk3 = cumL + 192;  // delta e^(end-cumA)
+    const float* edl = cumL + 256;  // e^(end-cumA)
+    const bf16* xs = xsb + k * LM16 * LDP;
+    const bf16* dys = dysb + k * LM16 * LDP;
+    const bf16* dSs = dSsb + k * PN;
 
-    __syncthreads();  // the previous head is done with xs / dys / Ss / dSs / the scalars (and CB on entry)
-    st16_as8((xy_sel ? dys : xs) + xy_r * LDP + xy_col, rxy);
-    *(u32x4*)((char*)Ss + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rs;
-    *(u32x4*)((char*)dSs + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rd;
-    if (w == 0) {
-      cumL[lane] = cs.cum;
-      delL[lane] = cs.delta;
-    }
-    issue(hh + 1 < a.hph ? h + 1 : h);  // unconditional: the last head reloads its own rows
-    __syncthreads();
+    __syncthreads();  // this head staged; the previous head's phase B done (and CB on entry)
 
     // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
     {
@@ -288,8 +315,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       float fcol[RB];  // per-lane column factor of row r = 16 rb + r16
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float cl = cumL[16 * rb + r16];
-        fcol[rb] = blue ? exp_hw(cl) : delL[16 * rb + r16] * exp_hw(cs.end - cl);
+        fcol[rb] = (blue ? fbl : fk3)[16 * rb + r16];
       }
       const bf16* opA = blue ? Ss : dSs;  // A: rows n, k = p (native tiles)
       const bf16* opB = blue ? dys : xs;  // B: k = p, columns r
@@ -337,7 +363,13 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       }
     }
 
-    __syncthreads();  // w tiles complete
+    __syncthreads();  // w tiles complete; Ss free
+
+    // the next head into the other buffers and Ss, then the refill with the
+    // head after it (unconditional: past the last head the last head's rows
+    // are reloaded and staged, into buffers never read again)
+    stage(k ^ 1);
+    issue(hh + 2 < a.hph ? h + 2 : hbase + a.hph - 1);
 
     // ---- phase B: K3 d_dv^T = dS_{c+1} . B^T and ORANGE d_v_or^T = dy^T . w for
     // the item (p tile ipt, row block irb); dx; K3 decay and dvx row sums ----
@@ -372,7 +404,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       }
       const int r = 16 * irb + r16;  // this lane's column
       const float dl = delL[r];
-      const float edec = exp_hw(cs.end - cumL[r]);
+      const float edec = edl[r];
       float xv[4];
       frag_get(ld_colk(xs, LDP, 16 * irb, 16 * ipt, lane), xv);  // x[r][p .. p+3], p = 16 pt + 4q
       float dvo[4], s1 = 0.0f, s2 = 0.0f;
@@ -393,11 +425,11 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         pb[PB_DVX + ipt * 64 + r] = s2;
       }
     }
-    __syncthreads();  // partial sums complete
     prev_h = h;
     prev_cs = cs;
     prev_Ah = Ah;
   }
+  __syncthreads();  // the last head's partial sums complete
   if (a.hph > 0) {
     const bool on = w == (int)((a.hph - 1) & 3);
     float2 v = make_float2(0.0f, 0.0f);
