@@ -22,8 +22,11 @@
 //                         K1 suffix sum and d_dt.
 //   phase B  wave w       item (p tile w/4, row block w%4): K3 d_v = dS B^T and
 //                         ORANGE d_v = dy^T w, dx, the K3 decay and dvx row sums.
-// The per-head step scalars (cumA, delta) sit in LDS so that per-element values
-// are LDS reads rather than lane shuffles.
+// The per-head step scalars (cumA, delta and the per-step decay factors) sit in
+// LDS so that per-element values are LDS reads rather than lane shuffles.  The
+// next head's rows and states, prefetched into registers one head ahead, are
+// written to LDS during phase B (x, dy, dS_{c+1} double buffered by head
+// parity, S_c in place): two barriers per head.
 #include "ssd_common.cuh"
 
 namespace ssmvjp {
