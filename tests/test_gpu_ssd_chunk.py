@@ -58,6 +58,13 @@ M2_SHAPES = [
     (2, 96, 4, 16, 48, 4, 16),
     (1, 77, 3, 48, 16, 1, 32),
     (1, 64, 8, 64, 64, 2, 48),
+    # P=64, N=128, L=64 (the 16-wave kernel in bf16): head loops of odd
+    # length (the next head is staged into buffers chosen by head parity),
+    # several groups, a short last chunk, a single head per workgroup
+    (1, 150, 3, 64, 128, 1, 64),
+    (2, 128, 6, 64, 128, 2, 64),
+    (4, 300, 5, 64, 128, 1, 64),
+    (1, 64, 8, 64, 128, 1, 64),
 ]
 
 
