@@ -115,7 +115,12 @@ __global__ void __launch_bounds__(SCAN_NTH) ssd_state_scan_kernel(SsdArgs a, int
             r16 = lane & 15;
   __builtin_assume(w >= 0 && w < SCAN_NW);  // lets the tile loop compile without branches
   const int nblk = N / NB;
+  // XCD-aware order: the n blocks of one (batch, head, direction) read the same
+  // v or dy rows, and the heads of a batch the same B or C rows, so
+  // consecutive ids are given workgroups that land on the same XCD (ids are
+  // dealt to the 8 XCDs round robin) and walk their chunks side by side
   i64 bid = blockIdx.x;
+  if (gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
   const int nbi = (int)(bid % nblk);
   bid /= nblk;
   const int dir = (int)(bid % 2);  // 0 forward (S), 1 reverse (dS)
