@@ -311,8 +311,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py measures one GPU: this build runs on a single MI355X and launches no multi-GPU work "
-            "(the backward shards by batch and B/C group with no exchange; see the design notes).")
+        log("bench.py measures one GPU: the library runs on a single MI355X and launches no multi-GPU work "
+            "(the backward would shard by batch and B/C group, with no exchange between GPUs).")
         sys.exit(2)
 
     import numpy as np

@@ -24,7 +24,7 @@
  *       Mamba-2 (per-head decay) and Mamba-1 (per-state decay) branches, and the
  *       five mutations of its verification table.
  *
- * Readings taken where the pages are silent (each is listed in the design notes):
+ * Readings taken where the pages are silent:
  *  - dt is the raw pre-softplus value; delta = softplus(dt) (P3: "drop the
  *    softplus derivative" is a defect).  softplus(z) = log1p(exp(z)), z > 20 -> z.
  *  - the input is scaled by delta (P1: "(pre-scaled) input v"): v = x * delta.
