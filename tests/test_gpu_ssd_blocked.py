@@ -51,7 +51,17 @@ BLOCKED_SHAPES = [
     (2, 96, 2, 2, 64, 128, 2, 64),   # 128: the compile-time P=64, N=128 instance
     (1, 130, 4, 2, 64, 128, 1, 64),  # 256: P=64, N=128, two heads per group, last chunk of 2 steps
     (1, 72, 4, 3, 48, 16, 3, 48),    # 192: three blocks, odd sizes, last chunk of 24 steps
+    (1, 80, 4, 2, 128, 64, 1, 64),   # 256: the largest head dim (P = 128) supported in both dtypes
 ]
+
+
+@pytest.mark.parametrize("shape", [(1, 80, 4, 2, 128, 128, 1, 64)])
+def test_blocked_largest_bf16_shape(shape):
+    """P = N = 128: the largest state the row-blocked path supports (bf16 only)."""
+    b, T, M, H, P, N, G, L = shape
+    announce(f"ssd blocked raw bf16 largest {shape}")
+    inp = synth.raw_inputs(b, T, M, H, P, N, G, seed=11)
+    _compare(_gpu_raw(inp, "bf16", L), _oracle_raw(inp, "bf16"), RAW_OUTS, TOL["bf16"])
 
 
 @pytest.mark.parametrize("shape", BLOCKED_SHAPES)

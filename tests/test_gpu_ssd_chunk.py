@@ -65,6 +65,9 @@ M2_SHAPES = [
     (2, 128, 6, 64, 128, 2, 64),
     (4, 300, 5, 64, 128, 1, 64),
     (1, 64, 8, 64, 128, 1, 64),
+    # the largest supported states: P = 128 at L = 64, P = N = 128 at L = 32
+    (1, 100, 2, 128, 64, 1, 64),
+    (1, 96, 2, 128, 128, 1, 32),
 ]
 
 
