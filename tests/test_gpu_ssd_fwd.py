@@ -56,6 +56,9 @@ M2_SHAPES = [
     (1, 64, 8, 64, 64, 2, 48),
     (1, 150, 2, 32, 80, 1, 64),
     (2, 70, 2, 96, 112, 2, 64),
+    # large heads: N = 128 (the largest state) with P = 160 and P = 256
+    (1, 80, 2, 160, 128, 1, 64),
+    (1, 100, 2, 256, 128, 1, 64),
 ]
 
 
