@@ -68,6 +68,12 @@ M2_SHAPES = [
     # the largest supported states: P = 128 at L = 64, P = N = 128 at L = 32
     (1, 100, 2, 128, 64, 1, 64),
     (1, 96, 2, 128, 128, 1, 32),
+    # 64 chunks with a short last chunk, then more chunks than a wave has
+    # lanes (65, 69), also at the 16-wave kernel's shape
+    (1, 1020, 2, 16, 32, 1, 16),
+    (1, 1030, 2, 16, 32, 1, 16),
+    (2, 1100, 2, 16, 32, 2, 16),
+    (1, 4150, 2, 64, 128, 1, 64),
 ]
 
 
@@ -86,6 +92,7 @@ RAW_SHAPES = [
     (2, 100, 2, 4, 16, 32, 4, 32),
     (1, 48, 1, 4, 32, 16, 1, 64),
     (1, 40, 4, 2, 16, 16, 1, 16),
+    (1, 530, 2, 2, 16, 16, 1, 8),  # 67 chunks
 ]
 
 
