@@ -114,6 +114,12 @@ def _ssd(**kw):
     (dict(chunk_len=128), bd.EUNSUPPORTED),
     (dict(form=1, mimo_rank=4, headdim=128, dstate=128), bd.OK),
     (dict(form=1, mimo_rank=4, headdim=128, dstate=128, dtype=0), bd.EUNSUPPORTED),
+    # byte offsets inside one batch element are 32-bit: here the stored chunk
+    # states (4 heads x 16 KiB per chunk) reach 2 GiB at 2^21 steps; the batch
+    # size does not enter the bound
+    (dict(seqlen=(1 << 21) - 64), bd.OK),
+    (dict(seqlen=1 << 21), bd.EUNSUPPORTED),
+    (dict(batch=64, seqlen=(1 << 21) - 64), bd.OK),
 ])
 def test_ssd_descriptor_validation(kw, status):
     st, _ = _ws("ssd_chunk_bwd_workspace", _ssd(**kw))
