@@ -64,6 +64,19 @@ def test_blocked_largest_bf16_shape(shape):
     _compare(_gpu_raw(inp, "bf16", L), _oracle_raw(inp, "bf16"), RAW_OUTS, TOL["bf16"])
 
 
+@pytest.mark.parametrize("shape", [(1, 130, 4, 2, 64, 128, 1, 64), (1, 128, 4, 2, 32, 32, 2, 32)])
+@pytest.mark.parametrize("regime", ["no_decay", "slow_decay"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_blocked_decay_regimes(shape, regime, dtype):
+    """da = 0 (no decay: every exp factor is 1) and da = -0.005 per step (slow
+    decay over the whole sequence), against the default inputs' fast decay."""
+    b, T, M, H, P, N, G, L = shape
+    announce(f"ssd blocked raw {dtype} {shape} {regime}")
+    inp = synth.raw_inputs(b, T, M, H, P, N, G, seed=5 + sum(shape))
+    inp["da"][:] = 0.0 if regime == "no_decay" else -0.005
+    _compare(_gpu_raw(inp, dtype, L), _oracle_raw(inp, dtype), RAW_OUTS, TOL[dtype])
+
+
 @pytest.mark.parametrize("shape", BLOCKED_SHAPES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_blocked_raw_parity(shape, dtype):

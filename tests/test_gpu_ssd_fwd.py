@@ -71,6 +71,24 @@ def test_mamba2_form_parity(shape, dtype):
     _compare(_gpu_m2(inp, dtype, L), _oracle_m2(inp, dtype), TOL[dtype])
 
 
+@pytest.mark.parametrize("shape", [(1, 200, 3, 64, 128, 1, 64), (2, 130, 2, 32, 32, 2, 32)])
+@pytest.mark.parametrize("regime", ["no_decay", "weak_decay_long_steps"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_regimes(shape, regime, dtype):
+    """A = 0 (plain running sums of the inputs) and A = -0.01 with steps of
+    about 4 (slow decay, growing states), against the default inputs' fast
+    decay."""
+    b, T, H, P, N, G, L = shape
+    announce(f"ssd fwd mamba2 {dtype} {shape} {regime}")
+    inp = synth.mamba_inputs(b, T, H, P, N, G, False, seed=sum(shape) + 7)
+    if regime == "no_decay":
+        inp["A"][:] = 0.0
+    else:
+        inp["A"][:] = -0.01
+        inp["dt"] = inp["dt"] + 6.0
+    _compare(_gpu_m2(inp, dtype, L), _oracle_m2(inp, dtype), TOL[dtype])
+
+
 RAW_SHAPES = [
     # b, T, M, H, P, N, G, L
     (1, 64, 4, 2, 32, 32, 2, 16),
