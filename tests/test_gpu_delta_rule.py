@@ -74,6 +74,21 @@ def test_delta_rule_parity(shape):
     _compare(_gpu(inp, dSf), _oracle(c, dSf32))
 
 
+@pytest.mark.parametrize("case", ["no_decay", "no_write", "full_write"])
+def test_delta_rule_degenerate_gates(case):
+    """g = 0 (no decay of the state), beta = 0 (the state never changes: the
+    write path of every step is zero) and beta = 1 (each step fully replaces
+    the state's component along k), with non-zero S0 and dS_final."""
+    announce(f"delta_rule degenerate {case}")
+    inp = synth.kda_inputs(1, 40, 2, 4, 128, 64, seed=3, nonzero_state=True)
+    if case == "no_decay":
+        inp["g"][:] = 0.0
+    else:
+        inp["beta"][:] = 0.0 if case == "no_write" else 1.0
+    dSf = np.random.default_rng(5).standard_normal((1, 4, 128, 64))
+    _compare(_gpu(inp, dSf), _oracle(_f32(inp), dSf.astype(np.float32).astype(np.float64)))
+
+
 def test_delta_rule_empty_sequence():
     announce("delta_rule T=0")
     inp = synth.kda_inputs(2, 0, 1, 2, 128, 32, seed=1)

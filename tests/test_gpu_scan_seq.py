@@ -60,6 +60,22 @@ def test_random_shapes_fp32(shape):
     _compare(_gpu(inp, "f32", K), _oracle(inp, "f32"), TOL["f32"])
 
 
+@pytest.mark.parametrize("per_state", [False, True])
+@pytest.mark.parametrize("regime", ["no_decay", "weak_decay_long_steps"])
+def test_decay_regimes_fp32(per_state, regime):
+    """A = 0 (plain running sums) and A = -0.01 with steps of about 4 (slow
+    decay, growing states), for the per-head (Mamba-2) and per-state (Mamba-1)
+    decay; the default inputs cover fast decay."""
+    announce(f"scan_seq decay {regime} per_state={per_state}")
+    inp = synth.mamba_inputs(2, 70, 3, 8, 16, 1, per_state, seed=29)
+    if regime == "no_decay":
+        inp["A"][:] = 0.0
+    else:
+        inp["A"][:] = -0.01
+        inp["dt"] = inp["dt"] + 6.0
+    _compare(_gpu(inp, "f32", 8), _oracle(inp, "f32"), TOL["f32"])
+
+
 def test_bf16_storage():
     announce("scan_seq bf16 small")
     inp = synth.workload_inputs("mamba2_seq_small")
