@@ -96,6 +96,35 @@ __device__ __forceinline__ void st16_as8(bf16* p, const u32x4& u) {
 }
 __device__ __forceinline__ int tile_off(int pt, int nt) { return (pt * NT + nt) * 256; }
 
+// The four sums of x[0..3] over the 4 rows of 16 lanes (lanes with the same
+// lane % 16) at once: two row-pair swaps (odd rows of the first operand with
+// even rows of the second) and one half swap.  Row q ends with the sum of x[q].
+__device__ __forceinline__ float sum4q_x4(const float x[4]) {
+  auto bits = [](float f) { return __builtin_bit_cast(int, f); };
+  auto flt = [](unsigned u) { return __builtin_bit_cast(float, u); };
+  const auto a = __builtin_amdgcn_permlane16_swap(bits(x[0]), bits(x[1]), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(bits(x[2]), bits(x[3]), false, false);
+  const float u = flt(a[0]) + flt(a[1]), w = flt(b[0]) + flt(b[1]);  // rows: x0, x1, x0, x1 / x2, x3, x2, x3 pair sums
+  const auto c = __builtin_amdgcn_permlane32_swap(bits(u), bits(w), false, false);
+  return flt(c[0]) + flt(c[1]);
+}
+
+// The four sums of v[0..3] over the 16 lanes of a DPP row at once: a butterfly
+// that halves the values each lane carries at every exchange (partners r16 ^ 8
+// by row rotation, then 7 - r16 within the 8-lane half, then r16 ^ 2 and
+// r16 ^ 1 within the quad).  Lane r16 ends with the sum of v[r16 >> 2].
+__device__ __forceinline__ float sum16x4(const float v[4], int r16) {
+  const bool h8 = (r16 & 8) != 0, h4 = (r16 & 4) != 0;
+  const float k0 = h8 ? v[2] : v[0], k1 = h8 ? v[3] : v[1];  // kept
+  const float s0 = h8 ? v[0] : v[2], s1 = h8 ? v[1] : v[3];  // handed to the partner
+  const float a0 = k0 + dpp_f<0x128>(s0), a1 = k1 + dpp_f<0x128>(s1);  // row_ror:8
+  const float k = h4 ? a1 : a0, s = h4 ? a0 : a1;
+  float r = k + dpp_f<0x141>(s);  // row_half_mirror
+  r += dpp_f<0x4E>(r);            // quad_perm [2, 3, 0, 1]
+  r += dpp_f<0xB1>(r);            // quad_perm [1, 0, 3, 2]
+  return r;
+}
+
 // DA: also the per-chunk dA partial sums (a separate instantiation, so that
 // the plain backward keeps its registers)
 template <bool DA>
@@ -305,10 +334,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         wv[j] = cb * dec;  // w = CB * decay: the d_v_orange operand
       }
       store4(Wt + pair * 256 + 4 * lane, f32x4{wv[0], wv[1], wv[2], wv[3]});
-#pragma unroll
-      for (int j = 0; j < 4; ++j) orow[j] = sum16(orow[j]);
+      const float osum = sum16x4(orow, r16);  // row 4q + r16 / 4 of the t block
       ocol = sum4q(ocol);
-      if (r16 == 0) *(f32x4*)(pb + PB_OROW + pair * 16 + 4 * q) = f32x4{orow[0], orow[1], orow[2], orow[3]};
+      if ((r16 & 3) == 0) pb[PB_OROW + pair * 16 + 4 * q + (r16 >> 2)] = osum;
       if (q == 0) pb[PB_OCOL + pair * 16 + r16] = ocol;
     }
 
@@ -343,19 +371,21 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         }
       }
       if (blue) {
+        float bsum[RB];  // sum_n C dC_blue = fcol * sum_n C acc, this lane's 4 n
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           float cv[4];
           frag_get(ld_colk(Cs, LDN, 16 * rb, 16 * nt_own, lane), cv);  // C[r][n .. n+3], n = 16 nt + 4q
-          float bsum = 0.0f;  // sum_n C dC_blue = fcol * sum_n C acc
+          float s = 0.0f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
-            bsum = fmaf(cv[j], acc[rb][j], bsum);
+            s = fmaf(cv[j], acc[rb][j], s);
           }
-          bsum = sum4q(bsum) * fcol[rb];
-          if (q == 0) pb[PB_BLUE + nt_own * 64 + 16 * rb + r16] = bsum;
+          bsum[rb] = s * fcol[rb];
         }
+        // row q of lanes: the sum over the n tile for row block q
+        pb[PB_BLUE + nt_own * 64 + 16 * q + r16] = sum4q_x4(bsum);
       } else {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
