@@ -90,7 +90,13 @@ ssmvjp_status ssm_scan_bwd_workspace(const ssmvjp_scan_desc* desc, size_t* bytes
  *   dx [b,T,H,P] (dtype)   d_dt [b,T,H] f32   dB, dC [b,T,G,N] (dtype)
  *   d_s0 [b,H,P,N] f32
  * Constraints: b, T >= 0 (an empty batch or sequence enqueues nothing except
- * d_s0 = ds_final for T = 0); H % G == 0; P*N <= 32768; N <= 1024.
+ * d_s0 = ds_final for T = 0); H % G == 0 (SSMVJP_EINVAL otherwise).  One
+ * workgroup per (batch, head) holds the head's state in LDS, so with
+ * Q = ceil(P / min(P, 16)) groups of p values
+ *     N <= 1024,  P*N <= 32768,  Q*N <= 1024  and
+ *     4 * (P*(N+1) + 2*Q*N + ceil(Q*N / 64)) <= 65536 bytes of LDS
+ * (SSMVJP_EUNSUPPORTED otherwise; e.g. P = N = 128 needs 74,304 bytes and is
+ * refused, P = 64, N = 128 fits).
  * Pointers must be 4-byte aligned (f32) or 2-byte aligned (bf16). */
 ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc,
                            const void* x, const float* dt, const float* A,
@@ -146,7 +152,10 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
  *   - a multiple of 64 above 64 with L <= 64 and M dividing 64 (row-blocked
  *     kernels, e.g. the rank-4 MIMO form with L = 64): 64 rows of B, C, x and
  *     dy plus one state must fit 160 KiB of LDS (any P, N <= 128 with bf16;
- *     P*N <= 8192 more or less with float32). */
+ *     P*N <= 8192 more or less with float32).
+ * Alignment (SSMVJP_EINVAL otherwise): x_or_v, B, C, dy, dx_or_dv, dB and dC
+ * 16-byte aligned (the kernels move them in 16-byte vectors); the float32
+ * tensors 4-byte aligned; the workspace 256-byte aligned. */
 ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
                             const void* x_or_v, const float* dt_or_da, const float* A,
                             const void* B, const void* C, const float* s0,
@@ -160,7 +169,8 @@ ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc,
  * combined_backward's d_da).  Each chunk's per-head sum is formed in the
  * chunk kernel, and the sums over (batch, chunk) run in a fixed order.  The
  * other arguments and outputs are exactly those of ssd_chunk_bwd (same
- * workspace size); dA must not be NULL when batch > 0. */
+ * workspace size, same shape limits and 16-byte alignment of the big
+ * tensors); dA must not be NULL when batch > 0. */
 ssmvjp_status ssd_chunk_bwd_dA(const ssmvjp_ssd_desc* desc,
                                const void* x, const float* dt, const float* A,
                                const void* B, const void* C, const float* s0,
@@ -179,7 +189,8 @@ ssmvjp_status ssd_chunk_bwd_dA(const ssmvjp_ssd_desc* desc,
  *  - ssd_chunk_bwd_grads: the per-chunk BLUE / ORANGE / K3 / K2 / K1 backwards
  *    and the Mamba-2 chain, reading the states the previous call left in the
  *    workspace.  The workspace must not be modified in between.
- * Arguments mean what they mean for ssd_chunk_bwd. */
+ * Arguments mean what they mean for ssd_chunk_bwd, with the same shape limits
+ * and the same alignment (the big tensors 16-byte aligned, the workspace 256). */
 ssmvjp_status ssd_chunk_bwd_states(const ssmvjp_ssd_desc* desc,
                                    const void* x_or_v, const float* dt_or_da, const float* A,
                                    const void* B, const void* C, const float* s0,

@@ -113,18 +113,34 @@ def _dtype_code(t):
 
 
 def _need(t, name, dtype, shape, device):
+    """Check an optional tensor argument (None passes): shape, dtype and layout.
+    The device is checked by _on_gpu once every shape has been checked."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
-    if t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(device, *tensors):
+    """Every tensor handed to the library lives on the same GPU (there is no CPU path)."""
+    if not device.type == "cuda":
+        raise ValueError("inputs must be GPU tensors (there is no CPU path)")
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"a tensor is on {t.device}, expected {device} (there is no CPU path)")
+
+
+def _check_out(out, spec, device):
+    """Every tensor of a caller-supplied ``out`` dict must match what the call writes:
+    the kernels see only pointers, so a wrong size would be written out of bounds."""
+    for name, (dtype, shape) in spec.items():
+        if name not in out or out[name] is None:
+            raise ValueError(f"out is missing '{name}'")
+        _need(out[name], f"out['{name}']", dtype, shape, device)
 
 
 def _workspace(nbytes, device, workspace):
@@ -133,6 +149,8 @@ def _workspace(nbytes, device, workspace):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
+        if not workspace.is_contiguous() or not workspace.is_cuda or workspace.device != device:
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
         return workspace, workspace.numel() * workspace.element_size()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
@@ -165,6 +183,8 @@ def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, want_dA=Fals
     dt [b,T,H], A [H] (Mamba-2) or [H,N] (Mamba-1), s0, ds_final [b,H,P,N] float32
     (s0 / ds_final may be None = zeros).
     """
+    if x is None or B is None or A is None or x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b,T,H,P], B [b,T,G,N] and A [H] or [H,N]")
     desc = scan_desc(x, A, B, ckpt_every)
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -173,20 +193,29 @@ def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, want_dA=Fals
     _need(dy, "dy", big, (b, T, H, P), dev)
     _need(B, "B", big, (b, T, G, N), dev)
     _need(C, "C", big, (b, T, G, N), dev)
+    for name, t in (("dt", dt), ("C", C), ("dy", dy)):
+        if t is None:
+            raise ValueError(f"{name} is required")
     _need(dt, "dt", torch.float32, (b, T, H), dev)
-    _need(A, "A", torch.float32, tuple(A.shape), dev)
+    if A.dim() not in (1, 2):
+        raise ValueError("A must be [H] (per-head decay) or [H,N] (per-state decay)")
+    _need(A, "A", torch.float32, (H,) if A.dim() == 1 else (H, N), dev)
     _need(s0, "s0", torch.float32, (b, H, P, N), dev)
     _need(ds_final, "ds_final", torch.float32, (b, H, P, N), dev)
+    spec = dict(dx=(big, (b, T, H, P)), d_dt=(torch.float32, (b, T, H)), dB=(big, (b, T, G, N)),
+                dC=(big, (b, T, G, N)), d_s0=(torch.float32, (b, H, P, N)))
     if out is None:
         out = dict(dx=torch.empty_like(x), d_dt=torch.empty_like(dt), dB=torch.empty_like(B),
                    dC=torch.empty_like(C), d_s0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
+    _check_out(out, spec, dev)
+    _on_gpu(dev, x, dt, A, B, C, s0, dy, ds_final, *out.values())
     ws, wsb = _workspace(ssm_scan_bwd_workspace(desc), dev, workspace)
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy), _ptr(ds_final), _ptr(out["dx"]),
             _ptr(out["d_dt"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["d_s0"]))
     if want_dA:
         if "dA" not in out:
             out["dA"] = torch.empty_like(A)
-        _need(out["dA"], "dA", torch.float32, tuple(A.shape), dev)
+        _need(out["dA"], "out['dA']", torch.float32, tuple(A.shape), dev)
         st = lib().ssm_scan_bwd_dA(ctypes.byref(desc), *args, _ptr(out["dA"]), _ptr(ws), wsb, _stream(stream))
         _check("ssm_scan_bwd_dA", st)
     else:
@@ -207,6 +236,42 @@ def ssd_desc(xv, B, chunk_len, form):
     return SsdDesc(b, T, H, P, N, G, M, int(chunk_len), form, _dtype_code(xv))
 
 
+def _ssd_inputs(xv, dtda, A, B, C, s0, form, chunk_len):
+    """Descriptor of a chunked call after checking every input against the shapes
+    x/v fixes: B, C [b,T,G,N] (RAW: [b,T,M,G,N]), dt/da [b,T,H], A [H], states
+    [b,H,P,N]."""
+    if xv is None or B is None:
+        raise ValueError("x/v and B are required")
+    if xv.dim() != (4 if form == FORM_MAMBA2 else 5):
+        raise ValueError(f"x/v must be {'[b,T,H,P]' if form == FORM_MAMBA2 else '[b,T,M,H,P]'}")
+    if B.dim() != xv.dim():
+        raise ValueError(f"B must be {'[b,T,G,N]' if form == FORM_MAMBA2 else '[b,T,M,G,N]'}")
+    desc = ssd_desc(xv, B, chunk_len, form)
+    b, T, H, P, N, G, M = desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate, desc.ngroups, desc.mimo_rank
+    dev, big = xv.device, xv.dtype
+    bc = (b, T, G, N) if form == FORM_MAMBA2 else (b, T, M, G, N)
+    _need(xv, "x/v", big, tuple(xv.shape), dev)
+    _need(B, "B", big, bc, dev)
+    _need(C, "C", big, bc, dev)
+    _need(dtda, "dt/da", torch.float32, (b, T, H), dev)
+    if form == FORM_MAMBA2:
+        _need(A, "A", torch.float32, (H,), dev)
+    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
+    if C is None or dtda is None or (form == FORM_MAMBA2 and A is None):
+        raise ValueError("C, dt/da (and A in the Mamba-2 form) are required")
+    return desc
+
+
+def _ssd_grad_spec(desc, xv, form):
+    b, T, H, P, N, G, M = (desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate, desc.ngroups,
+                           desc.mimo_rank)
+    big = xv.dtype
+    bc = (b, T, G, N) if form == FORM_MAMBA2 else (b, T, M, G, N)
+    names = ("dx", "d_dt") if form == FORM_MAMBA2 else ("dv", "d_da")
+    return {names[0]: (big, tuple(xv.shape)), names[1]: (torch.float32, (b, T, H)), "dB": (big, bc),
+            "dC": (big, bc), "d_s0": (torch.float32, (b, H, P, N))}
+
+
 def ssd_chunk_bwd_workspace(desc):
     n = ctypes.c_size_t(0)
     _check("ssd_chunk_bwd_workspace", lib().ssd_chunk_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
@@ -224,22 +289,19 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, want_dA=Fal
     returns dict dv, d_da, dB, dC, d_s0.
     """
     form = FORM_MAMBA2 if A is not None else FORM_RAW
-    desc = ssd_desc(xv, B, chunk_len, form)
+    desc = _ssd_inputs(xv, dtda, A, B, C, s0, form, chunk_len)
     b, T, H, P, N = desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate
     dev, big = xv.device, xv.dtype
-    _need(xv, "x/v", big, tuple(xv.shape), dev)
+    if dy is None:
+        raise ValueError("dy is required")
     _need(dy, "dy", big, tuple(xv.shape), dev)
-    _need(B, "B", big, tuple(B.shape), dev)
-    _need(C, "C", big, tuple(B.shape), dev)
-    _need(dtda, "dt/da", torch.float32, (b, T, H), dev)
-    if A is not None:
-        _need(A, "A", torch.float32, (H,), dev)
-    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
     _need(ds_final, "ds_final", torch.float32, (b, H, P, N), dev)
     names = ("dx", "d_dt") if form == FORM_MAMBA2 else ("dv", "d_da")
     if out is None:
         out = {names[0]: torch.empty_like(xv), names[1]: torch.empty_like(dtda), "dB": torch.empty_like(B),
                "dC": torch.empty_like(C), "d_s0": torch.empty((b, H, P, N), dtype=torch.float32, device=dev)}
+    _check_out(out, _ssd_grad_spec(desc, xv, form), dev)
+    _on_gpu(dev, xv, dtda, A, B, C, s0, dy, ds_final, *out.values())
     ws, wsb = _workspace(ssd_chunk_bwd_workspace(desc), dev, workspace)
     args = (_ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0), _ptr(dy), _ptr(ds_final),
             _ptr(out[names[0]]), _ptr(out[names[1]]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["d_s0"]))
@@ -248,7 +310,7 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, want_dA=Fal
             raise ValueError("dA needs the Mamba-2 (x, dt, A) form")
         if "dA" not in out:
             out["dA"] = torch.empty_like(A)
-        _need(out["dA"], "dA", torch.float32, (H,), dev)
+        _need(out["dA"], "out['dA']", torch.float32, (H,), dev)
         st = lib().ssd_chunk_bwd_dA(ctypes.byref(desc), *args, _ptr(out["dA"]), _ptr(ws), wsb, _stream(stream))
         _check("ssd_chunk_bwd_dA", st)
     else:
@@ -272,21 +334,17 @@ def ssd_chunk_fwd(xv, dtda, A, B, C, s0=None, *, chunk_len=64, out=None, want_fi
     s0 None = zeros; want_final=False leaves s_final out (None).
     """
     form = FORM_MAMBA2 if A is not None else FORM_RAW
-    desc = ssd_desc(xv, B, chunk_len, form)
+    desc = _ssd_inputs(xv, dtda, A, B, C, s0, form, chunk_len)
     b, T, H, P, N = desc.batch, desc.seqlen, desc.nheads, desc.headdim, desc.dstate
     dev, big = xv.device, xv.dtype
-    _need(xv, "x/v", big, tuple(xv.shape), dev)
-    _need(B, "B", big, tuple(B.shape), dev)
-    _need(C, "C", big, tuple(B.shape), dev)
-    _need(dtda, "dt/da", torch.float32, (b, T, H), dev)
-    if A is not None:
-        _need(A, "A", torch.float32, (H,), dev)
-    _need(s0, "s0", torch.float32, (b, H, P, N), dev)
     if out is None:
         out = {"y": torch.empty_like(xv),
                "s_final": torch.empty((b, H, P, N), dtype=torch.float32, device=dev) if want_final else None}
-    _need(out["y"], "y", big, tuple(xv.shape), dev)
-    _need(out["s_final"], "s_final", torch.float32, (b, H, P, N), dev)
+    if out.get("y") is None:
+        raise ValueError("out is missing 'y'")
+    _need(out["y"], "out['y']", big, tuple(xv.shape), dev)
+    _need(out.get("s_final"), "out['s_final']", torch.float32, (b, H, P, N), dev)
+    _on_gpu(dev, xv, dtda, A, B, C, s0, out["y"], out.get("s_final"))
     ws, wsb = _workspace(ssd_chunk_fwd_workspace(desc), dev, workspace)
     st = lib().ssd_chunk_fwd(ctypes.byref(desc), _ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0),
                              _ptr(out["y"]), _ptr(out["s_final"]), _ptr(ws), wsb, _stream(stream))
@@ -303,14 +361,20 @@ class SsdCall:
 
     def __init__(self, xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out=None, stream=None):
         self.form = FORM_MAMBA2 if A is not None else FORM_RAW
-        self.desc = ssd_desc(xv, B, chunk_len, self.form)
+        self.desc = _ssd_inputs(xv, dtda, A, B, C, s0, self.form, chunk_len)
         d = self.desc
         dev = xv.device
+        if dy is None:
+            raise ValueError("dy is required")
+        _need(dy, "dy", xv.dtype, tuple(xv.shape), dev)
+        _need(ds_final, "ds_final", torch.float32, (d.batch, d.nheads, d.headdim, d.dstate), dev)
         names = ("dx", "d_dt") if self.form == FORM_MAMBA2 else ("dv", "d_da")
         if out is None:
             out = {names[0]: torch.empty_like(xv), names[1]: torch.empty_like(dtda), "dB": torch.empty_like(B),
                    "dC": torch.empty_like(C),
                    "d_s0": torch.empty((d.batch, d.nheads, d.headdim, d.dstate), dtype=torch.float32, device=dev)}
+        _check_out(out, _ssd_grad_spec(d, xv, self.form), dev)
+        _on_gpu(dev, xv, dtda, A, B, C, s0, dy, ds_final, *out.values())
         self.out = out
         self.ws, self.wsb = _workspace(ssd_chunk_bwd_workspace(d), dev, None)
         self.stream = stream
@@ -351,6 +415,8 @@ def delta_rule_bwd_workspace(desc):
 
 
 def _delta_args(q, k, v, beta, g, S0, d_o, dS_final, want_dS0, out):
+    if q is None or v is None or q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [b,T,H,K] and v [b,T,HV,V]")
     desc = delta_desc(q, v, 1.0)
     b, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
@@ -363,10 +429,17 @@ def _delta_args(q, k, v, beta, g, S0, d_o, dS_final, want_dS0, out):
     _need(S0, "S0", f32, (b, HV, K, V), dev)
     _need(d_o, "d_o", f32, (b, T, HV, V), dev)
     _need(dS_final, "dS_final", f32, (b, HV, K, V), dev)
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g), ("d_o", d_o)):
+        if t is None:
+            raise ValueError(f"{name} is required")
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
                    dbeta=torch.empty_like(beta),
                    dS0=torch.empty((b, HV, K, V), dtype=f32, device=dev) if want_dS0 else None)
+    _check_out(out, dict(dq=(f32, (b, T, H, K)), dk=(f32, (b, T, H, K)), dv=(f32, (b, T, HV, V)),
+                         dg=(f32, (b, T, HV, K)), dbeta=(f32, (b, T, HV))), dev)
+    _need(out.get("dS0"), "out['dS0']", f32, (b, HV, K, V), dev)
+    _on_gpu(dev, q, k, v, beta, g, S0, d_o, dS_final, *out.values())
     p = _ptr
     args = (p(q), p(k), p(v), p(beta), p(g), p(S0), p(d_o), p(dS_final), p(out["dq"]), p(out["dk"]), p(out["dv"]),
             p(out["dg"]), p(out["dbeta"]), p(out.get("dS0")))

@@ -238,3 +238,25 @@ def test_dA_entry_points_validate_before_launching():
     assert L.ssm_scan_bwd_dA(ctypes.byref(s), *fake, mis, ws, 1 << 34, None) == bd.EINVAL
     # an empty batch has nothing to write
     assert L.ssm_scan_bwd_dA(ctypes.byref(_scan(batch=0)), *([None] * 14), None, 0, None) == bd.OK
+
+
+def test_scan_lds_limit_is_the_stated_one():
+    """P = N = 128 keeps P*N within 32768 but its state needs 74,304 bytes of
+    LDS (over the 64 KiB the header states); P = 64, N = 128 fits."""
+    assert _ws("ssm_scan_bwd_workspace", _scan(headdim=128, dstate=128))[0] == bd.EUNSUPPORTED
+    assert _ws("ssm_scan_bwd_workspace", _scan(headdim=64, dstate=256))[0] == bd.EUNSUPPORTED
+    assert _ws("ssm_scan_bwd_workspace", _scan(headdim=64, dstate=128))[0] == bd.OK
+
+
+def _lds_bytes(P, N):
+    Q = -(-P // min(P, 16))
+    return 4 * (P * (N + 1) + 2 * Q * N + -(-(Q * N) // 64))
+
+
+@pytest.mark.parametrize("P,N", [(1, 16), (4, 8), (16, 256), (33, 64), (64, 128), (96, 96), (128, 128), (20, 500),
+                                 (2, 1024), (64, 256), (128, 64)])
+def test_scan_header_formula_matches_the_library(P, N):
+    Q = -(-P // min(P, 16))
+    ok = N <= 1024 and P * N <= 32768 and Q * N <= 1024 and _lds_bytes(P, N) <= 65536
+    st = _ws("ssm_scan_bwd_workspace", _scan(headdim=P, dstate=N))[0]
+    assert st == (bd.OK if ok else bd.EUNSUPPORTED), (P, N, st)

@@ -4,6 +4,9 @@
   several value slices, GVA groups of 1, 2 and 4, sequences that end inside a
   checkpoint segment, non-zero initial state and final-state gradient;
 * T = 1 and T = 0 (dS0 is then the final-state gradient);
+* S0 = NULL and dS_final = NULL (zeros);
+* the full workload: qk heads 0, 7 and 15 of both batch elements, every
+  output (dq, dk, dv, dg, dbeta, dS0) against the oracle;
 * the full workload (b=2, T=4096, H=16, HV=32, K=V=128) in the launch
   configuration the benchmark times: batch element 0, qk head 0 (value heads
   0..1) against the oracle on that slice of the inputs, and the whole
@@ -30,8 +33,10 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to("cuda:0").contiguous()
 
 
-def _gpu(inp, dSf=None):
+def _gpu(inp, dSf=None, null_S0=False):
     t = {k: _dev(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
+    if null_S0:
+        t["S0"] = None
     out = bd.delta_rule_bwd(t["q"], t["k"], t["v"], t["beta"], t["g"], t["S0"], t["do"],
                             None if dSf is None else _dev(dSf), scale=inp["scale"])
     torch.cuda.synchronize()
@@ -117,6 +122,48 @@ def test_delta_rule_full_workload_slice_and_identity():
     sub = {"dq": got["dq"][:1, :, :nh], "dk": got["dk"][:1, :, :nh], "dv": got["dv"][:1, :, :nv],
            "dg": got["dg"][:1, :, :nv], "dbeta": got["dbeta"][:1, :, :nv], "dS0": got["dS0"][:1, :nv]}
     _compare(sub, ref)
+
+
+@pytest.mark.parametrize("null_S0,null_dSf", [(True, False), (False, True), (True, True)])
+def test_delta_rule_null_state_and_seed(null_S0, null_dSf):
+    """S0 = NULL and dS_final = NULL mean zeros (the header's contract)."""
+    announce(f"delta_rule NULL S0={null_S0} dS_final={null_dSf}")
+    inp = synth.kda_inputs(2, 45, 2, 4, 128, 64, seed=17, nonzero_state=True)
+    dSf = np.random.default_rng(19).standard_normal((2, 4, 128, 64))
+    c = _f32(inp)
+    if null_S0:
+        c["S0"] = np.zeros_like(c["S0"])
+    got = _gpu(inp, None if null_dSf else dSf, null_S0=null_S0)
+    _compare(got, _oracle(c, None if null_dSf else dSf.astype(np.float32).astype(np.float64)))
+
+
+def test_delta_rule_full_workload_heads_of_every_batch_element():
+    """The full workload: qk heads 0, 7 and 15 (each with its value heads) of
+    both batch elements against the oracle, every output including dk, dg and
+    dbeta, which no identity covers."""
+    w = synth.WORKLOADS["kda"]
+    announce("delta_rule full workload b=2 T=4096 H=16 HV=32 K=V=128, qk heads 0, 7, 15 of each batch element")
+    inp = synth.workload_inputs("kda")
+    got = _gpu(inp)
+    c = _f32(inp)
+    grp = w["HV"] // w["H"]
+    picks = [(bi, h) for bi in range(w["b"]) for h in (0, 7, w["H"] - 1)]
+    # the picked (batch element, qk head) slices stacked along the batch axis
+    def qk(a):
+        return np.stack([a[bi, :, h] for bi, h in picks])[:, :, None]
+
+    def vh(a):
+        return np.stack([a[bi, :, grp * h:grp * (h + 1)] for bi, h in picks])
+
+    sl = {"q": qk(c["q"]), "k": qk(c["k"]), "v": vh(c["v"]), "beta": vh(c["beta"]), "g": vh(c["g"]),
+          "do": vh(c["do"]), "S0": np.stack([c["S0"][bi, grp * h:grp * (h + 1)] for bi, h in picks]),
+          "scale": c["scale"]}
+    ref = _oracle(sl)
+    sub = {"dq": qk(got["dq"]), "dk": qk(got["dk"]), "dv": vh(got["dv"]), "dg": vh(got["dg"]),
+           "dbeta": vh(got["dbeta"]), "dS0": np.stack([got["dS0"][bi, grp * h:grp * (h + 1)] for bi, h in picks])}
+    for i, (bi, h) in enumerate(picks):
+        announce(f"  batch element {bi}, qk head {h}")
+        _compare({k: v[i:i + 1] for k, v in sub.items()}, {k: v[i:i + 1] for k, v in ref.items()})
 
 
 def test_delta_rule_deterministic():

@@ -2,9 +2,10 @@
 float64 oracle, through the C ABI.
 
 Covers both workloads of this path (Mamba-2 small, Mamba-1 per-state), random
-shapes with several groups and ragged checkpoint segments, bf16 storage, an
-empty sequence, bitwise equality across checkpoint intervals (the llama.cpp
-page's checkpoint-every-K requirement) and run-to-run determinism.
+shapes with several groups and ragged checkpoint segments, bf16 storage,
+s0 = NULL and ds_final = NULL (zeros), an empty sequence, bitwise equality
+across checkpoint intervals (the llama.cpp page's checkpoint-every-K
+requirement) and run-to-run determinism.
 """
 import numpy as np
 import pytest
@@ -20,8 +21,11 @@ pytestmark = pytest.mark.gpu
 OUTS = ("dx", "d_dt", "dB", "dC", "d_s0")
 
 
-def _gpu(inp, dtype, ckpt=0):
+def _gpu(inp, dtype, ckpt=0, null=()):
+    """The sequential backward on the GPU; tensors named in `null` are passed as NULL."""
     t = to_device(inp, dtype, BIG_MAMBA)
+    for k in null:
+        t[k] = None
     out = bd.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["s0"], t["dy"], t["ds_final"],
                           ckpt_every=ckpt)
     torch.cuda.synchronize()
@@ -106,3 +110,16 @@ def test_deterministic_across_runs():
     b = _gpu(inp, "f32")
     for k in OUTS:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("per_state", [False, True])
+@pytest.mark.parametrize("null", [("s0",), ("ds_final",), ("s0", "ds_final")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_null_initial_state_and_seed(per_state, null, dtype):
+    """s0 = NULL and ds_final = NULL mean zeros (the header's contract)."""
+    announce(f"scan_seq NULL {null} per_state={per_state} {dtype}")
+    inp = synth.mamba_inputs(2, 75, 4, 8, 16, 2, per_state, seed=41 + len(null))
+    zeroed = dict(inp)
+    for k in null:
+        zeroed[k] = np.zeros_like(inp[k])
+    _compare(_gpu(inp, dtype, 16, null=null), _oracle(zeroed, dtype), TOL[dtype])

@@ -6,9 +6,10 @@ row-blocked chunk kernels), through the C ABI.
   over heads), a shorter last chunk, the generic and the compile-time shapes;
 * the full rank-4 MIMO workload (b=2, T=4096, M=4, H=32, P=64, N=128, G=32,
   L=64, bf16) in the launch configuration of the library's default plan,
-  batch element 0 against the oracle and the whole batch through the identity
-  <dB, B> = <dv, v> of the exact VJP (y and the final state are bilinear in
-  (v, B) apart from the s0 term, which depends on neither);
+  every batch element against the oracle and the whole batch through the
+  identity <dB, B> = <dv, v> of the exact VJP (y and the final state are
+  bilinear in (v, B) apart from the s0 term, which depends on neither);
+* s0 = NULL and ds_final = NULL (zeros), in both dtypes;
 * edge cases: T = 1, a single short chunk, T = 0, determinism.
 """
 import numpy as np
@@ -25,8 +26,11 @@ pytestmark = pytest.mark.gpu
 RAW_OUTS = ("dv", "d_da", "dB", "dC", "d_s0")
 
 
-def _gpu_raw(inp, dtype, L):
+def _gpu_raw(inp, dtype, L, null=()):
+    """The chunked backward on the GPU; tensors named in `null` are passed as NULL."""
     t = to_device(inp, dtype, BIG_RAW)
+    for k in null:
+        t[k] = None
     out = bd.ssd_chunk_bwd(t["v"], t["da"], None, t["B"], t["C"], t["s0"], t["dy"], t["ds_final"], chunk_len=L)
     torch.cuda.synchronize()
     return {k: to_numpy(v) for k, v in out.items()}
@@ -86,7 +90,10 @@ def test_blocked_raw_parity(shape, dtype):
     _compare(_gpu_raw(inp, dtype, L), _oracle_raw(inp, dtype), RAW_OUTS, TOL[dtype])
 
 
-def test_blocked_full_mimo_workload_batch0_and_identity():
+def test_blocked_full_mimo_workload_every_batch_element():
+    """The full rank-4 MIMO workload in the library's default plan: every
+    output element of each batch element against the oracle (per batch
+    element), and the identity <dB, B> = <dv, v> over the whole batch."""
     w = synth.WORKLOADS["mimo_chunk"]
     announce("ssd blocked bf16 full MIMO workload b=2 T=4096 M=4 H=32 P=64 N=128 G=32 L=64")
     inp = synth.workload_inputs("mimo_chunk")
@@ -96,10 +103,25 @@ def test_blocked_full_mimo_workload_batch0_and_identity():
     rhs = float(np.sum(got["dv"] * c["v"]))
     print("[identity] <dB,B> =", lhs, " <dv,v> =", rhs, flush=True)
     assert abs(lhs - rhs) <= 2e-2 * max(abs(rhs), 1e-30) + 1e-3, (lhs, rhs)
-    c0 = {k: (v[:1] if isinstance(v, np.ndarray) and v.ndim >= 3 else v) for k, v in c.items()}
-    ref = oracle.raw_seq_bwd(c0["v"], c0["da"], c0["B"], c0["C"], c0["s0"], c0["dy"], c0["ds_final"])
-    got0 = {k: v[:1] for k, v in got.items()}
-    _compare(got0, ref, RAW_OUTS, TOL["bf16"])
+    ref = oracle.raw_seq_bwd(c["v"], c["da"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"])
+    for bi in range(w["b"]):
+        announce(f"  batch element {bi}")
+        _compare({k: v[bi:bi + 1] for k, v in got.items()}, {k: v[bi:bi + 1] for k, v in ref.items()}, RAW_OUTS,
+                 TOL["bf16"])
+
+
+@pytest.mark.parametrize("shape", [(1, 130, 4, 2, 64, 128, 1, 64), (1, 128, 4, 2, 32, 32, 2, 32)])
+@pytest.mark.parametrize("null", [("s0",), ("ds_final",), ("s0", "ds_final")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_blocked_null_initial_state_and_seed(shape, null, dtype):
+    """s0 = NULL and ds_final = NULL mean zeros on the row-blocked path too."""
+    b, T, M, H, P, N, G, L = shape
+    announce(f"ssd blocked raw {dtype} {shape} NULL {null}")
+    inp = synth.raw_inputs(b, T, M, H, P, N, G, seed=13 + sum(shape) + len(null))
+    zeroed = dict(inp)
+    for k in null:
+        zeroed[k] = np.zeros_like(inp[k])
+    _compare(_gpu_raw(inp, dtype, L, null=null), _oracle_raw(zeroed, dtype), RAW_OUTS, TOL[dtype])
 
 
 @pytest.mark.parametrize("T", [1, 10, 64])

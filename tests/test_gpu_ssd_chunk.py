@@ -6,8 +6,9 @@
 * the GPU chunked path against the GPU sequential path in fp32 (1e-5), small
   and at the full Mamba-2 chunked workload shape;
 * the full bf16 workload (b=4, T=4096, H=32, P=64, N=128) in the launch
-  configuration the benchmark times, checked on batch element 0 against the
-  oracle and on the whole batch through the identity <dB, B> = <dx, x>;
+  configuration the benchmark times, every batch element against the oracle,
+  and the whole batch through the identity <dB, B> = <dx, x>;
+* s0 = NULL and ds_final = NULL (zeros), in both dtypes and both kernels;
 * edge cases: one short chunk, T = 1, T = 0, determinism.
 """
 import numpy as np
@@ -25,8 +26,11 @@ M2_OUTS = ("dx", "d_dt", "dB", "dC", "d_s0")
 RAW_OUTS = ("dv", "d_da", "dB", "dC", "d_s0")
 
 
-def _gpu_m2(inp, dtype, L):
+def _gpu_m2(inp, dtype, L, null=()):
+    """The chunked backward on the GPU; tensors named in `null` are passed as NULL."""
     t = to_device(inp, dtype, BIG_MAMBA)
+    for k in null:
+        t[k] = None
     out = bd.ssd_chunk_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["s0"], t["dy"], t["ds_final"], chunk_len=L)
     torch.cuda.synchronize()
     return {k: to_numpy(v) for k, v in out.items()}
@@ -148,21 +152,45 @@ def test_chunked_matches_gpu_sequential_fp32_full_workload_shape():
     _compare(_gpu_m2(inp, "f32", w["L"]), _gpu_seq(inp, "f32"), M2_OUTS, 1e-5)
 
 
-def test_full_bf16_workload_batch0_and_identity():
+def test_full_bf16_workload_every_batch_element():
+    """The full workload in the launch configuration the benchmark times,
+    every output element of every batch element against the oracle (each
+    batch element separately, so that an error confined to one of them cannot
+    hide behind the others' larger values), plus the identity <dB, B> = <dx, x>
+    of the exact VJP over the whole batch."""
     w = synth.WORKLOADS["mamba2_chunk"]
     announce("ssd bf16 full workload b=4 T=4096 H=32 P=64 N=128 L=64")
     inp = synth.workload_inputs("mamba2_chunk")
     got = _gpu_m2(inp, "bf16", w["L"])
     c = synth.as_dtype(inp, "bf16", "mamba")
-    # identity of the exact VJP, whole batch: <dB, B> = <dx, x>
     lhs = float(np.sum(got["dB"] * c["B"]))
     rhs = float(np.sum(got["dx"] * c["x"]))
     assert abs(lhs - rhs) <= 2e-2 * max(abs(rhs), 1e-30) + 1e-3, (lhs, rhs)
-    # batch element 0 against the oracle
-    c0 = {k: (v[:1] if isinstance(v, np.ndarray) and v.ndim >= 3 else v) for k, v in c.items()}
-    ref = oracle.mamba_seq_bwd(c0["x"], c0["dt"], c0["A"], c0["B"], c0["C"], c0["s0"], c0["dy"], c0["ds_final"])
-    got0 = {k: v[:1] for k, v in got.items()}
-    _compare(got0, ref, M2_OUTS, TOL["bf16"])
+    ref = oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"])
+    for bi in range(w["b"]):
+        announce(f"  batch element {bi}")
+        _compare({k: v[bi:bi + 1] for k, v in got.items()}, {k: v[bi:bi + 1] for k, v in ref.items()}, M2_OUTS,
+                 TOL["bf16"])
+
+
+NULL_SHAPES = [(1, 150, 3, 64, 128, 1, 64),  # the 16-wave kernel's shape (bf16)
+               (2, 130, 4, 32, 32, 2, 32)]   # the general per-chunk kernel
+
+
+@pytest.mark.parametrize("shape", NULL_SHAPES)
+@pytest.mark.parametrize("null", [("s0",), ("ds_final",), ("s0", "ds_final")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_null_initial_state_and_seed(shape, null, dtype):
+    """s0 = NULL and ds_final = NULL mean zeros (the header's contract): the
+    zero-seed case is the ordinary training case, where the final state feeds
+    nothing downstream."""
+    b, T, H, P, N, G, L = shape
+    announce(f"ssd mamba2 {dtype} {shape} NULL {null}")
+    inp = synth.mamba_inputs(b, T, H, P, N, G, False, seed=sum(shape) + len(null))
+    zeroed = dict(inp)
+    for k in null:
+        zeroed[k] = np.zeros_like(inp[k])
+    _compare(_gpu_m2(inp, dtype, L, null=null), _oracle_m2(zeroed, dtype), M2_OUTS, TOL[dtype])
 
 
 @pytest.mark.parametrize("T,L", [(10, 64), (1, 16), (64, 64)])
