@@ -202,6 +202,28 @@ ssmvjp_status ssd_chunk_bwd_grads(const ssmvjp_ssd_desc* desc,
                                   void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssd_chunk_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a device array of
+ * SSMVJP_NOALLOC_SCRATCH_BYTES (96 MiB) that the library owns: each device
+ * holds its own copy from the first call on that device until the process
+ * ends.  The call allocates nothing (no hipMalloc, no hipFree); the caller
+ * still passes every input and output.  Arguments, layouts, limits, alignment
+ * and results are exactly those of ssd_chunk_bwd; a shape whose
+ * ssd_chunk_bwd_workspace size exceeds SSMVJP_NOALLOC_SCRATCH_BYTES returns
+ * SSMVJP_EWORKSPACE before anything is enqueued (the Mamba-2 head shape
+ * H = 32, P = 64, N = 128 in bf16 fits up to b*T = 4096 tokens, e.g. one
+ * sequence of 4096).  Every call on one device shares that device's array:
+ * calls whose work overlaps on one device (other streams, other host threads)
+ * race and must be serialised by the caller. */
+#define SSMVJP_NOALLOC_SCRATCH_BYTES (96u << 20)
+ssmvjp_status ssd_chunk_bwd_noalloc(const ssmvjp_ssd_desc* desc,
+                                    const void* x_or_v, const float* dt_or_da, const float* A,
+                                    const void* B, const void* C, const float* s0,
+                                    const void* dy, const float* ds_final,
+                                    void* dx_or_dv, float* d_dt_or_dda, void* dB, void* dC, float* d_s0,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* ssd_chunk_fwd: chunked SSD forward (the step before the backward)         */
 /* ------------------------------------------------------------------------ */

@@ -21,7 +21,7 @@ FORM_MAMBA2, FORM_RAW = 0, 1
 DELTA_CKPT, DELTA_BWD, DELTA_REDUCE, DELTA_ALL = 1, 2, 4, 7
 
 _STATUS_FNS = ("ssm_scan_bwd_workspace", "ssm_scan_bwd", "ssm_scan_bwd_dA", "ssd_chunk_bwd_workspace",
-               "ssd_chunk_bwd", "ssd_chunk_bwd_dA", "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads",
+               "ssd_chunk_bwd", "ssd_chunk_bwd_dA", "ssd_chunk_bwd_states", "ssd_chunk_bwd_grads", "ssd_chunk_bwd_noalloc",
                "ssd_chunk_fwd_workspace", "ssd_chunk_fwd", "delta_rule_bwd_workspace", "delta_rule_bwd",
                "delta_rule_bwd_stages")
 EXPORTS = _STATUS_FNS + ("ssmvjp_status_str", "ssmvjp_version")
@@ -72,6 +72,7 @@ def lib():
         L.ssd_chunk_bwd_dA.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 15 + [sz, vp]
         L.ssd_chunk_bwd_states.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 10 + [sz, vp]
         L.ssd_chunk_bwd_grads.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 11 + [sz, vp]
+        L.ssd_chunk_bwd_noalloc.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 14
         L.ssd_chunk_fwd_workspace.argtypes = [ctypes.POINTER(SsdDesc), ctypes.POINTER(sz)]
         L.ssd_chunk_fwd.argtypes = [ctypes.POINTER(SsdDesc)] + [vp] * 9 + [sz, vp]
         L.delta_rule_bwd_workspace.argtypes = [ctypes.POINTER(DeltaDesc), ctypes.POINTER(sz)]
@@ -316,6 +317,33 @@ def ssd_chunk_bwd(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, want_dA=Fal
     else:
         st = lib().ssd_chunk_bwd(ctypes.byref(desc), *args, _ptr(ws), wsb, _stream(stream))
         _check("ssd_chunk_bwd", st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20  # SSMVJP_NOALLOC_SCRATCH_BYTES
+
+
+def ssd_chunk_bwd_noalloc(xv, dtda, A, B, C, s0, dy, ds_final, *, chunk_len, out, stream=None):
+    """ssd_chunk_bwd on the library's own device array instead of a workspace.
+
+    ``out`` (required: this call allocates nothing) holds the output tensors,
+    as returned by ssd_chunk_bwd.  Shapes whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise (SSMVJP_EWORKSPACE).
+    """
+    form = FORM_MAMBA2 if A is not None else FORM_RAW
+    desc = _ssd_inputs(xv, dtda, A, B, C, s0, form, chunk_len)
+    if dy is None or out is None:
+        raise ValueError("dy and out are required")
+    dev = xv.device
+    _need(dy, "dy", xv.dtype, tuple(xv.shape), dev)
+    _need(ds_final, "ds_final", torch.float32, (desc.batch, desc.nheads, desc.headdim, desc.dstate), dev)
+    _check_out(out, _ssd_grad_spec(desc, xv, form), dev)
+    _on_gpu(dev, xv, dtda, A, B, C, s0, dy, ds_final, *out.values())
+    names = ("dx", "d_dt") if form == FORM_MAMBA2 else ("dv", "d_da")
+    st = lib().ssd_chunk_bwd_noalloc(ctypes.byref(desc), _ptr(xv), _ptr(dtda), _ptr(A), _ptr(B), _ptr(C), _ptr(s0),
+                                     _ptr(dy), _ptr(ds_final), _ptr(out[names[0]]), _ptr(out[names[1]]),
+                                     _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["d_s0"]), _stream(stream))
+    _check("ssd_chunk_bwd_noalloc", st)
     return out
 
 
