@@ -27,8 +27,10 @@ Functions and the passages they follow:
   K1 backwards and the combine.
 * ``ssd_mamba2_bwd`` -- the chunked backward with the Mamba-2 input chain
   (x, dt, A) -> (v = x*softplus(dt), da = softplus(dt)*A).
-* ``kda_fwd`` / ``kda_bwd`` -- the KDA gated delta rule: forward F1..F6 and the
-  BPTT steps 1..6 with the GVA view+sum (K3 notes, "反向传播推导").
+* ``kda_fwd`` / ``kda_bwd`` -- the KDA gated delta rule: forward F1..F6 (K3
+  notes, "反向传播推导") and its reverse-time adjoint, derived from F1..F6 by
+  writing each step as a linear map of the previous state, with the gradients
+  of q and k summed over the value heads of each qk head.
 
 Parity pins for every function are in ``tests/test_oracle_*.py`` (finite
 differences of the float64 forward, closed forms, a hand-derived worked example,

@@ -18,7 +18,9 @@
  *       K1..K4 recompute, the reverse per-chunk loop (BLUE, ORANGE, K4 step) and
  *       the batched K3/K2/K1 backwards.
  *  [P2] K3 notes, section "反向传播推导" (backward derivation of the KDA gated
- *       delta rule): forward F1..F6, steps 1..6 and the GVA view+sum.
+ *       delta rule): the forward F1..F6, the warning box on the two paths into
+ *       the gated state's gradient, and the grouping of value heads under qk
+ *       heads.  The backward here is derived from F1..F6 (see orc_kda_bwd).
  *  [P3] llama.cpp PR "S1-31: SSM_SCAN_BACK -- Mamba has a backward": the reverse
  *       recurrence with the non-zero final-state seed, store-all states, the
  *       Mamba-2 (per-head decay) and Mamba-1 (per-state decay) branches, and the
@@ -68,7 +70,7 @@ enum {
   MUT_STRICT_MASK = 16,      /* triu(0) mask: drop the diagonal of the causal mask */
   MUT_NO_M_REDUCE = 17,      /* forget the mimo_rank reduction of d_cumA (keep m=0) */
   /* KDA (P2) */
-  MUT_DROP_KDR = 21,         /* drop -k (x) dr from dS_dec_total */
+  MUT_DROP_KDR = 21,         /* drop the residual path -beta k u^T from the gated state's gradient */
   MUT_WRONG_GVA = 22         /* map value head hv to qk head hv % H instead of hv / G */
 };
 
@@ -792,136 +794,157 @@ int orc_kda_fwd(i64 b, i64 T, i64 H, i64 HV, i64 K, i64 V, double scale,
   return 0;
 }
 
-/* BPTT over t = T-1 .. 0 (P2 steps 1..5), store-all states, then the GVA
- * reduction of dq and dk (step 6). dS_final NULL = zeros; dS0 NULL = skip. */
+/* Backward of the KDA gated delta rule, derived here from the forward
+ * equations F1..F6 of the notes ([P2]) by writing one step as a linear map of
+ * the previous state.  Per value head, with Q = scale * q_t and the gated state
+ * X = diag(exp(g_t)) S_{t-1}:
+ *     S_t = X + beta_t k_t (v_t - X^T k_t)^T
+ *         = (I - beta_t k_t k_t^T) X + beta_t k_t v_t^T,        o_t = S_t^T Q.
+ * J = <d_o, o> + <dS_final, S_{T-1}> is differentiated in reverse time.  Let
+ * Sbar be dJ/dS_t from the later steps and the seed.  The readout adds its own
+ * part and gives q's gradient:
+ *     Sbar' = Sbar + Q d_o_t^T,     qbar_t = scale * S_t d_o_t.
+ * With the residual r = v_t - X^T k_t and one vector u = Sbar'^T k_t (a value
+ * per state column), the write contributes
+ *     vbar_t = beta_t u,    betabar_t = u . r,
+ *     kbar_t = beta_t (Sbar' r - X u),
+ *     Xbar   = Sbar' - beta_t k_t u^T
+ * (the second term of Xbar is the path through the residual that the notes'
+ * warning box insists on), and the gate
+ *     gbar_t[i] = sum_j Xbar[i,j] X[i,j],      Sbar_{t-1} = diag(exp(g_t)) Xbar.
+ * After step 0, Sbar is dJ/dS0.  q and k are shared by the HV/H value heads of
+ * a qk head (the notes' view of the value heads as groups of a qk head), so
+ * their gradients are the sums of the per-value-head ones, added in ascending
+ * value-head order.  States of every step are kept (store-all).
+ * dS_final NULL = zeros; dS0 NULL = not written. */
 int orc_kda_bwd(i64 b, i64 T, i64 H, i64 HV, i64 K, i64 V, double scale,
                 const double* q, const double* k, const double* v, const double* beta,
                 const double* g, const double* S0, const double* d_o, const double* dS_final,
                 double* dq, double* dk, double* dv, double* dg, double* dbeta, double* dS0,
                 int mutation, int nthreads) {
   if (b < 0 || T < 0 || H <= 0 || HV <= 0 || HV % H || K <= 0 || V <= 0) return 1;
-  const i64 grp = HV / H;
-  double* dq_e = (double*)calloc((size_t)(b * T * HV * K) + 1, sizeof(double));
-  double* dk_e = (double*)calloc((size_t)(b * T * HV * K) + 1, sizeof(double));
-  if (!dq_e || !dk_e) { free(dq_e); free(dk_e); return 2; }
+  /* per-value-head gradients of q and k, summed over each group afterwards */
+  double* qbar = (double*)calloc((size_t)(b * T * HV * K) + 1, sizeof(double));
+  double* kbar = (double*)calloc((size_t)(b * T * HV * K) + 1, sizeof(double));
+  if (!qbar || !kbar) { free(qbar); free(kbar); return 2; }
   set_threads(nthreads);
   int fail = 0;
 #pragma omp parallel for schedule(dynamic)
   for (i64 task = 0; task < b * HV; ++task) {
     const i64 bi = task / HV, hv = task % HV, h = kda_qk_head(hv, H, HV, mutation);
     const i64 KV = K * V;
-    double* S = (double*)malloc(sizeof(double) * (size_t)((T + 1) * KV)); /* S[t+1] = S_t */
-    double* Sdec = (double*)malloc(sizeof(double) * (size_t)KV);
-    double* St = (double*)malloc(sizeof(double) * (size_t)KV);
-    double* dSacc = (double*)malloc(sizeof(double) * (size_t)KV);
-    double* r = (double*)malloc(sizeof(double) * (size_t)V);
-    double* dr = (double*)malloc(sizeof(double) * (size_t)V);
-    double* a = (double*)malloc(sizeof(double) * (size_t)K);
-    double* da_ = (double*)malloc(sizeof(double) * (size_t)K);
-    if (!S || !Sdec || !St || !dSacc || !r || !dr || !a || !da_) { fail = 1; goto kdone; }
-    /* forward, store all states */
-    for (i64 e = 0; e < KV; ++e) S[e] = S0 ? S0[IX4(bi, hv, 0, 0, HV, K, V) + e] : 0.0;
+    double* hist = (double*)malloc(sizeof(double) * (size_t)((T + 1) * KV)); /* hist[t] = S_{t-1} */
+    double* Sbar = (double*)malloc(sizeof(double) * (size_t)KV);
+    double* X = (double*)malloc(sizeof(double) * (size_t)KV);
+    double* resid = (double*)malloc(sizeof(double) * (size_t)V);
+    double* u = (double*)malloc(sizeof(double) * (size_t)V);
+    double* gate = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!hist || !Sbar || !X || !resid || !u || !gate) { fail = 1; goto next_task; }
+
+    /* forward pass keeping every state */
+    for (i64 e = 0; e < KV; ++e) hist[e] = S0 ? S0[IX4(bi, hv, 0, 0, HV, K, V) + e] : 0.0;
     for (i64 t = 0; t < T; ++t) {
       const double* kt = k + IX4(bi, t, h, 0, T, H, K);
       const double* vt = v + IX4(bi, t, hv, 0, T, HV, V);
       const double* gt = g + IX4(bi, t, hv, 0, T, HV, K);
       const double bt = beta[(bi * T + t) * HV + hv];
-      const double* Sp = S + t * KV;
-      double* Sn = S + (t + 1) * KV;
-      for (i64 kk = 0; kk < K; ++kk)
-        for (i64 vv = 0; vv < V; ++vv) Sn[kk * V + vv] = exp(gt[kk]) * Sp[kk * V + vv];
-      for (i64 vv = 0; vv < V; ++vv) {
-        double p = 0.0;
-        for (i64 kk = 0; kk < K; ++kk) p += kt[kk] * Sn[kk * V + vv];
-        r[vv] = vt[vv] - p;
+      const double* prev = hist + t * KV;
+      double* cur = hist + (t + 1) * KV;
+      for (i64 i = 0; i < K; ++i) {
+        const double e = exp(gt[i]);
+        for (i64 j = 0; j < V; ++j) cur[i * V + j] = e * prev[i * V + j];
       }
-      for (i64 kk = 0; kk < K; ++kk)
-        for (i64 vv = 0; vv < V; ++vv) Sn[kk * V + vv] += bt * kt[kk] * r[vv];
+      for (i64 j = 0; j < V; ++j) {
+        double kx = 0.0;
+        for (i64 i = 0; i < K; ++i) kx += kt[i] * cur[i * V + j];
+        resid[j] = vt[j] - kx;
+      }
+      for (i64 i = 0; i < K; ++i)
+        for (i64 j = 0; j < V; ++j) cur[i * V + j] += bt * kt[i] * resid[j];
     }
-    /* backward */
-    for (i64 e = 0; e < KV; ++e) dSacc[e] = dS_final ? dS_final[IX4(bi, hv, 0, 0, HV, K, V) + e] : 0.0;
+
+    /* reverse pass */
+    for (i64 e = 0; e < KV; ++e) Sbar[e] = dS_final ? dS_final[IX4(bi, hv, 0, 0, HV, K, V) + e] : 0.0;
     for (i64 t = T - 1; t >= 0; --t) {
       const double* qt = q + IX4(bi, t, h, 0, T, H, K);
       const double* kt = k + IX4(bi, t, h, 0, T, H, K);
       const double* vt = v + IX4(bi, t, hv, 0, T, HV, V);
       const double* gt = g + IX4(bi, t, hv, 0, T, HV, K);
-      const double* dot = d_o + IX4(bi, t, hv, 0, T, HV, V);
+      const double* obar = d_o + IX4(bi, t, hv, 0, T, HV, V);
       const double bt = beta[(bi * T + t) * HV + hv];
-      const double* Sp = S + t * KV;
-      /* recompute S_dec, r, a and S_t */
-      for (i64 kk = 0; kk < K; ++kk)
-        for (i64 vv = 0; vv < V; ++vv) Sdec[kk * V + vv] = exp(gt[kk]) * Sp[kk * V + vv];
-      for (i64 vv = 0; vv < V; ++vv) {
-        double p = 0.0;
-        for (i64 kk = 0; kk < K; ++kk) p += kt[kk] * Sdec[kk * V + vv];
-        r[vv] = vt[vv] - p;
+      const double* Sprev = hist + t * KV;       /* S_{t-1} */
+      const double* St = hist + (t + 1) * KV;    /* S_t */
+      double* qb = qbar + IX4(bi, t, hv, 0, T, HV, K);
+      double* kb = kbar + IX4(bi, t, hv, 0, T, HV, K);
+
+      /* readout o_t = S_t^T Q */
+      for (i64 i = 0; i < K; ++i) {
+        double so = 0.0;
+        for (i64 j = 0; j < V; ++j) so += St[i * V + j] * obar[j];
+        qb[i] = scale * so;
+        for (i64 j = 0; j < V; ++j) Sbar[i * V + j] += scale * qt[i] * obar[j];
       }
-      for (i64 kk = 0; kk < K; ++kk) a[kk] = bt * kt[kk];
-      for (i64 kk = 0; kk < K; ++kk)
-        for (i64 vv = 0; vv < V; ++vv) St[kk * V + vv] = Sdec[kk * V + vv] + a[kk] * r[vv];
-      /* step 1: o = (scale q)^T S_t */
-      for (i64 kk = 0; kk < K; ++kk)
-        for (i64 vv = 0; vv < V; ++vv) dSacc[kk * V + vv] += scale * qt[kk] * dot[vv];
-      for (i64 kk = 0; kk < K; ++kk) {
-        double acc = 0.0;
-        for (i64 vv = 0; vv < V; ++vv) acc += dot[vv] * St[kk * V + vv];
-        dq_e[IX4(bi, t, hv, kk, T, HV, K)] = acc;
+      /* the gated state and the residual of this step, recomputed from S_{t-1} */
+      for (i64 i = 0; i < K; ++i) {
+        gate[i] = exp(gt[i]);
+        for (i64 j = 0; j < V; ++j) X[i * V + j] = gate[i] * Sprev[i * V + j];
       }
-      /* step 2: S_t = S_dec + a (x) r */
-      for (i64 kk = 0; kk < K; ++kk) {
-        double acc = 0.0;
-        for (i64 vv = 0; vv < V; ++vv) acc += r[vv] * dSacc[kk * V + vv];
-        da_[kk] = acc;
+      for (i64 j = 0; j < V; ++j) {
+        double kx = 0.0, ks = 0.0;
+        for (i64 i = 0; i < K; ++i) {
+          kx += kt[i] * X[i * V + j];
+          ks += kt[i] * Sbar[i * V + j];
+        }
+        resid[j] = vt[j] - kx;
+        u[j] = ks;
       }
-      for (i64 vv = 0; vv < V; ++vv) {
-        double acc = 0.0;
-        for (i64 kk = 0; kk < K; ++kk) acc += a[kk] * dSacc[kk * V + vv];
-        dr[vv] = acc;
+      /* the write S_t = X + beta k (v - X^T k)^T */
+      double bb = 0.0;
+      for (i64 j = 0; j < V; ++j) {
+        dv[IX4(bi, t, hv, j, T, HV, V)] = bt * u[j];
+        bb += u[j] * resid[j];
       }
-      /* step 3: a = beta k */
-      double db = 0.0;
-      for (i64 kk = 0; kk < K; ++kk) db += kt[kk] * da_[kk];
-      dbeta[(bi * T + t) * HV + hv] = db;
-      /* step 4: r = v - k^T S_dec ; dk = beta da - S_dec dr */
-      for (i64 vv = 0; vv < V; ++vv) dv[IX4(bi, t, hv, vv, T, HV, V)] = dr[vv];
-      for (i64 kk = 0; kk < K; ++kk) {
-        double acc = 0.0;
-        for (i64 vv = 0; vv < V; ++vv) acc += Sdec[kk * V + vv] * dr[vv];
-        dk_e[IX4(bi, t, hv, kk, T, HV, K)] = bt * da_[kk] - acc;
+      dbeta[(bi * T + t) * HV + hv] = bb;
+      for (i64 i = 0; i < K; ++i) {
+        double sr = 0.0, xu = 0.0;
+        for (i64 j = 0; j < V; ++j) {
+          sr += Sbar[i * V + j] * resid[j];
+          xu += X[i * V + j] * u[j];
+        }
+        kb[i] = bt * (sr - xu);
       }
-      /* step 5: dS_dec_total = dS_acc - k (x) dr ; dg ; dS_{t-1} */
       if (mutation != MUT_DROP_KDR)
-        for (i64 kk = 0; kk < K; ++kk)
-          for (i64 vv = 0; vv < V; ++vv) dSacc[kk * V + vv] -= kt[kk] * dr[vv];
-      for (i64 kk = 0; kk < K; ++kk) {
-        double acc = 0.0;
-        for (i64 vv = 0; vv < V; ++vv) acc += Sdec[kk * V + vv] * dSacc[kk * V + vv];
-        dg[IX4(bi, t, hv, kk, T, HV, K)] = acc;
-        const double eg = exp(gt[kk]);
-        for (i64 vv = 0; vv < V; ++vv) dSacc[kk * V + vv] *= eg;
+        for (i64 i = 0; i < K; ++i)
+          for (i64 j = 0; j < V; ++j) Sbar[i * V + j] -= bt * kt[i] * u[j];
+      /* the gate X = diag(exp(g)) S_{t-1} */
+      for (i64 i = 0; i < K; ++i) {
+        double gx = 0.0;
+        for (i64 j = 0; j < V; ++j) gx += Sbar[i * V + j] * X[i * V + j];
+        dg[IX4(bi, t, hv, i, T, HV, K)] = gx;
+        for (i64 j = 0; j < V; ++j) Sbar[i * V + j] *= gate[i];
       }
     }
     if (dS0)
-      for (i64 e = 0; e < KV; ++e) dS0[IX4(bi, hv, 0, 0, HV, K, V) + e] = dSacc[e];
-  kdone:
-    free(S); free(Sdec); free(St); free(dSacc); free(r); free(dr); free(a); free(da_);
+      for (i64 e = 0; e < KV; ++e) dS0[IX4(bi, hv, 0, 0, HV, K, V) + e] = Sbar[e];
+  next_task:
+    free(hist); free(Sbar); free(X); free(resid); free(u); free(gate);
   }
-  /* step 6: GVA reduce H_V -> H (value head hv = h*G + j), ascending j */
+  /* q and k are read by every value head of their group: sum the per-value-head
+   * gradients, ascending value head */
   for (i64 bi = 0; bi < b; ++bi)
     for (i64 t = 0; t < T; ++t)
       for (i64 h = 0; h < H; ++h)
-        for (i64 kk = 0; kk < K; ++kk) {
+        for (i64 i = 0; i < K; ++i) {
           double sq = 0.0, sk = 0.0;
           for (i64 hv = 0; hv < HV; ++hv) {
             if (kda_qk_head(hv, H, HV, mutation) != h) continue;
-            sq += dq_e[IX4(bi, t, hv, kk, T, HV, K)];
-            sk += dk_e[IX4(bi, t, hv, kk, T, HV, K)];
+            sq += qbar[IX4(bi, t, hv, i, T, HV, K)];
+            sk += kbar[IX4(bi, t, hv, i, T, HV, K)];
           }
-          dq[IX4(bi, t, h, kk, T, H, K)] = sq * scale;
-          dk[IX4(bi, t, h, kk, T, H, K)] = sk;
+          dq[IX4(bi, t, h, i, T, H, K)] = sq;
+          dk[IX4(bi, t, h, i, T, H, K)] = sk;
         }
-  (void)grp;
-  free(dq_e);
-  free(dk_e);
+  free(qbar);
+  free(kbar);
   return fail ? 2 : 0;
 }

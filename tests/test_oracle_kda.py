@@ -8,8 +8,8 @@
     in (v, S0);
   * value columns are independent in the recurrence (a perturbation of one
     column of v changes no other column of o);
-  * dropping -k (x) dr from dS_dec_total (the notes' two-path warning) and a
-    wrong GVA head map each fail the FD gate by >= 100x.
+  * dropping the residual path from the gated state's gradient (the notes'
+    two-path warning) and a wrong GVA head map each fail the FD gate by >= 100x.
 """
 import numpy as np
 import pytest
