@@ -82,26 +82,88 @@ def traffic_from_profile(kernel_name):
         return None
 
 
+def machine_info():
+    """What the numbers were measured on."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = None
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "hip_runtime": torch.version.hip, "rocm": rocm,
+            "torch": torch.__version__}
+
+
+def rel_maxabs(got, ref):
+    """max |got - ref| / max |ref| over one tensor (the parity tests' measure)."""
+    import numpy as np
+
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
+def _first(c, n=1):
+    return {k: (v[:n] if hasattr(v, "ndim") and v.ndim >= 3 else v) for k, v in c.items()}
+
+
+def _oracle_ssm(c, w, nthreads):
+    """The float64 oracle's backward on the (already sliced) inputs c; returns (seconds, outputs)."""
+    import oracle
+
+    t0 = time.perf_counter()
+    if w["form"] == "raw":
+        ref = oracle.raw_seq_bwd(c["v"], c["da"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"], nthreads=nthreads)
+    else:
+        ref = oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"],
+                                   nthreads=nthreads)
+    return time.perf_counter() - t0, ref
+
+
+def _head_slice(c, w, nh):
+    """The first nh heads of batch element 0 (per-head B/C follow the heads when G = H)."""
+    out = _first(c)
+    hk = ("v", "dy") if w["form"] == "raw" else ("x", "dy")
+    for k in hk:
+        out[k] = out[k][..., :nh, :]
+    for k in ("dt", "da"):
+        if k in out:
+            out[k] = out[k][..., :nh]
+    if "A" in out and w["form"] != "raw":
+        out["A"] = out["A"][:nh]
+    for k in ("s0", "ds_final"):
+        out[k] = out[k][:, :nh]
+    if w["G"] == w["H"]:
+        for k in ("B", "C"):
+            out[k] = out[k][..., :nh, :]
+    return out
+
+
 def cpu_baseline(inp_bf16, w):
-    """The float64 oracle on one of the b sequences (all heads, all T steps)."""
+    """The float64 oracle on one of the b sequences (all heads, all T steps), on
+    every host core; also on one core over the first heads of that sequence.
+    Returns (record, oracle outputs for batch element 0)."""
     import oracle
 
     threads = oracle.default_threads()
-    c = {k: (v[:1] if hasattr(v, "ndim") and v.ndim >= 3 else v) for k, v in inp_bf16.items()}
-    t0 = time.perf_counter()
-    if w["form"] == "raw":
-        oracle.raw_seq_bwd(c["v"], c["da"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"], nthreads=threads)
-    else:
-        oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"],
-                             nthreads=threads)
-    sec = time.perf_counter() - t0
-    return {"value": w["T"] / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {w['b']} sequences (T={w['T']}, all {w['H']} heads), float64 store-all "
-                      f"sequential reverse recurrence, {sec:.2f} s"}
+    sec, ref = _oracle_ssm(_first(inp_bf16), w, threads)
+    nh = max(1, w["H"] // 8)
+    sec1, _ = _oracle_ssm(_head_slice(inp_bf16, w, nh), w, 1)
+    rec = {"value": w["T"] / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"1 of {w['b']} sequences (T={w['T']}, all {w['H']} heads), float64 store-all "
+                     f"sequential reverse recurrence, {sec:.2f} s",
+           "one_core": {"value": w["T"] * nh / w["H"] / sec1, "unit": "tokens/s", "cores": 1,
+                        "sample": f"heads 0..{nh - 1} of that sequence, {sec1:.2f} s, scaled by {nh}/{w['H']} "
+                                  f"of the heads"}}
+    return rec, ref
 
 
 def kda_cpu_baseline(c, w):
-    """The float64 oracle on batch element 0, qk head 0 and its value heads (all T steps)."""
+    """The float64 oracle on batch element 0, qk head 0 and its value heads (all T
+    steps), threaded over the value heads, and on one core over one value head.
+    Returns (record, oracle outputs of that slice)."""
     import oracle
 
     threads = oracle.default_threads()
@@ -109,14 +171,22 @@ def kda_cpu_baseline(c, w):
     sl = {k: c[k][:1, :, :1] for k in ("q", "k")}
     sl.update({k: c[k][:1, :, :grp] for k in ("v", "beta", "g", "do")})
     t0 = time.perf_counter()
-    oracle.kda_bwd(sl["q"], sl["k"], sl["v"], sl["beta"], sl["g"], c["S0"][:1, :grp], sl["do"], None,
-                   scale=c["scale"], nthreads=threads)
+    ref = oracle.kda_bwd(sl["q"], sl["k"], sl["v"], sl["beta"], sl["g"], c["S0"][:1, :grp], sl["do"], None,
+                         scale=c["scale"], nthreads=threads)
     sec = time.perf_counter() - t0
-    frac = grp / (w["b"] * w["HV"])  # share of the workload's (batch, value head) sequences
-    return {"value": w["b"] * w["T"] * frac / sec, "unit": "tokens/s", "cores": min(threads, grp), "kind": "oracle",
-            "sample": f"batch element 0, qk head 0 and its {grp} value heads (T={w['T']}), float64 store-all "
-                      f"reverse recurrence, {sec:.2f} s; scaled by the {grp}/{w['b'] * w['HV']} share of the "
-                      f"(batch, value head) sequences"}
+    t0 = time.perf_counter()
+    oracle.kda_bwd(sl["q"], sl["k"], sl["v"][:, :, :1], sl["beta"][:, :, :1], sl["g"][:, :, :1], c["S0"][:1, :1],
+                   sl["do"][:, :, :1], None, scale=c["scale"], nthreads=1)
+    sec1 = time.perf_counter() - t0
+    seqs = w["b"] * w["HV"]  # (batch, value head) sequences of the workload
+    rec = {"value": w["b"] * w["T"] * grp / seqs / sec, "unit": "tokens/s", "cores": min(threads, grp),
+           "kind": "oracle",
+           "sample": f"batch element 0, qk head 0 and its {grp} value heads (T={w['T']}), float64 store-all "
+                     f"reverse recurrence, {sec:.2f} s; scaled by the {grp}/{seqs} share of the "
+                     f"(batch, value head) sequences",
+           "one_core": {"value": w["b"] * w["T"] / seqs / sec1, "unit": "tokens/s", "cores": 1,
+                        "sample": f"value head 0 of that slice, {sec1:.2f} s, scaled by 1/{seqs}"}}
+    return rec, ref
 
 
 def kda_flops(w):
@@ -186,8 +256,17 @@ def bench_kda(args, dev):
         "phases": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                    for k, v in phases.items()},
     }
+    line["seed"] = w["seed"]
+    line["machine"] = machine_info()
+    line["timing"] = "back-to-back steps (nothing between the library calls); warm infinity cache"
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = kda_cpu_baseline(c, w)
+        line["cpu_baseline"], ref = kda_cpu_baseline(c, w)
+        grp = w["HV"] // w["H"]
+        o = call.out
+        got = {"dq": o["dq"][:1, :, :1], "dk": o["dk"][:1, :, :1], "dv": o["dv"][:1, :, :grp],
+               "dg": o["dg"][:1, :, :grp], "dbeta": o["dbeta"][:1, :, :grp]}
+        line["rel_maxabs"] = {k: float(f"{rel_maxabs(v.double().cpu().numpy(), ref[k]):.3e}") for k, v in got.items()}
+        line["rel_maxabs_sample"] = "batch element 0, qk head 0 and its value heads, against the float64 oracle"
     print(json.dumps(line), flush=True)
 
 
@@ -283,6 +362,9 @@ def bench_fwd(args, dev):
     line["cold_cache"] = {"flush_bytes": MALL_FLUSH_BYTES, "ms_per_step": round(cold_ms, 4),
                           "tokens_per_s": round(b * T / (cold_ms / 1e3), 1),
                           "note": "median per-step event time, infinity cache evicted before each step"}
+    line["seed"] = w["seed"]
+    line["machine"] = machine_info()
+    line["timing"] = "back-to-back steps (nothing between the library calls); warm infinity cache"
     if not args.no_cpu_baseline:
         import oracle
 
@@ -303,10 +385,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD, choices=("mamba2_chunk", "mimo_chunk", "kda", "mamba2_fwd"),
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=("mamba2_chunk", "mimo_chunk", "kda", "mamba2_fwd", "mamba2_seq_small", "mamba1_seq"),
                     help="mamba2_chunk (default, the headline line), mimo_chunk (rank-4 MIMO, RAW form), "
-                         "kda (gated delta rule, b=2 T=4096 H=16 HV=32 K=V=128, fp32) or mamba2_fwd (the "
-                         "chunked forward at the mamba2_chunk shape)")
+                         "kda (gated delta rule, b=2 T=4096 H=16 HV=32 K=V=128, fp32), mamba2_fwd (the "
+                         "chunked forward at the mamba2_chunk shape), or the sequential path's small fp32 "
+                         "workloads mamba2_seq_small (b=1 T=64 H=2 P=4 N=8) and mamba1_seq (b=2 T=256 D=64 N=16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -337,6 +421,8 @@ def main():
         return bench_kda(args, dev)
     if args.workload == "mamba2_fwd":
         return bench_fwd(args, dev)
+    if args.workload in ("mamba2_seq_small", "mamba1_seq"):
+        return bench_seq(args, dev)
     w = dict(synth.WORKLOADS[args.workload])
     w.setdefault("M", 1)
     inp = synth.workload_inputs(args.workload)
@@ -426,8 +512,67 @@ def main():
                           "tokens_per_s": round(tokens / (cold_ms / 1e3), 1),
                           "state_scans_ms": round(cold_scans, 4), "chunk_grads_ms": round(cold_grads, 4),
                           "note": "median per-step event times, infinity cache evicted before each step"}
+    line["seed"] = w["seed"]
+    line["machine"] = machine_info()
+    line["timing"] = ("ms_per_step: wall clock over back-to-back steps (nothing between the library calls), "
+                      "warm infinity cache; cold_cache: every step after a 512 MiB write")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, w)
+        line["cpu_baseline"], ref = cpu_baseline(c, w)
+        line["rel_maxabs"] = {k: float(f"{rel_maxabs(v[:1].double().cpu().numpy(), ref[k]):.3e}")
+                              for k, v in call.out.items()}
+        line["rel_maxabs_sample"] = "batch element 0, every output element, against the float64 oracle"
+    print(json.dumps(line), flush=True)
+
+
+def bench_seq(args, dev):
+    """The sequential backward (ssm_scan_bwd) on one of the small fp32 workloads:
+    tokens/s only; these are latency-bound correctness configurations, so no
+    roofline claim is made."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_vjp_amd import binding, synth
+
+    w = dict(synth.WORKLOADS[args.workload])
+    inp = synth.workload_inputs(args.workload)
+    c = synth.as_dtype(inp, "f32", "mamba")
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(torch.float32).to(dev).contiguous()
+         for k, v in c.items() if isinstance(v, np.ndarray)}
+    call = binding.ScanCall(t["x"], t["dt"], t["A"], t["B"], t["C"], t["s0"], t["dy"], t["ds_final"])
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        call.run()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    tokens = w["b"] * w["T"]
+    line = {
+        "metric": "sequential scan-backward tokens/s (B·T/s)", "value": round(tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w["b"], "seqlen": w["T"], "heads": w["H"], "headdim": w["P"],
+                   "dstate": w["N"], "ngroups": w["G"], "decay": "per_state" if w["per_state"] else "per_head"},
+        "roofline": None,
+        "roofline_note": "latency-bound correctness configuration (a few thousand tokens): no roofline claim",
+        "seed": w["seed"], "machine": machine_info(),
+        "timing": "back-to-back steps (nothing between the library calls)",
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        ref = oracle.mamba_seq_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["s0"], c["dy"], c["ds_final"],
+                                   nthreads=threads)
+        sec = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": tokens / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                "sample": f"the whole workload, float64 store-all reverse recurrence, {sec:.3f} s"}
+        line["rel_maxabs"] = {k: float(f"{rel_maxabs(v.double().cpu().numpy(), ref[k]):.3e}")
+                              for k, v in call.out.items()}
     print(json.dumps(line), flush=True)
 
 

@@ -41,6 +41,15 @@
  *    on every call (all reductions run in a fixed order, no float atomics).
  *  - "big" tensors (x or v, B, C, dy and their gradients) are float32 or
  *    bfloat16 as selected by `dtype`; everything else is float32.
+ *  - Debug finiteness mode: with the environment variable SSMVJP_CHECK_FINITE
+ *    set (to anything but "0") when a call is made, every entry point scans
+ *    the outputs it wrote for NaN and infinite values after its launches,
+ *    synchronises the stream and returns SSMVJP_ENONFINITE if it found one
+ *    (the outputs are still written).  While the mode is on, the *_workspace
+ *    queries report 256 more bytes, which hold the scan's flag (burn-mamba's
+ *    combined_backward checks its intermediates for NaNs in the same spirit;
+ *    here the intermediates stay inside the kernels, so the outputs are
+ *    checked).  Off by default: the normal calls neither scan nor synchronise.
  */
 #ifndef SSMVJP_H
 #define SSMVJP_H
@@ -57,7 +66,8 @@ typedef enum {
   SSMVJP_EINVAL = 1,        /* bad descriptor, NULL required pointer, misaligned pointer */
   SSMVJP_EUNSUPPORTED = 2,  /* valid arguments outside what the kernels implement */
   SSMVJP_EWORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace query */
-  SSMVJP_EHIP = 4           /* a HIP launch or runtime call failed */
+  SSMVJP_EHIP = 4,          /* a HIP launch or runtime call failed */
+  SSMVJP_ENONFINITE = 5     /* debug mode only: an output holds a NaN or an infinity */
 } ssmvjp_status;
 
 enum { SSMVJP_F32 = 0, SSMVJP_BF16 = 1 };                         /* dtype of the big tensors */

@@ -14,7 +14,7 @@ import torch
 
 LIB_PATH = Path(__file__).resolve().parent / "libssmvjp.so"
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ENONFINITE = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 DECAY_PER_HEAD, DECAY_PER_STATE = 0, 1
 FORM_MAMBA2, FORM_RAW = 0, 1
@@ -223,6 +223,25 @@ def ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, want_dA=Fals
         st = lib().ssm_scan_bwd(ctypes.byref(desc), *args, _ptr(ws), wsb, _stream(stream))
         _check("ssm_scan_bwd", st)
     return out
+
+
+class ScanCall:
+    """A prepared ssm_scan_bwd call on fixed device buffers (for repeated timing):
+    arguments are checked once, ``run()`` only enqueues the backward."""
+
+    def __init__(self, x, dt, A, B, C, s0, dy, ds_final, *, ckpt_every=0, stream=None):
+        self.out = ssm_scan_bwd(x, dt, A, B, C, s0, dy, ds_final, ckpt_every=ckpt_every, stream=stream)
+        self.desc = scan_desc(x, A, B, ckpt_every)
+        self.ws, self.wsb = _workspace(ssm_scan_bwd_workspace(self.desc), x.device, None)
+        self.stream = stream
+        p, o = _ptr, self.out
+        self._args = (p(x), p(dt), p(A), p(B), p(C), p(s0), p(dy), p(ds_final), p(o["dx"]), p(o["d_dt"]), p(o["dB"]),
+                      p(o["dC"]), p(o["d_s0"]))
+        self._keep = (x, dt, A, B, C, s0, dy, ds_final)
+
+    def run(self):
+        st = lib().ssm_scan_bwd(ctypes.byref(self.desc), *self._args, _ptr(self.ws), self.wsb, _stream(self.stream))
+        _check("ssm_scan_bwd", st)
 
 
 # --------------------------------------------------------------------------- #

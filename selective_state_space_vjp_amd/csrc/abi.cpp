@@ -3,6 +3,9 @@
 // before anything is enqueued; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "../../include/ssmvjp.h"
 #include "kernels.h"
 
@@ -55,19 +58,56 @@ ssmvjp_status delta_check(const ssmvjp_delta_desc* d) {
 
 ssmvjp_status hip_status(hipError_t e) { return e == hipSuccess ? SSMVJP_OK : SSMVJP_EHIP; }
 
+// ---- debug finiteness mode (SSMVJP_CHECK_FINITE set and not "0") ----
+// The flag lives in FLAG_BYTES at the end of the workspace, after the plan's
+// own bytes rounded up to 256; the workspace queries include it while the
+// mode is on.
+constexpr size_t FLAG_BYTES = 256;
+
+bool check_finite_on() {
+  const char* e = std::getenv("SSMVJP_CHECK_FINITE");
+  return e && e[0] && std::strcmp(e, "0") != 0;
+}
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t with_flag(size_t plan_bytes) { return check_finite_on() ? round256(plan_bytes) + FLAG_BYTES : plan_bytes; }
+
+struct OutSpan {
+  const void* p;
+  int64_t n;
+  bool bf16;
+};
+
+// After the launches: clear the flag, scan every output, read the flag back
+// (this synchronises the stream) and turn a raised flag into ENONFINITE.
+template <size_t K>
+ssmvjp_status finite_check(void* workspace, size_t plan_bytes, const OutSpan (&outs)[K], hipStream_t stream) {
+  unsigned* flag = (unsigned*)((char*)workspace + round256(plan_bytes));
+  launch_flag_clear(flag, stream);
+  for (const OutSpan& o : outs) launch_nonfinite_check(o.p, o.n, o.bf16, flag, stream);
+  unsigned host = 0;
+  if (hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess) return SSMVJP_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SSMVJP_EHIP;
+  return host ? SSMVJP_ENONFINITE : SSMVJP_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* ssmvjp_version(void) { return "0.1.0"; }
 
-const char* ssmvjp_status_str(ssmvjp_status s) {
+const char* ssmvjp_status_str(ssmvjp_status status) {
+  // callers (C, ctypes) may pass any int: read the bits as an int, since
+  // loading an out-of-range value through the C++ enum type is undefined
+  int s;
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case SSMVJP_OK: return "ok";
     case SSMVJP_EINVAL: return "invalid argument";
     case SSMVJP_EUNSUPPORTED: return "unsupported shape or option";
     case SSMVJP_EWORKSPACE: return "workspace missing or too small";
     case SSMVJP_EHIP: return "HIP runtime error";
+    case SSMVJP_ENONFINITE: return "non-finite value in an output (SSMVJP_CHECK_FINITE)";
   }
   return "unknown status";
 }
@@ -78,7 +118,7 @@ ssmvjp_status ssm_scan_bwd_workspace(const ssmvjp_scan_desc* desc, size_t* bytes
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = scan_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = seq_plan(*desc).bytes;
+  *bytes = with_flag(seq_plan(*desc).bytes);
   return SSMVJP_OK;
 }
 
@@ -101,11 +141,18 @@ static ssmvjp_status scan_run(const ssmvjp_scan_desc* desc, const void* x, const
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
   const SeqPlan plan = seq_plan(d);
-  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
-    return SSMVJP_EWORKSPACE;
+  const size_t need = with_flag(plan.bytes);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
   SeqPointers ptr{x, dt, A, B, C, s0, dy, ds_final, dx, d_dt, dB, dC, d_s0, workspace, dA};
-  return hip_status(launch_seq_bwd(d, plan, ptr, (hipStream_t)stream));
+  s = hip_status(launch_seq_bwd(d, plan, ptr, (hipStream_t)stream));
+  if (s != SSMVJP_OK || !check_finite_on()) return s;
+  const bool bf = d.dtype == SSMVJP_BF16;
+  const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nbc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const OutSpan outs[] = {{dx, nx, bf}, {d_dt, d.batch * d.seqlen * d.nheads, false}, {dB, nbc, bf}, {dC, nbc, bf},
+                          {d_s0, d.batch * d.nheads * d.headdim * d.dstate, false},
+                          {dA, dA ? d.nheads * (d.decay == SSMVJP_DECAY_PER_STATE ? d.dstate : 1) : 0, false}};
+  return finite_check(workspace, plan.bytes, outs, (hipStream_t)stream);
 }
 
 ssmvjp_status ssm_scan_bwd(const ssmvjp_scan_desc* desc, const void* x, const float* dt, const float* A,
@@ -131,7 +178,7 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = ssd_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = ssd_plan(*desc).bytes;
+  *bytes = with_flag(ssd_plan(*desc).bytes);
   return SSMVJP_OK;
 }
 
@@ -158,11 +205,21 @@ static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, co
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
   const SsdPlan plan = ssd_plan(d);
-  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
-    return SSMVJP_EWORKSPACE;
+  const size_t need = with_flag(plan.bytes);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
   SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace, dA};
-  return hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+  s = hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+  if (s != SSMVJP_OK || !check_finite_on()) return s;
+  const bool bf = d.dtype == SSMVJP_BF16;
+  const int64_t nx = d.batch * d.seqlen * d.mimo_rank * d.nheads * d.headdim;
+  const int64_t nbc = d.batch * d.seqlen * d.mimo_rank * d.ngroups * d.dstate;
+  const OutSpan outs[] = {{grads ? dx_or_dv : nullptr, nx, bf},
+                          {grads ? d_dt_or_dda : nullptr, d.batch * d.seqlen * d.nheads, false},
+                          {grads ? dB : nullptr, nbc, bf}, {grads ? dC : nullptr, nbc, bf},
+                          {states ? d_s0 : nullptr, d.batch * d.nheads * d.headdim * d.dstate, false},
+                          {grads ? dA : nullptr, dA ? d.nheads : 0, false}};
+  return finite_check(workspace, plan.bytes, outs, (hipStream_t)stream);
 }
 
 ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
@@ -221,7 +278,7 @@ ssmvjp_status ssd_chunk_fwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = ssd_fwd_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = ssd_fwd_workspace_bytes(*desc);
+  *bytes = with_flag(ssd_fwd_workspace_bytes(*desc));
   return SSMVJP_OK;
 }
 
@@ -240,11 +297,15 @@ ssmvjp_status ssd_chunk_fwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, con
   const void* pf[] = {dt_or_da, A, s0, s_final};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
-  const size_t need = ssd_fwd_workspace_bytes(d);
+  const size_t plan_bytes = ssd_fwd_workspace_bytes(d), need = with_flag(plan_bytes);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (d.batch == 0) return SSMVJP_OK;
   SsdFwdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, y, s_final, workspace};
-  return hip_status(launch_ssd_fwd(d, ptr, (hipStream_t)stream));
+  s = hip_status(launch_ssd_fwd(d, ptr, (hipStream_t)stream));
+  if (s != SSMVJP_OK || !check_finite_on()) return s;
+  const OutSpan outs[] = {{y, d.batch * d.seqlen * d.mimo_rank * d.nheads * d.headdim, d.dtype == SSMVJP_BF16},
+                          {s_final, d.batch * d.nheads * d.headdim * d.dstate, false}};
+  return finite_check(workspace, plan_bytes, outs, (hipStream_t)stream);
 }
 
 // ------------------------------- delta_rule_bwd -----------------------------
@@ -253,7 +314,7 @@ ssmvjp_status delta_rule_bwd_workspace(const ssmvjp_delta_desc* desc, size_t* by
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = delta_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = delta_plan(*desc).bytes;
+  *bytes = with_flag(delta_plan(*desc).bytes);
   return SSMVJP_OK;
 }
 
@@ -272,11 +333,21 @@ static ssmvjp_status delta_run(const ssmvjp_delta_desc* desc, int32_t stages, co
   for (const void* p : pf)
     if (p && !aligned(p, 16)) return SSMVJP_EINVAL;
   const DeltaPlan plan = delta_plan(d);
-  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
-    return SSMVJP_EWORKSPACE;
+  const size_t need = with_flag(plan.bytes);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (d.batch == 0) return SSMVJP_OK;
   DeltaPointers ptr{q, k, v, beta, g, S0, d_o, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace};
-  return hip_status(launch_delta_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+  s = hip_status(launch_delta_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+  if (s != SSMVJP_OK || !check_finite_on()) return s;
+  const bool bwd = stages & SSMVJP_DELTA_BWD, red = stages & SSMVJP_DELTA_REDUCE;
+  const int64_t bt = d.batch * d.seqlen;
+  const OutSpan outs[] = {{red ? dq : nullptr, bt * d.nqk_heads * d.dk, false},
+                          {red ? dk : nullptr, bt * d.nqk_heads * d.dk, false},
+                          {bwd ? dv : nullptr, bt * d.nv_heads * d.dv, false},
+                          {red ? dg : nullptr, bt * d.nv_heads * d.dk, false},
+                          {red ? dbeta : nullptr, bt * d.nv_heads, false},
+                          {bwd ? dS0 : nullptr, d.batch * d.nv_heads * d.dk * d.dv, false}};
+  return finite_check(workspace, plan.bytes, outs, (hipStream_t)stream);
 }
 
 ssmvjp_status delta_rule_bwd(const ssmvjp_delta_desc* desc, const float* q, const float* k, const float* v,

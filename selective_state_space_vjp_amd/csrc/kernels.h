@@ -117,4 +117,10 @@ DeltaPlan delta_plan(const ssmvjp_delta_desc& d);
 hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, const DeltaPointers& ptr,
                             hipStream_t stream, int stages);
 
+// ---------------------------- debug finiteness -----------------------------
+// flag = 0; then flag = 1 if any of the n elements at p (bf16 or float) is NaN
+// or infinite (finite.hip)
+void launch_flag_clear(unsigned* flag, hipStream_t stream);
+void launch_nonfinite_check(const void* p, int64_t n, bool is_bf16, unsigned* flag, hipStream_t stream);
+
 }  // namespace ssmvjp

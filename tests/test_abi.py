@@ -260,3 +260,34 @@ def test_scan_header_formula_matches_the_library(P, N):
     ok = N <= 1024 and P * N <= 32768 and Q * N <= 1024 and _lds_bytes(P, N) <= 65536
     st = _ws("ssm_scan_bwd_workspace", _scan(headdim=P, dstate=N))[0]
     assert st == (bd.OK if ok else bd.EUNSUPPORTED), (P, N, st)
+
+
+def test_nonfinite_status_and_debug_workspace(monkeypatch):
+    """The debug finiteness mode (SSMVJP_CHECK_FINITE) has its own status, and
+    while it is on every workspace query reports 256 more bytes (the scan's
+    flag), rounded after the plan's own bytes."""
+    assert bd.status_str(bd.ENONFINITE).startswith("non-finite")
+    queries = [("ssm_scan_bwd_workspace", _scan()),
+               ("ssd_chunk_bwd_workspace", bd.SsdDesc(1, 100, 2, 16, 16, 1, 1, 16, 0, 0)),
+               ("ssd_chunk_fwd_workspace", bd.SsdDesc(1, 100, 2, 16, 16, 1, 1, 16, 0, 1)),
+               ("delta_rule_bwd_workspace", bd.DeltaDesc(1, 20, 1, 2, 128, 32, 1.0, 0))]
+    monkeypatch.delenv("SSMVJP_CHECK_FINITE", raising=False)
+    off = [_ws(fn, d) for fn, d in queries]
+    monkeypatch.setenv("SSMVJP_CHECK_FINITE", "0")
+    assert [_ws(fn, d) for fn, d in queries] == off
+    monkeypatch.setenv("SSMVJP_CHECK_FINITE", "1")
+    for (fn, d), (st0, n0) in zip(queries, off):
+        st, n = _ws(fn, d)
+        assert st == st0 == bd.OK
+        assert n == (n0 + 255) // 256 * 256 + 256, (fn, n0, n)
+
+
+def test_debug_mode_still_validates_before_launching(monkeypatch):
+    """With the mode on, a workspace sized for the mode off is refused before
+    anything is enqueued."""
+    monkeypatch.delenv("SSMVJP_CHECK_FINITE", raising=False)
+    d = _scan()
+    n = _ws("ssm_scan_bwd_workspace", d)[1]
+    monkeypatch.setenv("SSMVJP_CHECK_FINITE", "1")
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(13)]
+    assert bd.lib().ssm_scan_bwd(ctypes.byref(d), *fake, ctypes.c_void_p(1 << 20), n, None) == bd.EWORKSPACE
