@@ -231,9 +231,10 @@ def bench_kda(args, dev):
     ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K for j in range(3)]
     tokens = w["b"] * w["T"]
     fl = kda_flops(w)
-    part_bytes = w["b"] * w["T"] * w["HV"] * (w["V"] // 32) * 4 * w["K"] * 4
-    red_bytes = part_bytes + 4 * (2 * w["b"] * w["T"] * w["H"] * w["K"] + w["b"] * w["T"] * w["HV"] * (w["K"] + 2)
-                                  + w["b"] * w["T"] * w["H"] * w["K"])
+    # per (token, value head, 32-column slice): dq_e, dk_e and dg partial rows and one dbeta partial
+    part_bytes = w["b"] * w["T"] * w["HV"] * (w["V"] // 32) * (3 * w["K"] + 1) * 4
+    # the reduction reads the partials, writes dq, dk ([b,T,H,K]), dg ([b,T,HV,K]) and dbeta
+    red_bytes = part_bytes + 4 * (2 * w["b"] * w["T"] * w["H"] * w["K"] + w["b"] * w["T"] * w["HV"] * (w["K"] + 1))
     phases = {
         "ckpt": {"kernel": "delta_fwd_ckpt_kernel", "ms": ms[0], "flops": fl["ckpt"],
                  "TFLOPs": fl["ckpt"] / (ms[0] * 1e9)},

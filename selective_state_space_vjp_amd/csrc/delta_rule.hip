@@ -1,5 +1,5 @@
 // delta_rule.hip -- backward of the KDA gated delta rule (K3 notes, section
-// "反向传播推导": forward F1..F6, BPTT steps 1..6 and the GVA view+sum).
+// "反向传播推导": forward F1..F6 and the grouping of value heads under qk heads).
 //
 // Per (batch b, value head hv) the forward keeps a [K x V] state S and, at
 // step t, with the key/query of qk head h = hv / (HV/H):
@@ -7,14 +7,16 @@
 //   r     = v_t - k_t^T S_dec        (F2, F3)
 //   S_t   = S_dec + (beta_t k_t) (x) r     (F4, F5)
 //   o_t   = (scale q_t)^T S_t        (F6)
-// The backward walks t = T-1 .. 0 carrying dS (seeded with dS_final):
-//   dS += (scale q_t) (x) do_t ;  dq_e = S_t do_t                       (step 1)
-//   da  = dS r ;  dr = dS^T (beta_t k_t)                                (step 2)
-//   dbeta = k_t . da                                                    (step 3)
-//   dv = dr ;  dk_e = beta_t da - S_dec dr                              (step 4)
-//   dS -= k_t (x) dr   (the second path into dS_dec, summed with the first)
-//   dg  = rowsum(S_dec (.) dS) ;  dS = exp(g_t) (.) dS                  (step 5)
-//   dq = scale * sum of dq_e, dk = sum of dk_e over the value heads of a qk head  (step 6)
+// The backward walks t = T-1 .. 0 carrying dS (seeded with dS_final).  With
+// one vector per state column, u = dS'^T k_t (dS' = dS after the readout's
+// part), every gradient of the step follows (the adjoint of the step written
+// as S_t = (I - beta k k^T) S_dec + beta k v^T):
+//   dS' = dS + (scale q_t) (x) do_t ;   dq_e = S_t do_t
+//   dv = dr = beta_t u ;   dbeta = u . r
+//   dk_e = beta_t (dS' r - S_dec u)
+//   dS_dec = dS' - k_t (x) dr   (the path through r, summed with the direct one)
+//   dg = rowsum(S_dec (.) dS_dec) ;   dS_{t-1} = exp(g_t) (.) dS_dec
+//   dq = scale * sum of dq_e, dk = sum of dk_e over the value heads of a qk head.
 //
 // MI355X organisation (three launches):
 //  * Columns of S are independent in the recurrence (r[v] and the update of
@@ -22,20 +24,24 @@
 //    kernel runs one workgroup (8 waves, two per SIMD) per (batch, value head,
 //    slice).  A thread owns a 4 x 2 block of its slice (rows 4kq..4kq+3,
 //    columns 2vq, 2vq+1); the 32 threads that share a column block sit in one
-//    half wave, so the per-column sums over k (k^T S_dec, dS^T a) are DPP row
+//    half wave, so the per-column sums over k (k^T S_dec, k^T dS') are DPP row
 //    sums plus one permlane16 swap, with no LDS traffic and no barrier.
 //  * delta_fwd_ckpt_kernel walks the sequence forward and stores the state
-//    at the start of every NS-step sub-segment (the checkpoints).
+//    at the start of every NS-step sub-segment (the checkpoints) and the
+//    residual r of every step.
 //  * delta_bwd_kernel walks the sub-segments in reverse: it recomputes the
-//    NS states of a sub-segment from its checkpoint into registers, then runs
-//    the NS backward steps.  dv is a per-column output and is stored
-//    directly.  The per-row outputs (dq_e, da, S_dec dr, dg: sums over v)
-//    never feed back into the recurrence; each thread folds its 2 columns,
-//    half waves are paired with one permlane32 swap, and the 8 waves are
-//    summed through LDS once per sub-segment into the slice's partial sums.
+//    NS states of a sub-segment from its checkpoint and the stored residuals
+//    into registers (elementwise: no column sums), then runs the NS backward
+//    steps.  dv is a per-column output and is stored directly.  The per-row
+//    outputs (dq_e, dk_e, dg: sums over v) never feed back into the
+//    recurrence; each thread folds its 2 columns, half waves are paired with
+//    one permlane32 swap, and the 8 waves are summed through LDS once per
+//    sub-segment into the slice's partial sums (rows stored in the order the
+//    lanes hold them, so that the LDS reads and the stores are contiguous),
+//    together with the slice's part of dbeta = sum over the columns of u r.
 //  * delta_reduce_kernel adds the slice partials in slice order, applies the
-//    GVA sum over the value heads of each qk head (ascending), and forms dq,
-//    dk, dg and dbeta.
+//    sum over the value heads of each qk head (ascending), and forms dq, dk,
+//    dg and dbeta.
 // The next sub-segment's inputs and checkpoint are loaded into registers while
 // the current one runs.  Everything is float32; every sum runs in a fixed
 // order, so results are bitwise reproducible.  No float atomics.
@@ -52,15 +58,19 @@ constexpr int VT = 2;            // state columns per thread
 constexpr int NE = 4 * VT;       // state elements per thread (4 rows x VT columns)
 constexpr int VS = NW * 2 * VT;  // columns of the state per workgroup (16 column blocks of 2)
 constexpr int NS = 8;            // steps per sub-segment = checkpoint interval
-constexpr int NQ = 4;            // per-row outputs: dq_e, da, S_dec dr, dg
+constexpr int NQ = 3;            // per-row outputs: dq_e, dk_e, dg
+constexpr int NO = 4 * NQ;       // per-row outputs of one thread (4 rows each)
 
 struct DeltaArgs {
   i64 b, T, H, HV, V, nvs, nck, grp;
   float scale;
   const float *q, *k, *v, *beta, *g, *S0, *d_o, *dSf;
   float *dq, *dk, *dv, *dg, *dbeta, *dS0;
-  float* ck;    // [b][HV][nvs][nck][NE/4][NTH] float4: state at the start of each sub-segment
-  float* part;  // [b][T][HV][nvs][NQ][DK] per-slice partial sums of the per-row outputs
+  float* ck;     // [b][HV][nvs][nck][NE/4][NTH] float4: state at the start of each sub-segment
+  float* rres;   // [b][HV][nvs][nck*NS][VS] residual r of every step, per slice
+  float* part;   // [b][T][HV][nvs][NQ][4][32] per-slice partial sums of the per-row outputs;
+                 // row k = 4 kq + i at [i][kq]
+  float* partb;  // [b][T][HV][nvs] per-slice partial sums of dbeta
 };
 
 // sum over the 32 lanes of a half wave; every lane of the half wave gets the
@@ -181,6 +191,7 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
     pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
   };
   float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (NE * NTH);
+  float* rb = a.rres + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * NS * VS;
   if (a.nck > 0) issue(0);
   for (i64 j = 0; j < a.nck; ++j) {
     const int ns = (int)(T - j * NS < NS ? T - j * NS : NS);
@@ -204,6 +215,8 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
       float sd[NE], r[VT], vv[VT];
       ld_cols(&sv[s][VT * vq], vv);
       fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], vv, r);
+      // the residual of this step for the backward's recompute (one lane per column block)
+      if (kq == 0) *(float2*)(rb + (j * NS + s) * VS + VT * vq) = make_float2(r[0], r[1]);
     }
   }
 }
@@ -215,11 +228,11 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
   __shared__ __align__(16) float sq[NS][DK];  // scale * q
   __shared__ __align__(16) float sk[NS][DK];
   __shared__ __align__(16) float se[NS][DK];  // exp(g)
-  __shared__ __align__(16) float sv[NS][VS];
   __shared__ __align__(16) float sdo[NS][VS];
   __shared__ __align__(16) float sr[NS][VS];  // r of each step, per column
   __shared__ float sb[NS];
-  __shared__ __align__(16) float red[NS][NW][16][32];  // per-wave per-row outputs
+  __shared__ __align__(16) float red[NS][NW][NO][32];  // per-wave per-row outputs, [4 qd + i][kq]
+  __shared__ float redb[NS][NW];                        // per-wave parts of dbeta
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
   const int kq = lane & 31, vq = 2 * w + half;
   const Slot sl = slot_of(a);
@@ -229,14 +242,16 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
   load_block(dS, a.dSf ? a.dSf + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : nullptr, V, kq, vq);
 
   // register prefetch of one sub-segment: q, k, g rows (threads 0..255, one
-  // float4 each), the slices of v (threads 0..63) and do (threads 64..127),
+  // float4 each), the slices of r (threads 0..63) and do (threads 64..127),
   // beta (threads 0..NS-1), and every thread's part of the checkpoint
-  u32x4 pq, pk, pg, pv, pd, pc[NE / 4];
+  u32x4 pq, pk, pg, pr, pd, pc[NE / 4];
   float pb;
   const int srow = (tid & 255) >> 5, scol = 4 * (tid & 31);
   const bool stager = tid < 256;
   const int vrow = (tid & 63) >> 3, vcol = 4 * (tid & 7);
-  const float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (NE * NTH);
+  const i64 slice = (sl.bi * a.HV + sl.hv) * a.nvs + sl.vs;
+  const float* ckb = a.ck + slice * a.nck * (NE * NTH);
+  const float* rsb = a.rres + slice * a.nck * NS * VS;
   auto issue = [&](i64 j) {
     const i64 t0 = j * NS;
     const int ns = (int)(T - t0 < NS ? T - t0 : NS);
@@ -244,17 +259,16 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     const brsrc rq = make_rsrc(a.q + qk0, seg_bytes(ns, a.H * DK, DK));
     const brsrc rk = make_rsrc(a.k + qk0, seg_bytes(ns, a.H * DK, DK));
     const brsrc rg = make_rsrc(a.g + hv0 * DK, seg_bytes(ns, a.HV * DK, DK));
-    const brsrc rv = make_rsrc(a.v + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
+    const brsrc rr = make_rsrc(rsb + t0 * VS, (unsigned)(ns * VS * 4));
     const brsrc rd = make_rsrc(a.d_o + hv0 * V + sl.vs * VS, seg_bytes(ns, a.HV * V, VS));
     const brsrc rb = make_rsrc(a.beta + hv0, seg_bytes(ns, a.HV, 1));
     const brsrc rc = make_rsrc(ckb + j * NE * NTH, NE * NTH * 4);
     const unsigned qoff = stager ? (unsigned)((srow * a.H * DK + scol) * 4) : BUF_OOB;
-    const unsigned voff = (unsigned)((vrow * a.HV * V + vcol) * 4);
     pq = bload16(rq, qoff);
     pk = bload16(rk, qoff);
     pg = bload16(rg, stager ? (unsigned)((srow * a.HV * DK + scol) * 4) : BUF_OOB);
-    pv = bload16(rv, tid < 64 ? voff : BUF_OOB);
-    pd = bload16(rd, tid >= 64 && tid < 128 ? voff : BUF_OOB);
+    pr = bload16(rr, tid < 64 ? (unsigned)((vrow * VS + vcol) * 4) : BUF_OOB);
+    pd = bload16(rd, tid >= 64 && tid < 128 ? (unsigned)((vrow * a.HV * V + vcol) * 4) : BUF_OOB);
     pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
 #pragma unroll
     for (int i = 0; i < NE / 4; ++i) pc[i] = bload16(rc, (unsigned)((i * NTH + tid) * 16));
@@ -274,7 +288,7 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
         *(f32x4*)&sk[srow][scol] = as_f4(pk);
         *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
       }
-      if (tid < 64) *(f32x4*)&sv[vrow][vcol] = as_f4(pv);
+      if (tid < 64) *(f32x4*)&sr[vrow][vcol] = as_f4(pr);
       if (tid >= 64 && tid < 128) *(f32x4*)&sdo[vrow][vcol] = as_f4(pd);
       if (tid < NS) sb[tid] = pb;
 #pragma unroll
@@ -287,18 +301,26 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     if (j > 0) issue(j - 1);
     __syncthreads();  // staged rows visible; the previous reduction is done with red
 
-    // recompute the sub-segment's S_dec (registers) and r (LDS, per column)
+    // recompute the sub-segment's S_dec into registers from the checkpoint and
+    // the stored residuals: S_dec = exp(g) (.) S, S = S_dec + (beta k) (x) r
     float sd[NS][NE];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s >= ns) break;
-      float r[VT], vv[VT];
-      ld_cols(&sv[s][VT * vq], vv);
-      fwd_step(S, sd[s], lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], vv, r);
-      if (kq == 0) *(float2*)&sr[s][VT * vq] = make_float2(r[0], r[1]);
+      const f32x4 eg = lds4(&se[s][4 * kq]), kk = lds4(&sk[s][4 * kq]);
+      float rr[VT];
+      ld_cols(&sr[s][VT * vq], rr);
+      const float beta = sb[s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = beta * kk[i];
+#pragma unroll
+        for (int c = 0; c < VT; ++c) {
+          sd[s][VT * i + c] = eg[i] * S[VT * i + c];
+          S[VT * i + c] = fmaf(ai, rr[c], sd[s][VT * i + c]);
+        }
+      }
     }
-    // sr is written and read by the same wave (a column block lives in one
-    // half wave), and LDS operations of a wave complete in order
 
     // backward steps
 #pragma unroll
@@ -309,61 +331,77 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
       ld_cols(&sdo[s][VT * vq], dd);
       ld_cols(&sr[s][VT * vq], rr);
       const float beta = sb[s];
-      float o[16];  // per-row outputs: o[4*qd + i], qd = dq_e, da, S_dec dr, dg
-      float drp[VT];
+      float o[NO];  // per-row outputs: o[4*qd + i], qd = dq_e, dk_e, dg
+      float da[4], up[VT];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = beta * kk[i];
-        float dq_e = 0.0f, da = 0.0f;
+        float dq_e = 0.0f, dai = 0.0f;
 #pragma unroll
         for (int c = 0; c < VT; ++c) {
           const int e = VT * i + c;
-          dS[e] = fmaf(qq[i], dd[c], dS[e]);                     // step 1: dS += (scale q) (x) do
-          dq_e = fmaf(fmaf(ai, rr[c], sd[s][e]), dd[c], dq_e);  //         dq_e = S_t do
-          da = fmaf(rr[c], dS[e], da);                          // step 2: da = dS r
-          drp[c] = i == 0 ? ai * dS[e] : fmaf(ai, dS[e], drp[c]);  //      dr = dS^T a
+          dS[e] = fmaf(qq[i], dd[c], dS[e]);                     // dS' = dS + (scale q) (x) do
+          dq_e = fmaf(fmaf(ai, rr[c], sd[s][e]), dd[c], dq_e);  // dq_e = S_t do
+          dai = fmaf(rr[c], dS[e], dai);                        // dS' r
+          up[c] = i == 0 ? kk[i] * dS[e] : fmaf(kk[i], dS[e], up[c]);  // u = dS'^T k
         }
         o[i] = dq_e;
-        o[4 + i] = da;
+        da[i] = dai;
       }
-      float dr[VT];
+      float u[VT], dr[VT];
 #pragma unroll
-      for (int c = 0; c < VT; ++c) dr[c] = sum32(drp[c]);
+      for (int c = 0; c < VT; ++c) {
+        u[c] = sum32(up[c]);
+        dr[c] = beta * u[c];
+      }
+      const float bpart = fmaf(rr[0], u[0], rr[1] * u[1]);  // this column block's u . r
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float sdr = 0.0f, dg = 0.0f;
+        float su = 0.0f, dg = 0.0f;
 #pragma unroll
         for (int c = 0; c < VT; ++c) {
           const int e = VT * i + c;
-          sdr = fmaf(sd[s][e], dr[c], sdr);     // step 4: S_dec dr
-          dS[e] = fmaf(-kk[i], dr[c], dS[e]);   // step 5: dS_dec = dS - k (x) dr
-          dg = fmaf(sd[s][e], dS[e], dg);       //         dg = rowsum(S_dec (.) dS_dec)
-          dS[e] *= eg[i];                       //         dS_{t-1} = exp(g) (.) dS_dec
+          su = fmaf(sd[s][e], u[c], su);        // S_dec u
+          dS[e] = fmaf(-kk[i], dr[c], dS[e]);   // dS_dec = dS' - k (x) dr
+          dg = fmaf(sd[s][e], dS[e], dg);       // dg = rowsum(S_dec (.) dS_dec)
+          dS[e] *= eg[i];                       // dS_{t-1} = exp(g) (.) dS_dec
         }
-        o[8 + i] = sdr;
-        o[12 + i] = dg;
+        o[4 + i] = beta * (da[i] - su);         // dk_e = beta (dS' r - S_dec u)
+        o[8 + i] = dg;
       }
       // dv = dr: this column block's values, from one lane per half wave
       if (kq == 0) {
         float* dvp = a.dv + ((sl.bi * T + t0 + s) * a.HV + sl.hv) * V + sl.vs * VS + VT * vq;
         *(float2*)dvp = make_float2(dr[0], dr[1]);
       }
-      // per-row outputs: pair the half waves (same rows, other columns)
+      // per-row outputs: pair the half waves (same rows, other columns); half
+      // 0 keeps outputs 0..5, half 1 outputs 6..11
 #pragma unroll
-      for (int jv = 0; jv < 8; ++jv) red[s][w][8 * half + jv][kq] = pair_halves(o[jv], o[8 + jv]);
+      for (int jv = 0; jv < NO / 2; ++jv) red[s][w][(NO / 2) * half + jv][kq] = pair_halves(o[jv], o[NO / 2 + jv]);
+      const float bw = pair_halves(bpart, bpart);  // both halves: the wave's 4 columns
+      if (lane == 0) redb[s][w] = bw;
     }
     __syncthreads();  // red complete
-    // sum the waves; thread -> row k, (step, output) pairs hsel, hsel+4, ...
+    // sum the waves: thread (row group kq, output slots p = m*16 + tid/32) reads
+    // red[s][.][js][kq] for 32 consecutive kq (one bank each), stores 32
+    // consecutive partial sums
     {
-      const int kr = tid & (DK - 1), hsel = tid >> 7;
+      const int pk0 = tid >> 5;
 #pragma unroll
-      for (int m = 0; m < NS * NQ / (NTH / DK); ++m) {
-        const int pidx = hsel + (NTH / DK) * m, s = pidx >> 2, qd = pidx & 3;
+      for (int m = 0; m < NS * NO / (NTH / 32); ++m) {
+        const int pidx = pk0 + (NTH / 32) * m, s = pidx / NO, js = pidx % NO;
         if (s >= ns) continue;
-        float acc = red[s][0][4 * qd + (kr & 3)][kr >> 2];
+        float acc = red[s][0][js][kq];
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) acc += red[s][ww][4 * qd + (kr & 3)][kr >> 2];
-        a.part[((((sl.bi * T + t0 + s) * a.HV + sl.hv) * a.nvs + sl.vs) * NQ + qd) * DK + kr] = acc;
+        for (int ww = 1; ww < NW; ++ww) acc += red[s][ww][js][kq];
+        a.part[((((sl.bi * T + t0 + s) * a.HV + sl.hv) * a.nvs + sl.vs) * NQ + js / 4) * DK + (js & 3) * 32 + kq] =
+            acc;
+      }
+      if (tid < ns) {
+        float acc = redb[tid][0];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) acc += redb[tid][ww];
+        a.partb[((sl.bi * T + t0 + tid) * a.HV + sl.hv) * a.nvs + sl.vs] = acc;
       }
     }
   }
@@ -382,33 +420,41 @@ __global__ void __launch_bounds__(256) delta_reduce_kernel(DeltaArgs a) {
   const i64 id = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (id >= a.b * a.T * a.H) return;  // whole waves
   const i64 h = id % a.H, bt = id / a.H;
-  const int k0 = 2 * lane;
-  const float2 kk = *(const float2*)(a.k + (bt * a.H + h) * DK + k0);
+  // lane handles stored positions lane and lane + 64, i.e. rows k = 4 (p % 32) + p / 32
+  const int k0 = 4 * (lane & 31) + (lane >> 5), k1 = k0 + 2;
   float dq0 = 0.f, dq1 = 0.f, dk0 = 0.f, dk1 = 0.f;
   for (i64 j = 0; j < a.grp; ++j) {
     const i64 hv = h * a.grp + j;
-    const float* pp = a.part + (bt * a.HV + hv) * a.nvs * NQ * DK + k0;
+    const float* pp = a.part + (bt * a.HV + hv) * a.nvs * NQ * DK;
     float s[NQ][2];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) s[qd][0] = s[qd][1] = 0.0f;
     for (i64 vs = 0; vs < a.nvs; ++vs)
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const float2 x = *(const float2*)(pp + (vs * NQ + qd) * DK);
-        s[qd][0] += x.x;
-        s[qd][1] += x.y;
+        s[qd][0] += pp[(vs * NQ + qd) * DK + lane];
+        s[qd][1] += pp[(vs * NQ + qd) * DK + 64 + lane];
       }
-    *(float2*)(a.dg + (bt * a.HV + hv) * DK + k0) = make_float2(s[3][0], s[3][1]);
-    const float db = wave_sum(fmaf(kk.x, s[1][0], kk.y * s[1][1]));
-    if (lane == 0) a.dbeta[bt * a.HV + hv] = db;
-    const float bta = a.beta[bt * a.HV + hv];
+    float* dgp = a.dg + (bt * a.HV + hv) * DK;
+    dgp[k0] = s[2][0];
+    dgp[k1] = s[2][1];
+    if (lane == 0) {
+      const float* pb = a.partb + (bt * a.HV + hv) * a.nvs;
+      float db = 0.0f;
+      for (i64 vs = 0; vs < a.nvs; ++vs) db += pb[vs];
+      a.dbeta[bt * a.HV + hv] = db;
+    }
     dq0 += s[0][0];
     dq1 += s[0][1];
-    dk0 += bta * s[1][0] - s[2][0];
-    dk1 += bta * s[1][1] - s[2][1];
+    dk0 += s[1][0];
+    dk1 += s[1][1];
   }
-  *(float2*)(a.dq + (bt * a.H + h) * DK + k0) = make_float2(a.scale * dq0, a.scale * dq1);
-  *(float2*)(a.dk + (bt * a.H + h) * DK + k0) = make_float2(dk0, dk1);
+  float* dqp = a.dq + (bt * a.H + h) * DK;
+  float* dkp = a.dk + (bt * a.H + h) * DK;
+  dqp[k0] = a.scale * dq0;
+  dqp[k1] = a.scale * dq1;
+  dkp[k0] = dk0;
+  dkp[k1] = dk1;
 }
 
 }  // namespace
@@ -434,7 +480,9 @@ DeltaPlan delta_plan(const ssmvjp_delta_desc& d) {
     return o;
   };
   p.off_ck = carve(d.batch * d.nv_heads * p.nck * DK * d.dv * 4);  // NE * NTH floats per (slice, checkpoint)
+  p.off_r = carve(d.batch * d.nv_heads * p.nck * NS * d.dv * 4);    // residual of every step
   p.off_part = carve(d.batch * d.seqlen * d.nv_heads * p.vsplit * NQ * DK * 4);
+  p.off_partb = carve(d.batch * d.seqlen * d.nv_heads * p.vsplit * 4);
   p.bytes = (size_t)off;
   return p;
 }
@@ -449,7 +497,9 @@ hipError_t launch_delta_bwd(const ssmvjp_delta_desc& d, const DeltaPlan& plan, c
   a.dS0 = ptr.dS0;
   char* ws = (char*)ptr.workspace;
   a.ck = (float*)(ws + plan.off_ck);
+  a.rres = (float*)(ws + plan.off_r);
   a.part = (float*)(ws + plan.off_part);
+  a.partb = (float*)(ws + plan.off_partb);
   const i64 nwg = d.batch * d.nv_heads * plan.vsplit;
   if (nwg == 0) return hipSuccess;
   if ((stages & SSMVJP_DELTA_CKPT) && d.seqlen > 0)

@@ -102,7 +102,7 @@ struct DeltaPlan {
   int64_t CK;          // checkpoint interval (steps)
   int64_t nck;         // checkpoints per (b, hv)
   int64_t vsplit;      // value-column slices per (b, hv), one workgroup each
-  int64_t off_ck, off_part;
+  int64_t off_ck, off_r, off_part, off_partb;
   size_t bytes;
 };
 
