@@ -18,7 +18,8 @@ ROOT = PKG.parent
 BUILD = ROOT / "_build"
 LIB = PKG / "libssmvjp.so"
 SOURCES = ["abi.cpp", "scan_seq.hip", "ssd_chunk.hip", "ssd_chunk16.hip", "ssd_blocked.hip", "ssd_fwd.hip", "delta_rule.hip",
-           "noalloc.hip", "finite.hip"]
+           "noalloc.hip", "finite.hip",
+           "ssd_pad.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", str(ROOT / "include")]

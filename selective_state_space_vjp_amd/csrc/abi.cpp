@@ -43,8 +43,16 @@ ssmvjp_status ssd_check(const ssmvjp_ssd_desc* d) {
   if (d->form != SSMVJP_FORM_MAMBA2 && d->form != SSMVJP_FORM_RAW) return SSMVJP_EINVAL;
   if (d->form == SSMVJP_FORM_MAMBA2 && d->mimo_rank != 1) return SSMVJP_EINVAL;
   if (!valid_dtype(d->dtype)) return SSMVJP_EINVAL;
-  if (!ssd_shape_supported(*d)) return SSMVJP_EUNSUPPORTED;
+  if (!ssd_shape_supported(*d) && !ssd_pad_supported(*d)) return SSMVJP_EUNSUPPORTED;
   return SSMVJP_OK;
+}
+
+// workspace of the chunked backward: its plan, or the zero-padded problem's
+size_t ssd_bytes(const ssmvjp_ssd_desc& d) {
+  return ssd_shape_supported(d) ? ssd_plan(d).bytes : ssd_pad_workspace_bytes(d);
+}
+size_t ssd_fwd_bytes(const ssmvjp_ssd_desc& d) {
+  return ssd_fwd_shape_supported(d) ? ssd_fwd_workspace_bytes(d) : ssd_fwd_pad_workspace_bytes(d);
 }
 
 ssmvjp_status delta_check(const ssmvjp_delta_desc* d) {
@@ -178,7 +186,7 @@ ssmvjp_status ssd_chunk_bwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = ssd_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = with_flag(ssd_plan(*desc).bytes);
+  *bytes = with_flag(ssd_bytes(*desc));
   return SSMVJP_OK;
 }
 
@@ -204,12 +212,12 @@ static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, co
   const void* pf[] = {dt_or_da, A, s0, ds_final, d_dt_or_dda, d_s0, dA};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
-  const SsdPlan plan = ssd_plan(d);
-  const size_t need = with_flag(plan.bytes);
+  const size_t plan_bytes = ssd_bytes(d), need = with_flag(plan_bytes);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (!has_state) return SSMVJP_OK;
   SsdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, dy, ds_final, dx_or_dv, d_dt_or_dda, dB, dC, d_s0, workspace, dA};
-  s = hip_status(launch_ssd_bwd(d, plan, ptr, (hipStream_t)stream, stages));
+  s = hip_status(ssd_shape_supported(d) ? launch_ssd_bwd(d, ssd_plan(d), ptr, (hipStream_t)stream, stages)
+                                        : launch_ssd_bwd_padded(d, ptr, (hipStream_t)stream, stages));
   if (s != SSMVJP_OK || !check_finite_on()) return s;
   const bool bf = d.dtype == SSMVJP_BF16;
   const int64_t nx = d.batch * d.seqlen * d.mimo_rank * d.nheads * d.headdim;
@@ -219,7 +227,7 @@ static ssmvjp_status ssd_run(const ssmvjp_ssd_desc* desc, const void* x_or_v, co
                           {grads ? dB : nullptr, nbc, bf}, {grads ? dC : nullptr, nbc, bf},
                           {states ? d_s0 : nullptr, d.batch * d.nheads * d.headdim * d.dstate, false},
                           {grads ? dA : nullptr, dA ? d.nheads : 0, false}};
-  return finite_check(workspace, plan.bytes, outs, (hipStream_t)stream);
+  return finite_check(workspace, plan_bytes, outs, (hipStream_t)stream);
 }
 
 ssmvjp_status ssd_chunk_bwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, const float* dt_or_da,
@@ -269,7 +277,7 @@ ssmvjp_status ssd_fwd_check(const ssmvjp_ssd_desc* desc) {
   if (d.form != SSMVJP_FORM_MAMBA2 && d.form != SSMVJP_FORM_RAW) return SSMVJP_EINVAL;
   if (d.form == SSMVJP_FORM_MAMBA2 && d.mimo_rank != 1) return SSMVJP_EINVAL;
   if (!valid_dtype(d.dtype)) return SSMVJP_EINVAL;
-  if (!ssd_fwd_shape_supported(d)) return SSMVJP_EUNSUPPORTED;
+  if (!ssd_fwd_shape_supported(d) && !ssd_fwd_pad_supported(d)) return SSMVJP_EUNSUPPORTED;
   return SSMVJP_OK;
 }
 }  // namespace
@@ -278,7 +286,7 @@ ssmvjp_status ssd_chunk_fwd_workspace(const ssmvjp_ssd_desc* desc, size_t* bytes
   if (!bytes) return SSMVJP_EINVAL;
   ssmvjp_status s = ssd_fwd_check(desc);
   if (s != SSMVJP_OK) return s;
-  *bytes = with_flag(ssd_fwd_workspace_bytes(*desc));
+  *bytes = with_flag(ssd_fwd_bytes(*desc));
   return SSMVJP_OK;
 }
 
@@ -297,11 +305,12 @@ ssmvjp_status ssd_chunk_fwd(const ssmvjp_ssd_desc* desc, const void* x_or_v, con
   const void* pf[] = {dt_or_da, A, s0, s_final};
   for (const void* p : pf)
     if (p && !aligned(p, 4)) return SSMVJP_EINVAL;
-  const size_t plan_bytes = ssd_fwd_workspace_bytes(d), need = with_flag(plan_bytes);
+  const size_t plan_bytes = ssd_fwd_bytes(d), need = with_flag(plan_bytes);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SSMVJP_EWORKSPACE;
   if (d.batch == 0) return SSMVJP_OK;
   SsdFwdPointers ptr{x_or_v, dt_or_da, A, B, C, s0, y, s_final, workspace};
-  s = hip_status(launch_ssd_fwd(d, ptr, (hipStream_t)stream));
+  s = hip_status(ssd_fwd_shape_supported(d) ? launch_ssd_fwd(d, ptr, (hipStream_t)stream)
+                                            : launch_ssd_fwd_padded(d, ptr, (hipStream_t)stream));
   if (s != SSMVJP_OK || !check_finite_on()) return s;
   const OutSpan outs[] = {{y, d.batch * d.seqlen * d.mimo_rank * d.nheads * d.headdim, d.dtype == SSMVJP_BF16},
                           {s_final, d.batch * d.nheads * d.headdim * d.dstate, false}};

@@ -97,6 +97,16 @@ bool ssd_fwd_shape_supported(const ssmvjp_ssd_desc& d);
 size_t ssd_fwd_workspace_bytes(const ssmvjp_ssd_desc& d);
 hipError_t launch_ssd_fwd(const ssmvjp_ssd_desc& d, const SsdFwdPointers& ptr, hipStream_t stream);
 
+// P or N not a multiple of 16: the same calls on a zero-padded copy in the
+// workspace (ssd_pad.hip); *_supported is true only where the unpadded shape
+// is not supported and the padded one is
+bool ssd_pad_supported(const ssmvjp_ssd_desc& d);
+bool ssd_fwd_pad_supported(const ssmvjp_ssd_desc& d);
+size_t ssd_pad_workspace_bytes(const ssmvjp_ssd_desc& d);
+size_t ssd_fwd_pad_workspace_bytes(const ssmvjp_ssd_desc& d);
+hipError_t launch_ssd_bwd_padded(const ssmvjp_ssd_desc& d, const SsdPointers& ptr, hipStream_t stream, int stages);
+hipError_t launch_ssd_fwd_padded(const ssmvjp_ssd_desc& d, const SsdFwdPointers& ptr, hipStream_t stream);
+
 // ------------------------------ delta rule ---------------------------------
 struct DeltaPlan {
   int64_t CK;          // checkpoint interval (steps)

@@ -75,7 +75,9 @@ static void ssd_checks() {
   bad.mimo_rank = 2;  // Mamba-2 form needs M = 1
   CHECK(ssd_chunk_bwd_workspace(&bad, &n), SSMVJP_EINVAL);
   bad = d;
-  bad.headdim = 20;  // not a multiple of 16
+  bad.headdim = 20;  // not a multiple of 16: zero-padded to 32
+  CHECK(ssd_chunk_bwd_workspace(&bad, &n), SSMVJP_OK);
+  bad.chunk_len = 24;  // the fused chunk length is not padded
   CHECK(ssd_chunk_bwd_workspace(&bad, &n), SSMVJP_EUNSUPPORTED);
   bad = d;
   bad.form = 7;
@@ -125,6 +127,8 @@ static void ssd_checks() {
   CHECK(ssd_chunk_bwd_noalloc(&big, p[0], (const float*)p[1], (const float*)p[2], p[3], p[4], (const float*)p[5],
                               p[6], (const float*)p[7], p[8], (float*)p[9], p[10], p[11], (float*)p[12], nullptr),
         SSMVJP_EWORKSPACE);
+  bad = d;
+  bad.form = 7;
   CHECK(ssd_chunk_bwd_noalloc(&bad, p[0], (const float*)p[1], (const float*)p[2], p[3], p[4], (const float*)p[5],
                               p[6], (const float*)p[7], p[8], (float*)p[9], p[10], p[11], (float*)p[12], nullptr),
         SSMVJP_EINVAL);

@@ -98,8 +98,14 @@ def _ssd(**kw):
     (dict(form=0, mimo_rank=2), bd.EINVAL),
     (dict(form=3), bd.EINVAL),
     (dict(chunk_len=0), bd.EINVAL),
-    (dict(headdim=20), bd.EUNSUPPORTED),
-    (dict(dstate=40), bd.EUNSUPPORTED),
+    # P or N off the 16-multiple: run zero-padded to the next multiple of 16
+    # when the padded shape is supported
+    (dict(headdim=20), bd.OK),
+    (dict(dstate=40), bd.OK),
+    (dict(headdim=4, dstate=8, chunk_len=16), bd.OK),
+    (dict(headdim=4, dstate=8, chunk_len=64, dtype=0), bd.OK),
+    (dict(headdim=120, dstate=128), bd.EUNSUPPORTED),  # padded to P = N = 128: too large at L = 64
+    (dict(headdim=20, chunk_len=72), bd.EUNSUPPORTED),  # padding does not cover the chunk length
     (dict(dstate=256), bd.EUNSUPPORTED),
     (dict(headdim=112, dstate=80), bd.EUNSUPPORTED),
     (dict(headdim=128, dstate=128), bd.EUNSUPPORTED),
@@ -183,8 +189,9 @@ def test_ssd_stage_entry_points_validate_like_the_full_call():
     (dict(form=1, mimo_rank=4), bd.OK, bd.EINVAL),
     (dict(form=1, mimo_rank=3, chunk_len=16), bd.OK, bd.EINVAL),  # steps straddle 16-row tiles
     (dict(headdim=48, dstate=96, dtype=0), bd.OK, bd.EINVAL),
-    (dict(headdim=20), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
-    (dict(dstate=40), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
+    (dict(headdim=20), bd.OK, bd.EINVAL),  # zero-padded to 32
+    (dict(dstate=40), bd.OK, bd.EINVAL),   # zero-padded to 48
+    (dict(dstate=250), bd.EUNSUPPORTED, bd.EUNSUPPORTED),  # 256 after padding: over the forward's N <= 128
     (dict(dstate=256), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
     (dict(form=1, mimo_rank=65), bd.EUNSUPPORTED, bd.EUNSUPPORTED),
     (dict(nheads=3, ngroups=2), bd.EINVAL, bd.EINVAL),
@@ -291,3 +298,12 @@ def test_debug_mode_still_validates_before_launching(monkeypatch):
     monkeypatch.setenv("SSMVJP_CHECK_FINITE", "1")
     fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(13)]
     assert bd.lib().ssm_scan_bwd(ctypes.byref(d), *fake, ctypes.c_void_p(1 << 20), n, None) == bd.EWORKSPACE
+
+
+def test_padded_workspace_holds_the_padded_problem():
+    """A P or N off the 16-multiple needs the padded problem's workspace plus
+    the padded copies of the inputs and outputs: more than the next supported
+    shape's own workspace."""
+    n_pad = _ws("ssd_chunk_bwd_workspace", _ssd(headdim=20, dtype=0))[1]
+    n_32 = _ws("ssd_chunk_bwd_workspace", _ssd(headdim=32, dtype=0))[1]
+    assert n_pad > n_32

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "selective_state_space_vjp_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LIB_SOURCES = ["abi.cpp", "scan_seq.hip", "ssd_chunk.hip", "ssd_chunk16.hip", "ssd_blocked.hip", "ssd_fwd.hip",
-               "delta_rule.hip", "noalloc.hip", "finite.hip"]
+               "delta_rule.hip", "noalloc.hip", "finite.hip", "ssd_pad.hip"]
 SAN_ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
 
