@@ -410,13 +410,35 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
+        # a plain 1 GiB device copy: the reference for the HBM byte counters
+        # (FETCH_SIZE / WRITE_SIZE of a known transfer) and the rate a pure
+        # streaming kernel reaches on this GPU (read + write bytes / time)
         n = 1 << 28  # 2^28 float32 = 1 GiB
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        ms = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        fill = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.fill_(1.0)
+            e1.record()
+            torch.cuda.synchronize()
+            fill.append(e0.elapsed_time(e1))
+        med = sorted(ms)[2]
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 6, "copy_ms_median": round(med, 4),
+                          "copy_GBps": round(2 * n * 4 / (med * 1e6), 1),
+                          "fill_GBps": round(n * 4 / (sorted(fill)[2] * 1e6), 1),
+                          "machine": machine_info()}), flush=True)
         return
     if args.workload == "kda":
         return bench_kda(args, dev)
