@@ -29,6 +29,12 @@
 // a small buffer; a third kernel, one wave per (batch, chunk, head), adds them
 // up, runs the K1 suffix sum and the chain to d_dt (or d_da).
 //
+// A workgroup's start-up loads (its own rows, the head's state and step
+// scalars, the first pair's rows) are issued together, so their latencies
+// overlap; each later pair's rows are prefetched into registers during the
+// previous pair.  The transposed-read products are scheduled with their reads
+// issued ahead of the MFMAs that consume them.
+//
 // Products accumulate in float32; with bf16 storage the MFMA operands are bf16
 // (inputs as given, d_cb and w rounded once).
 #include "ssd_common.cuh"
@@ -119,6 +125,62 @@ __device__ __forceinline__ void bk_stage_state(T* dst, const T* src, int PN, int
     *(u32x4*)((char*)dst + bk_state_off<SWZ>(idx)) = bload16(r, (unsigned)idx * 16u);
 }
 
+// 64 rows (ncol columns) or one [P x N] state as 16-byte chunks, loaded into
+// registers now and written into LDS later, so that a workgroup's start-up
+// loads are all in flight together (compile-time shapes: the register arrays
+// are sized exactly)
+template <int NR, typename T>
+__device__ __forceinline__ void bk_load_rows(u32x4 (&r)[NR], const T* src, i64 stride, int ncol, int valid, int tid) {
+  constexpr int E16 = 16 / sizeof(T);
+  const int cpr = ncol / E16;
+  const brsrc rs = make_rsrc(src, valid > 0 ? (unsigned)(((valid - 1) * stride + ncol) * sizeof(T)) : 0u);
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int idx = tid + it * BK_NTH, row = idx / cpr, col = (idx % cpr) * E16;
+    r[it] = bload16(rs, idx < BK_R * cpr ? (unsigned)((row * stride + col) * sizeof(T)) : BUF_OOB);
+  }
+}
+template <bool SWZ, int NR, typename T>
+__device__ __forceinline__ void bk_put_rows(T* dst, int pitch, const u32x4 (&r)[NR], int ncol, int tid) {
+  constexpr int E16 = 16 / sizeof(T);
+  const int cpr = ncol / E16;
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int idx = tid + it * BK_NTH;
+    if (idx < BK_R * cpr) bk_put16<SWZ>(dst, pitch, idx / cpr, (idx % cpr) * E16, r[it]);
+  }
+}
+template <int NR, typename T>
+__device__ __forceinline__ void bk_load_state(u32x4 (&r)[NR], const T* src, int PN, int tid) {
+  const brsrc rs = make_rsrc(src, (unsigned)(PN * sizeof(T)));
+#pragma unroll
+  for (int it = 0; it < NR; ++it) r[it] = bload16(rs, (unsigned)(tid + it * BK_NTH) * 16u);
+}
+template <bool SWZ, int NR, typename T>
+__device__ __forceinline__ void bk_put_state(T* dst, const u32x4 (&r)[NR], int PN, int tid) {
+  constexpr int E16 = 16 / sizeof(T);
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int idx = tid + it * BK_NTH;
+    if (idx < PN / E16) *(u32x4*)((char*)dst + bk_state_off<SWZ>(idx)) = r[it];
+  }
+}
+
+// Scheduling pattern for a run of n MFMAs whose B operands are n LDS reads
+// (one each): the first `ahead` reads, then one MFMA per read, so that reads
+// stay in flight under the products instead of each product waiting for its
+// own read.
+template <int n, int ahead>
+__device__ __forceinline__ void bk_pipeline_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, ahead, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < n - ahead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, ahead, 0);
+}
+
 // bf16: two workgroups per CU, at most 256 registers (VGPR + AGPR) per lane.
 // CP, CN, CM: compile-time P, N and rank M (0: from the arguments).
 template <typename T, int CP, int CN, int CM>
@@ -131,6 +193,9 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
   // with a compile-time rank that is a multiple of 4, the 4 rows a lane holds
   // in a 16x16 tile (4q .. 4q+3) belong to one step: one decay per tile and lane
   constexpr bool STEP4 = CM != 0 && CM % 4 == 0;
+  // with compile-time P and N, a head's loads (scalars, own rows, state) are
+  // issued together into registers; otherwise they are staged one by one
+  constexpr bool MERGE = CP != 0 && CN != 0;
   const int PT = P / 16, NT = N / 16, LM = (int)a.LM, nblk = LM / BK_R;
   const int LDN = N + PAD, LDP = P + PAD, PN = P * N;
   T* Bs = (T*)smem_raw;    // [64][LDN] B rows of a source block
@@ -143,6 +208,7 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, q = lane >> 4,
             r16 = lane & 15;
   __builtin_assume(w >= 0 && w < BK_NW);
+  __builtin_assume(tid >= 0 && tid < BK_NTH);
   // XCD-aware order: consecutive workgroups of one (batch, chunk, group) share
   // their input rows, so they are given ids that land on the same XCD (ids are
   // dealt to the 8 XCDs round robin)
@@ -177,6 +243,7 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
   constexpr int E16 = 16 / sizeof(T);
   constexpr int MAXN = CN ? (BK_R * CN / E16 + BK_NTH - 1) / BK_NTH : BK_R * 128 / E16 / BK_NTH;
   constexpr int MAXP = CP ? (BK_R * CP / E16 + BK_NTH - 1) / BK_NTH : BK_R * 128 / E16 / BK_NTH;
+  constexpr int MAXS = MERGE ? (CP * CN / E16 + BK_NTH - 1) / BK_NTH : 1;
   u32x4 pn[MAXN], pp[MAXP];
   const int cpn = N / E16, cpp = P / E16;  // 16-byte chunks per row
   auto issue = [&](const T* srcN, const T* srcP, int valid) {
@@ -212,6 +279,8 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     const int nT = nblk - blk;
     const int nsteps = (int)a.hpg * nT;
     auto issue_step = [&](int hh, int tb) {
+      hh = __builtin_amdgcn_readfirstlane(hh);
+      tb = __builtin_amdgcn_readfirstlane(tb);
       const i64 h = g * a.hpg + hh;
       issue(Cg + (i64)tb * BK_R * bstr, (const T*)a.dy + xrow0 + (i64)tb * BK_R * xstr + h * P, valid_in(tb));
     };
@@ -221,20 +290,40 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     f32x4 dvT[BK_TMAX];  // d_v^T tiles (rows p, columns s) of the current head
     float s1 = 0.0f, ocol = 0.0f, cum_s = 0.0f, delta_s = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
-    bk_stage_rows<SWZ>(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    u32x4 rown[MAXN];  // the block's own B rows, written with the first head's rows
+    if constexpr (MERGE)
+      bk_load_rows(rown, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    else
+      bk_stage_rows<SWZ>(Bs, LDN, Bg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
     issue_step(0, blk);
     // step k = (head hh, target block tb), counted without divisions
     for (int k = 0, hh = 0, tb = blk; k < nsteps; ++k, tb = (tb + 1 == nblk) ? blk : tb + 1, hh += (tb == blk)) {
       const i64 h = g * a.hpg + hh;
       if (tb == blk) {
         // ---- a new head: its scalars, x / v rows and dS_{c+1}; then the K3 backward ----
-        cs = scalars(h);
+        const T* xg = (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P;
+        const T* dSg = (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+        u32x4 rx[MAXP], rst[MAXS];
+        if constexpr (MERGE) {  // all of the head's loads in flight together
+          ChunkScalars csn = issue_scalars(a, bi, c, h, lane);
+          bk_load_rows(rx, xg, xstr, P, valid_in(blk), tid);
+          bk_load_state(rst, dSg, PN, tid);
+          cs = finish_scalars(csn);
+        } else {
+          cs = scalars(h);
+        }
         cum_s = __shfl(cs.cum, l_col & 63, 64);
         delta_s = __shfl(cs.delta, l_col & 63, 64);
         const float edec = exp_hw(cs.end - cum_s), xcol = delta_s * edec;
         __syncthreads();  // the previous head is done with xs / STs
-        bk_stage_rows<SWZ>(xs, LDP, (const T*)a.xv + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-        bk_stage_state<SWZ>(STs, (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+        if constexpr (MERGE) {
+          if (k == 0) bk_put_rows<SWZ>(Bs, LDN, rown, N, tid);
+          bk_put_rows<SWZ>(xs, LDP, rx, P, tid);
+          bk_put_state<SWZ>(STs, rst, PN, tid);
+        } else {
+          bk_stage_rows<SWZ>(xs, LDP, xg, xstr, P, valid_in(blk), tid);
+          bk_stage_state<SWZ>(STs, dSg, PN, tid);
+        }
         __syncthreads();
         // K3: d_dv^T = dS_{c+1}.B^T (rows p, columns s); dB_k3^T += dS^T . (xcol v)^T
         s1 = 0.0f;
@@ -304,6 +393,7 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
         wf[tt] = frag_make<T>(wv);
         df[tt] = frag_make<T>(dv);
       }
+      if constexpr (CP && CN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int pt = 0; pt < BK_TMAX; ++pt) {  // d_v_or^T += dy^T . w
         if (pt >= PT) continue;
@@ -316,6 +406,7 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) mma(dBT[nt], bk_rowk<SWZ>(Cs, LDN, 16 * tt, 16 * nt, lane), df[tt]);
       }
+      if constexpr (CP && CN) bk_pipeline_reads<4 * (CP + CN) / 16, 8>();
 
       if (tb == nblk - 1) {
         // ---- the head's outputs: dx (= d_v, times delta for Mamba-2), the column sums ----
@@ -358,6 +449,8 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     const int nS = blk + 1;
     const int nsteps = (int)a.hpg * nS;
     auto issue_step = [&](int hh, int sb) {
+      hh = __builtin_amdgcn_readfirstlane(hh);
+      sb = __builtin_amdgcn_readfirstlane(sb);
       const i64 h = g * a.hpg + hh;
       issue(Bg + (i64)sb * BK_R * bstr, (const T*)a.xv + xrow0 + (i64)sb * BK_R * xstr + h * P, valid_in(sb));
     };
@@ -366,26 +459,45 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
     for (int i = 0; i < BK_TMAX; ++i) dCT[i] = zero4();
     float blue = 0.0f, orow = 0.0f, cum_t = 0.0f;
     ChunkScalars cs = {0.f, 0.f, 0.f, 0.f};
-    bk_stage_rows<SWZ>(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    u32x4 rown[MAXN];  // the block's own C rows, written with the first head's rows
+    if constexpr (MERGE)
+      bk_load_rows(rown, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
+    else
+      bk_stage_rows<SWZ>(Cs, LDN, Cg + (i64)blk * BK_R * bstr, bstr, N, valid_in(blk), tid);
     issue_step(0, 0);
     // step k = (head hh, source block sb), counted without divisions
     for (int k = 0, hh = 0, sb = 0; k < nsteps; ++k, sb = (sb == blk) ? 0 : sb + 1, hh += (sb == 0)) {
       const i64 h = g * a.hpg + hh;
       if (sb == 0) {
         // ---- a new head: its scalars, dy rows and S_c; d_end; BLUE ----
-        cs = scalars(h);
+        const T* dyg = (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P;
+        const T* Sg = (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+        const T* dSg = (const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN;
+        u32x4 rdy[MAXP], rst[MAXS], rds[MAXS];
+        if constexpr (MERGE) {  // all of the head's loads in flight together (dS_{c+1} only for d_end)
+          ChunkScalars csn = issue_scalars(a, bi, c, h, lane);
+          bk_load_rows(rdy, dyg, xstr, P, valid_in(blk), tid);
+          bk_load_state(rst, Sg, PN, tid);
+          if (blk == 0) bk_load_state(rds, dSg, PN, tid);
+          cs = finish_scalars(csn);
+        } else {
+          cs = scalars(h);
+        }
         cum_t = __shfl(cs.cum, l_col & 63, 64);
         const float ecol = exp_hw(cum_t);
         __syncthreads();  // the previous head is done with dys / STs
-        bk_stage_rows<SWZ>(dys, LDP, (const T*)a.dy + xrow0 + (i64)blk * BK_R * xstr + h * P, xstr, P, valid_in(blk), tid);
-        bk_stage_state<SWZ>(STs, (const T*)a.S + ((bi * a.nc + c) * a.H + h) * (i64)PN, PN, tid);
+        if constexpr (MERGE) {
+          if (k == 0) bk_put_rows<SWZ>(Cs, LDN, rown, N, tid);
+          bk_put_rows<SWZ>(dys, LDP, rdy, P, tid);
+          bk_put_state<SWZ>(STs, rst, PN, tid);
+        } else {
+          bk_stage_rows<SWZ>(dys, LDP, dyg, xstr, P, valid_in(blk), tid);
+          bk_stage_state<SWZ>(STs, Sg, PN, tid);
+        }
         __syncthreads();
         if (blk == 0) {  // d_end = sum_{p,n} S_c * dS_{c+1}, once per chunk and head
-          const brsrc rdS = make_rsrc((const T*)a.dS + ((bi * a.nc + c) * a.H + h) * (i64)PN, (unsigned)PN * esz);
           float part = 0.0f;
-          for (int idx = tid; idx < PN / E16; idx += BK_NTH) {
-            const u32x4 u = bload16(rdS, (unsigned)idx * 16u);
-            const u32x4 v = *(const u32x4*)((const char*)STs + bk_state_off<SWZ>(idx));
+          auto dot16 = [&](const u32x4& u, const u32x4& v) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if constexpr (BF) {
@@ -395,6 +507,15 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
                 part += __uint_as_float(u[e]) * __uint_as_float(v[e]);
               }
             }
+          };
+          if constexpr (MERGE) {
+#pragma unroll
+            for (int it = 0; it < MAXS; ++it)
+              if (tid + it * BK_NTH < PN / E16) dot16(rds[it], rst[it]);
+          } else {
+            const brsrc rdS = make_rsrc(dSg, (unsigned)PN * esz);
+            for (int idx = tid; idx < PN / E16; idx += BK_NTH)
+              dot16(bload16(rdS, (unsigned)idx * 16u), *(const u32x4*)((const char*)STs + bk_state_off<SWZ>(idx)));
           }
           part = wave_sum(part);
           if (lane == 0) red[w] = part;
@@ -464,12 +585,14 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
         }
         df[ss] = frag_make<T>(dv);
       }
+      if constexpr (CP && CN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < BK_TMAX; ++nt) {  // dC_k2^T += B^T . d_cb^T
         if (nt >= NT) continue;
 #pragma unroll
         for (int ss = 0; ss < 4; ++ss) mma(dCT[nt], bk_rowk<SWZ>(Bs, LDN, 16 * ss, 16 * nt, lane), df[ss]);
       }
+      if constexpr (CP && CN) bk_pipeline_reads<4 * CN / 16, 8>();
 
       if (sb == blk) {  // the head's row sums
         const float bw = sum4q(blue), ow = sum4q(orow);
