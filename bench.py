@@ -54,28 +54,35 @@ def algorithmic_bytes(w, elem=2, state_elem=2):
     return {"state_scans": scans, "chunk_grads": grads, "path": path}
 
 
-KERNEL_SOURCES = ("selective_state_space_vjp_amd/csrc/ssd_chunk.hip", "selective_state_space_vjp_amd/csrc/ssd_chunk16.hip",
-                  "selective_state_space_vjp_amd/csrc/ssd_blocked.hip", "selective_state_space_vjp_amd/csrc/ssd_common.cuh",
-                  "selective_state_space_vjp_amd/csrc/common.cuh")
+_CSRC = "selective_state_space_vjp_amd/csrc/"
+_COMMON = (_CSRC + "ssd_common.cuh", _CSRC + "common.cuh")
+# the sources each profiled kernel is built from (a counter summary is valid
+# for the kernel as long as these files are unchanged)
+KERNEL_SOURCES = {
+    "ssd_chunk16_kernel": (_CSRC + "ssd_chunk16.hip",) + _COMMON,
+    "ssd_chunk_bwd_kernel": (_CSRC + "ssd_chunk.hip",) + _COMMON,
+    "ssd_state_scan_kernel": (_CSRC + "ssd_chunk.hip",) + _COMMON,
+    "ssd_blocked_bwd_kernel": (_CSRC + "ssd_blocked.hip",) + _COMMON,
+}
 
 
-def sources_sha256(files=KERNEL_SOURCES):
-    """sha256 over the kernel sources, in order (identifies the kernels a counter run measured)."""
+def sources_sha256(kernel_name):
+    """sha256 over a kernel's sources, in order (identifies the kernel a counter run measured)."""
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES[kernel_name]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()
 
 
 def traffic_from_profile(kernel_name):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; None otherwise."""
+    on the kernel's current sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.json")
-    if not os.path.exists(path):
+    if kernel_name not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        if rec.get("sources_sha256") != sources_sha256():
+        if rec.get("sources_sha256") != sources_sha256(kernel_name):
             return None
         return float(rec["bytes_per_launch"])
     except Exception:
