@@ -212,15 +212,18 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
   // XCD-aware order: consecutive workgroups of one (batch, chunk, group) share
   // their input rows, so they are given ids that land on the same XCD (ids are
   // dealt to the 8 XCDs round robin)
+  // (32-bit unsigned arithmetic: the grid and its factors fit, and 64-bit
+  // division is a long scalar routine)
   unsigned id = blockIdx.x;
   if (gridDim.x % 8 == 0) id = (id % 8) * (gridDim.x / 8) + id / 8;
-  const int blk = (int)(id % nblk);
-  id /= nblk;
-  const int role = (int)(id % 2);  // 0 source block, 1 target block
-  id /= 2;
-  const i64 g = id % a.G;
-  id /= a.G;
-  const i64 c = id % a.nc, bi = id / a.nc;
+  const unsigned nblk32 = (unsigned)nblk, G32 = (unsigned)a.G, nc32 = (unsigned)a.nc;
+  const int blk = (int)(id % nblk32);
+  id /= nblk32;
+  const int role = (int)(id & 1u);  // 0 source block, 1 target block
+  id >>= 1;
+  const i64 g = (i64)(id % G32);
+  id /= G32;
+  const i64 c = (i64)(id % nc32), bi = (i64)(id / nc32);
   const i64 t0 = c * L;
   const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
   const int vrows = Lc * M;  // valid fused rows of this chunk
