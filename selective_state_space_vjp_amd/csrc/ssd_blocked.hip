@@ -216,14 +216,24 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
   // division is a long scalar routine)
   unsigned id = blockIdx.x;
   if (gridDim.x % 8 == 0) id = (id % 8) * (gridDim.x / 8) + id / 8;
-  const unsigned nblk32 = (unsigned)nblk, G32 = (unsigned)a.G, nc32 = (unsigned)a.nc;
-  const int blk = (int)(id % nblk32);
-  id /= nblk32;
+  // (a power-of-two factor is a shift and a mask)
+  auto divmod = [](unsigned& n, unsigned d) -> unsigned {
+    unsigned r;
+    if ((d & (d - 1u)) == 0u) {
+      r = n & (d - 1u);
+      n >>= __builtin_ctz(d);
+    } else {
+      const unsigned q = n / d;
+      r = n - q * d;
+      n = q;
+    }
+    return r;
+  };
+  const int blk = (int)divmod(id, (unsigned)nblk);
   const int role = (int)(id & 1u);  // 0 source block, 1 target block
   id >>= 1;
-  const i64 g = (i64)(id % G32);
-  id /= G32;
-  const i64 c = (i64)(id % nc32), bi = (i64)(id / nc32);
+  const i64 g = (i64)divmod(id, (unsigned)a.G);
+  const i64 c = (i64)divmod(id, (unsigned)a.nc), bi = (i64)id;
   const i64 t0 = c * L;
   const int Lc = (int)((a.T - t0) < L ? (a.T - t0) : L);
   const int vrows = Lc * M;  // valid fused rows of this chunk
