@@ -59,7 +59,8 @@ _COMMON = (_CSRC + "ssd_common.cuh", _CSRC + "common.cuh")
 # the sources each profiled kernel is built from (a counter summary is valid
 # for the kernel as long as these files are unchanged)
 KERNEL_SOURCES = {
-    "ssd_chunk16_kernel": (_CSRC + "ssd_chunk16.hip",) + _COMMON,
+    # (the build script too: it sets this file's scheduling strategy)
+    "ssd_chunk16_kernel": (_CSRC + "ssd_chunk16.hip",) + _COMMON + ("selective_state_space_vjp_amd/_build.py",),
     "ssd_chunk_bwd_kernel": (_CSRC + "ssd_chunk.hip",) + _COMMON,
     "ssd_state_scan_kernel": (_CSRC + "ssd_chunk.hip",) + _COMMON,
     "ssd_blocked_bwd_kernel": (_CSRC + "ssd_blocked.hip",) + _COMMON,
