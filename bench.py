@@ -6,6 +6,10 @@ chunk length 64, bf16 storage with float32 accumulation; seeded synthetic
 inputs already resident in HBM.  One step is one complete backward
 (ssd_chunk_bwd: both stages, every kernel) over the batch.
 
+Before the --warmup steps, the workload's steps run untimed for --settle-ms of
+wall time (default 100 ms), so that the timed steps see the GPU at its steady
+clocks rather than ramping up from idle.
+
 Prints one JSON line with the metric (tokens/s = b*T per second of wall time
 over exactly --steps steps, bracketed by device synchronisation), the
 roofline of the dominant kernel (algorithmic bytes per launch over its average
@@ -220,6 +224,7 @@ def bench_kda(args, dev):
     call = binding.DeltaCall(t["q"], t["k"], t["v"], t["beta"], t["g"], t["S0"], t["do"], None, scale=inp["scale"])
     del inp
     stages = (binding.DELTA_CKPT, binding.DELTA_BWD, binding.DELTA_REDUCE)
+    settle([lambda s=s: call.stage(s) for s in stages], args.settle_ms)
     for _ in range(args.warmup):
         for s in stages:
             call.stage(s)
@@ -268,6 +273,7 @@ def bench_kda(args, dev):
     line["seed"] = w["seed"]
     line["machine"] = machine_info()
     line["timing"] = "back-to-back steps (nothing between the library calls); warm infinity cache"
+    line["settle_ms"] = args.settle_ms
     if not args.no_cpu_baseline:
         line["cpu_baseline"], ref = kda_cpu_baseline(c, w)
         grp = w["HV"] // w["H"]
@@ -280,6 +286,24 @@ def bench_kda(args, dev):
 
 
 MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB infinity cache
+
+
+def settle(step_fns, ms):
+    """Run the workload's steps untimed for `ms` of wall time before the warm-up
+    steps.  An idle MI355X needs a few tens of milliseconds of load to reach its
+    steady clocks (measured: 20 timed steps after 5 warm-up steps from idle run
+    about 12 % slower than after 30 ms or more of settling, and no faster after
+    100 ms than after 30 ms), which the warm-up steps alone (about a millisecond
+    at the default workload) do not cover."""
+    import torch
+
+    if ms <= 0:
+        return
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        for f in step_fns:
+            f()
+        torch.cuda.synchronize()
 
 
 def cold_cache_steps(step_fns, n, dev):
@@ -333,6 +357,7 @@ def bench_fwd(args, dev):
     def step():
         binding.ssd_chunk_fwd(x, dt, A, B, C, s0, chunk_len=w["L"], out=out, workspace=ws)
 
+    settle([step], args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -374,6 +399,7 @@ def bench_fwd(args, dev):
     line["seed"] = w["seed"]
     line["machine"] = machine_info()
     line["timing"] = "back-to-back steps (nothing between the library calls); warm infinity cache"
+    line["settle_ms"] = args.settle_ms
     if not args.no_cpu_baseline:
         import oracle
 
@@ -393,6 +419,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps for this much wall time before the warm-up steps (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=("mamba2_chunk", "mimo_chunk", "kda", "mamba2_fwd", "mamba2_seq_small", "mamba1_seq"),
@@ -481,6 +509,7 @@ def main():
     else:
         grads_kernel = "ssd_chunk_bwd_kernel"
 
+    settle([call.states, call.grads], args.settle_ms)
     for _ in range(args.warmup):
         call.states()
         call.grads()
@@ -545,8 +574,10 @@ def main():
                           "note": "median per-step event times, infinity cache evicted before each step"}
     line["seed"] = w["seed"]
     line["machine"] = machine_info()
+    line["settle_ms"] = args.settle_ms
     line["timing"] = ("ms_per_step: wall clock over back-to-back steps (nothing between the library calls), "
-                      "warm infinity cache; cold_cache: every step after a 512 MiB write")
+                      "warm infinity cache, after settle_ms of untimed steps and the warm-up steps; "
+                      "cold_cache: every step after a 512 MiB write")
     if not args.no_cpu_baseline:
         line["cpu_baseline"], ref = cpu_baseline(c, w)
         line["rel_maxabs"] = {k: float(f"{rel_maxabs(v[:1].double().cpu().numpy(), ref[k]):.3e}")
@@ -570,6 +601,7 @@ def bench_seq(args, dev):
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(torch.float32).to(dev).contiguous()
          for k, v in c.items() if isinstance(v, np.ndarray)}
     call = binding.ScanCall(t["x"], t["dt"], t["A"], t["B"], t["C"], t["s0"], t["dy"], t["ds_final"])
+    settle([call.run], args.settle_ms)
     for _ in range(args.warmup):
         call.run()
     torch.cuda.synchronize()
@@ -590,7 +622,7 @@ def bench_seq(args, dev):
         "roofline": None,
         "roofline_note": "latency-bound correctness configuration (a few thousand tokens): no roofline claim",
         "seed": w["seed"], "machine": machine_info(),
-        "timing": "back-to-back steps (nothing between the library calls)",
+        "timing": "back-to-back steps (nothing between the library calls)", "settle_ms": args.settle_ms,
     }
     if not args.no_cpu_baseline:
         import oracle
