@@ -24,13 +24,49 @@
 //                         ORANGE d_v = dy^T w, dx, the K3 decay and dvx row sums.
 // The per-head step scalars (cumA, delta and the per-step decay factors) sit in
 // LDS so that per-element values are LDS reads rather than lane shuffles.  The
-// next head's rows and states, prefetched into registers one head ahead, are
-// written to LDS during phase B (x, dy, dS_{c+1} double buffered by head
-// parity, S_c in place): two barriers per head.
+// next head's x and dy rows and dS_{c+1} go straight from memory into the LDS
+// buffers of the other head parity (LDS-direct loads issued at the start of a
+// head); its S_c and step scalars come through registers and are written to
+// LDS during phase B (S_c in place): two barriers per head.
 #include "ssd_common.cuh"
 
 namespace ssmvjp {
 namespace {
+
+typedef __attribute__((address_space(3))) char lds_char;
+// raw buffer resource words (the form make_rsrc builds), made wave-uniform so
+// that they sit in scalar registers
+__device__ __forceinline__ u32x4 rsrc_words_u(const void* base, unsigned bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4 r;
+  r[0] = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)p);
+  r[1] = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(p >> 32)) & 0xffffu;
+  r[2] = (unsigned)__builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+// LDS-direct loads (each lane's 4 or 16 bytes written to LDS at M0 + the
+// lane's slot), issued as assembly: the compiler neither counts them nor, as
+// it does for its own LDS-direct loads, waits for every outstanding load
+// before the next transposed LDS read.  The caller waits with vmcnt before the
+// barrier that publishes the data.  M0 is named as clobbered; the compiler
+// uses it for nothing else in this file (it keeps no value there across these
+// statements), so its warning about clobbering a reserved register is muted.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_dword(unsigned lds_addr, unsigned off, u32x4 rs) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_dwordx4(unsigned lds_addr, unsigned off, u32x4 rs) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 constexpr int W16 = 16;          // waves per workgroup
 constexpr int NTH16 = 64 * W16;
@@ -42,7 +78,10 @@ constexpr int LDC = LM16 + 4;             // CB pitch (float)
 // banks, so the fragment reads along a row (16 lanes, 8 bytes each, one per
 // row) hit 32 distinct banks
 constexpr int LDN = N16 + 4;              // B / C pitch (bf16)
-constexpr int LDP = P16 + 4;              // x / dy pitch (bf16)
+// x / dy rows: unpadded, each 8-byte unit u of a row stored at u ^ f(row)
+// (xsw_off), which keeps the fragment reads along the rows and the transposed
+// ones on distinct banks and lets LDS-direct loads place any 8-byte unit
+constexpr int LDP = P16;
 constexpr int PN = P16 * N16;
 
 // partial row sums of one head (float offsets inside one set)
@@ -170,28 +209,54 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     st16_as8(Cs + r * LDN + col, bload16(rc_, (unsigned)(r * brs + col) * 2));
   }
 
-  // ---- register prefetch of one head: step scalars, A, x or dy rows, S_c and dS_{c+1} ----
-  // threads 0..511 stage x, 512..1023 dy (one 16-byte chunk each); every
-  // thread stages one chunk of S_c and one of dS_{c+1}
-  u32x4 rxy, rs, rd;
+  // ---- loads of one head ----
+  // The step scalars, A and S_c go through registers (S_c is staged in place
+  // during phase B, one 16-byte chunk per thread).  The x and dy rows and
+  // dS_{c+1} go straight from memory into LDS (LDS-direct loads into the
+  // buffers of the head's parity, free since the barrier before): waves 0..7
+  // load x, waves 8..15 dy, 4-byte units, four 256-byte wave loads each; every
+  // wave one 1 KiB block of dS_{c+1}.  Rows past the sequence read zeros (the
+  // resource covers the valid rows only).
+  u32x4 rs;
   ChunkScalars rcs = {0.f, 0.f, 0.f, 0.f};
   float rA = 0.0f;
   const i64 hbase = g * a.hpg + hs * a.hph;
   const unsigned xbytes = (unsigned)(((i64)(Lc - 1) * xrs + P16) * 2);
   const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));
-  const int xy_sel = tid >> 9, xy_idx = tid & 511, xy_r = xy_idx >> 3, xy_col = (xy_idx & 7) * 8;
-  auto issue = [&](i64 h) {
+  const int xy_sel = w >> 3, xw = w & 7;  // x or dy, and this wave's quarter of the rows
+  // source byte offset (in the head's rows) of this lane's 4 bytes for wave load i:
+  // LDS dword D = (4 xw + i) * 64 + lane of the row-major buffer, row D / 32, stored
+  // 8-byte unit (D % 32) / 2 = logical unit ^ f(row), half D % 2
+  unsigned xy_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (4 * xw + i) * 2 + (lane >> 5), e = lane & 31;
+    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+    const int u = (e >> 1) ^ f;
+    xy_off[i] = (unsigned)(row * xrs + 4 * u + 2 * (e & 1)) * 2u;
+  }
+  // dS_{c+1}: LDS 16-byte unit v = lane % 32 of tile 2w + lane / 32 holds the
+  // tile's unit u with the same quarter, rotated back by two units per quarter
+  const int dsv = lane & 31;
+  const unsigned ds_off = (unsigned)((2 * w + (lane >> 5)) * 512 + 16 * ((dsv & 24) | (((dsv & 7) - 2 * (dsv >> 3)) & 7)));
+  auto issue_regs = [&](i64 h) {
     rcs = issue_scalars(a, bi, c, h, lane);
     rA = bload_f32(rsA, (unsigned)(h * 4));
-    const brsrc bxy = make_rsrc((xy_sel ? dyg : xg) + (int)h * P16, xbytes);
-    rxy = bload16(bxy, (unsigned)(xy_r * xrs + xy_col) * 2);
     const i64 so = ((bi * a.nc + c) * a.H + h) * (i64)PN;
     rs = bload16(make_rsrc((const bf16*)a.S + so, PN * 2), (unsigned)tid * 16u);
-    rd = bload16(make_rsrc((const bf16*)a.dS + so, PN * 2), (unsigned)tid * 16u);
   };
-  issue(hbase);
-  // each head issues the next head's loads, then the d_dt (and dA) stores and one dx store
-  vmem_pad_stores<DA ? 3 : 2>(make_rsrc(a.dxv, 0u));
+  const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(lds_char*)smem_raw);
+  auto issue_lds = [&](i64 h, int k) {
+    const u32x4 wxy = rsrc_words_u((xy_sel ? dyg : xg) + (int)h * P16, xbytes);
+    const unsigned dxy = lds0 + (unsigned)(xy_sel ? L_DY : L_X) + (unsigned)(k * LM16 * LDP + 4 * xw * 128) * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_dword((unsigned)__builtin_amdgcn_readfirstlane((int)(dxy + 256u * i)), xy_off[i], wxy);
+    const i64 so = ((bi * a.nc + c) * a.H + h) * (i64)PN;
+    dma_dwordx4((unsigned)__builtin_amdgcn_readfirstlane((int)(lds0 + (unsigned)L_DS + (unsigned)(k * PN + w * 512) * 2u)),
+                ds_off, rsrc_words_u((const bf16*)a.dS + so, PN * 2));
+  };
+  issue_regs(hbase);
+  issue_lds(hbase, 0);
   __syncthreads();  // B, C staged
 
   // ---- C.B^T (K2 recompute) on the lower-triangular tile pairs, waves 0..9 ----
@@ -268,9 +333,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   auto stage = [&](int k) {
     ncs = finish_scalars(rcs);
     nA = rA;
-    st16_as8((xy_sel ? dysb : xsb) + k * LM16 * LDP + xy_r * LDP + xy_col, rxy);
     *(u32x4*)((char*)Ss + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rs;
-    *(u32x4*)((char*)(dSsb + k * PN) + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rd;
     if (w == 0) {  // per step r: cumA, delta, e^cumA (BLUE), delta e^(end-cumA) (K3), e^(end-cumA)
       float* sc = scb + k * SC_N * 64;
       const float edec = exp_hw(ncs.end - ncs.cum);
@@ -282,8 +345,6 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     }
   };
   stage(0);
-  issue(a.hph > 1 ? hbase + 1 : hbase);
-  vmem_pad_stores<1>(make_rsrc(a.dxv, 0u));  // as a head's dx store after its refill
 
   for (i64 hh = 0; hh < a.hph; ++hh) {
     const i64 h = hbase + hh;
@@ -301,7 +362,16 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     const bf16* dys = dysb + k * LM16 * LDP;
     const bf16* dSs = dSsb + k * PN;
 
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-direct loads have landed
     __syncthreads();  // this head staged; the previous head's phase B done (and CB on entry)
+
+    // the next head's loads (unconditional: past the last head the last head is
+    // reloaded into buffers never read again)
+    {
+      const i64 hn = hh + 1 < a.hph ? h + 1 : hbase + a.hph - 1;
+      issue_regs(hn);
+      issue_lds(hn, k ^ 1);
+    }
 
     // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
     {
@@ -316,7 +386,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < PT; ++kb)
-        mma(acc, ld_colk(dys, LDP, 16 * prt, 16 * kb, lane), ld_colk(xs, LDP, 16 * prs, 16 * kb, lane));
+        mma(acc, ld_colk_xs(dys, LDP, 16 * prt, 16 * kb, lane), ld_colk_xs(xs, LDP, 16 * prs, 16 * kb, lane));
       const int s_ = 16 * prs + r16;
       const float cs_s = cumL[s_], dls = delL[s_];
       const f32x4 ct = *(const f32x4*)(cumL + 16 * prt + 4 * q);  // rows t = 16 prt + 4q + j
@@ -359,7 +429,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         const Frag<bf16> fa = ld_ntv_s(opA + tile_off(kb, nt_own), lane);
         Frag<bf16> fb[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) fb[rb] = ld_colk(opB, LDP, 16 * rb, 16 * kb, lane);
+        for (int rb = 0; rb < RB; ++rb) fb[rb] = ld_colk_xs(opB, LDP, 16 * rb, 16 * kb, lane);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mma(acc[rb], fa, fb[rb]);
         if (!blue) {  // d_end partial: S_c (.) dS_{c+1} over this n tile
@@ -398,11 +468,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
     __syncthreads();  // w tiles complete; Ss free
 
-    // the next head into the other buffers and Ss, then the refill with the
-    // head after it (unconditional: past the last head the last head's rows
-    // are reloaded and staged, into buffers never read again)
+    // the next head's S_c into Ss (read in phase A only) and its step values
     stage(k ^ 1);
-    issue(hh + 2 < a.hph ? h + 2 : hbase + a.hph - 1);
 
     // ---- phase B: K3 d_dv^T = dS_{c+1} . B^T and ORANGE d_v_or^T = dy^T . w for
     // the item (p tile ipt, row block irb); dx; K3 decay and dvx row sums ----
@@ -426,7 +493,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < RB; ++kb) {
           if (kb < irb) continue;
-          f5a[kb] = ld_rowk(dys, LDP, 16 * kb, 16 * ipt, lane);
+          f5a[kb] = ld_rowk_xs(dys, LDP, 16 * kb, 16 * ipt, lane);
           f5b[kb] = ld_ntv(Wt + pair_of(kb, irb) * 256, lane);
         }
 #pragma unroll
@@ -439,7 +506,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       const float dl = delL[r];
       const float edec = edl[r];
       float xv[4];
-      frag_get(ld_colk(xs, LDP, 16 * irb, 16 * ipt, lane), xv);  // x[r][p .. p+3], p = 16 pt + 4q
+      frag_get(ld_colk_xs(xs, LDP, 16 * irb, 16 * ipt, lane), xv);  // x[r][p .. p+3], p = 16 pt + 4q
       float dvo[4], s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -462,6 +529,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     prev_cs = cs;
     prev_Ah = Ah;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no LDS-direct load outstanding past the loop
   __syncthreads();  // the last head's partial sums complete
   if (a.hph > 0) {
     const bool on = w == (int)((a.hph - 1) & 3);
