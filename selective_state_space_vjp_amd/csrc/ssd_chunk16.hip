@@ -26,8 +26,9 @@
 // LDS so that per-element values are LDS reads rather than lane shuffles.  The
 // next head's x and dy rows and dS_{c+1} go straight from memory into the LDS
 // buffers of the other head parity (LDS-direct loads issued at the start of a
-// head); its S_c and step scalars come through registers and are written to
-// LDS during phase B (S_c in place): two barriers per head.
+// head); its S_c goes into Ss the same way once phase A's readers of Ss are
+// past the second barrier, and its step scalars come through registers and
+// are written to LDS during phase B: two barriers per head.
 #include "ssd_common.cuh"
 
 namespace ssmvjp {
@@ -217,7 +218,6 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   // load x, waves 8..15 dy, 4-byte units, four 256-byte wave loads each; every
   // wave one 1 KiB block of dS_{c+1}.  Rows past the sequence read zeros (the
   // resource covers the valid rows only).
-  u32x4 rs;
   ChunkScalars rcs = {0.f, 0.f, 0.f, 0.f};
   float rA = 0.0f;
   const i64 hbase = g * a.hpg + hs * a.hph;
@@ -242,8 +242,6 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   auto issue_regs = [&](i64 h) {
     rcs = issue_scalars(a, bi, c, h, lane);
     rA = bload_f32(rsA, (unsigned)(h * 4));
-    const i64 so = ((bi * a.nc + c) * a.H + h) * (i64)PN;
-    rs = bload16(make_rsrc((const bf16*)a.S + so, PN * 2), (unsigned)tid * 16u);
   };
   const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(lds_char*)smem_raw);
   auto issue_lds = [&](i64 h, int k) {
@@ -255,8 +253,15 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     dma_dwordx4((unsigned)__builtin_amdgcn_readfirstlane((int)(lds0 + (unsigned)L_DS + (unsigned)(k * PN + w * 512) * 2u)),
                 ds_off, rsrc_words_u((const bf16*)a.dS + so, PN * 2));
   };
+  // S_c of head h into Ss by LDS-direct loads (the layout of the dS_{c+1} tiles)
+  auto issue_s = [&](i64 h) {
+    const i64 so = ((bi * a.nc + c) * a.H + h) * (i64)PN;
+    dma_dwordx4((unsigned)__builtin_amdgcn_readfirstlane((int)(lds0 + (unsigned)L_S + (unsigned)(w * 512) * 2u)),
+                ds_off, rsrc_words_u((const bf16*)a.S + so, PN * 2));
+  };
   issue_regs(hbase);
   issue_lds(hbase, 0);
+  issue_s(hbase);
   __syncthreads();  // B, C staged
 
   // ---- C.B^T (K2 recompute) on the lower-triangular tile pairs, waves 0..9 ----
@@ -326,14 +331,13 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
   float prev_Ah = 0.0f;
 
-  // the prefetched head into the buffers of parity k (x, dy, dS_{c+1}, step
-  // scalars) and into Ss; returns its step scalars
+  // the prefetched head's step scalars into the buffers of parity k (its x,
+  // dy, dS_{c+1} and S_c arrive by LDS-direct loads)
   ChunkScalars ncs = {0.f, 0.f, 0.f, 0.f};
   float nA = 0.0f;
   auto stage = [&](int k) {
     ncs = finish_scalars(rcs);
     nA = rA;
-    *(u32x4*)((char*)Ss + (tid >> 5) * 512 + swz((tid & 31) * 16)) = rs;
     if (w == 0) {  // per step r: cumA, delta, e^cumA (BLUE), delta e^(end-cumA) (K3), e^(end-cumA)
       float* sc = scb + k * SC_N * 64;
       const float edec = exp_hw(ncs.end - ncs.cum);
@@ -468,8 +472,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
     __syncthreads();  // w tiles complete; Ss free
 
-    // the next head's S_c into Ss (read in phase A only) and its step values
+    // the next head's step values, and its S_c into Ss (read in phase A only)
     stage(k ^ 1);
+    issue_s(hh + 1 < a.hph ? h + 1 : hbase + a.hph - 1);
 
     // ---- phase B: K3 d_dv^T = dS_{c+1} . B^T and ORANGE d_v_or^T = dy^T . w for
     // the item (p tile ipt, row block irb); dx; K3 decay and dvx row sums ----
