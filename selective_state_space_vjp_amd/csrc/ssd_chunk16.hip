@@ -22,13 +22,15 @@
 //                         K1 suffix sum and d_dt.
 //   phase B  wave w       item (p tile w/4, row block w%4): K3 d_v = dS B^T and
 //                         ORANGE d_v = dy^T w, dx, the K3 decay and dvx row sums.
-// The per-head step scalars (cumA, delta and the per-step decay factors) sit in
-// LDS so that per-element values are LDS reads rather than lane shuffles.  The
-// next head's x and dy rows and dS_{c+1} go straight from memory into the LDS
+// The per-head step scalars (cumA, delta, the per-step decay factors, sigma(dt)
+// and A) sit in LDS so that per-element values are LDS reads rather than lane
+// shuffles, and the d_cumA assembly reads them there a head later.  The next
+// head's x and dy rows and dS_{c+1} go straight from memory into the LDS
 // buffers of the other head parity (LDS-direct loads issued at the start of a
 // head); its S_c goes into Ss the same way once phase A's readers of Ss are
-// past the second barrier, and its step scalars come through registers and
-// are written to LDS during phase B: two barriers per head.
+// past the second barrier, and wave 0 loads its step scalars into registers
+// and writes them, with the factors, to LDS during phase B: two barriers per
+// head.
 #include "ssd_common.cuh"
 
 namespace ssmvjp {
@@ -100,7 +102,7 @@ constexpr int L_PB = L_CB + LM16 * LDC * 4;              // float [2][PB_SET]
 // x, dy, dS_{c+1} and the step scalars are double buffered by head parity: the
 // next head is staged during phase B of the current one, which reads them;
 // S_c, read only in phase A, is staged in place during phase B
-constexpr int SC_N = 5;                                  // per-step values: cumA, delta, and the factors below
+constexpr int SC_N = 7;                                  // per-step values: cumA, delta, the factors below, sigma(dt); A
 constexpr int L_SC = L_PB + 2 * PB_SET * 4;              // float [2][SC_N][64], by head parity
 constexpr int L_B = L_SC + 2 * SC_N * 64 * 4;            // bf16 [64][LDN]
 constexpr int L_C = L_B + LM16 * LDN * 2;                // bf16 [64][LDN]
@@ -135,6 +137,15 @@ __device__ __forceinline__ void st16_as8(bf16* p, const u32x4& u) {
   *(u32x2*)(p + 4) = hi;
 }
 __device__ __forceinline__ int tile_off(int pt, int nt) { return (pt * NT + nt) * 256; }
+// sum of the four products of two bf16 quadruples, added to c (two packed
+// bf16 dot products accumulated in float)
+__device__ __forceinline__ float dot2_bf16(s16x4 x, s16x4 y, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, y0 = {y[0], y[1]}, y1 = {y[2], y[3]};
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x0), __builtin_bit_cast(bf16x2, y0), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x1), __builtin_bit_cast(bf16x2, y1), c, false);
+}
 
 // The four sums of x[0..3] over the 4 rows of 16 lanes (lanes with the same
 // lane % 16) at once: two row-pair swaps (odd rows of the first operand with
@@ -211,8 +222,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   }
 
   // ---- loads of one head ----
-  // The step scalars, A and S_c go through registers (S_c is staged in place
-  // during phase B, one 16-byte chunk per thread).  The x and dy rows and
+  // Wave 0 loads the step scalars and A into registers.  The x and dy rows and
   // dS_{c+1} go straight from memory into LDS (LDS-direct loads into the
   // buffers of the head's parity, free since the barrier before): waves 0..7
   // load x, waves 8..15 dy, 4-byte units, four 256-byte wave loads each; every
@@ -240,8 +250,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   const int dsv = lane & 31;
   const unsigned ds_off = (unsigned)((2 * w + (lane >> 5)) * 512 + 16 * ((dsv & 24) | (((dsv & 7) - 2 * (dsv >> 3)) & 7)));
   auto issue_regs = [&](i64 h) {
-    rcs = issue_scalars(a, bi, c, h, lane);
-    rA = bload_f32(rsA, (unsigned)(h * 4));
+    if (w == 0) {
+      rcs = issue_scalars(a, bi, c, h, lane);
+      rA = bload_f32(rsA, (unsigned)(h * 4));
+    }
   };
   const unsigned lds0 = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(lds_char*)smem_raw);
   auto issue_lds = [&](i64 h, int k) {
@@ -295,7 +307,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   // d_da) for one head, from the partial sums in pb; lane = step.  Also the
   // head's dA partial sum over the chunk, sum_l d_da_l * delta_l (the same in
   // every lane).
-  auto epilogue = [&](const ChunkScalars& cs, float Ah, const float* pb) -> float2 {
+  auto epilogue = [&](const float* sc, const float* pb) -> float2 {
+    const float cum = sc[lane], end = sc[63], Ah = sc[384];
     float dc = 0.0f, qv = 0.0f, dvx = 0.0f;
     if (lane < LM16) {
       const int rbl = lane >> 4, rl = lane & 15;
@@ -309,36 +322,31 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         dec += pb[PB_DEC + k * 64 + lane];
         dvx += pb[PB_DVX + k * 64 + lane];
       }
-      qv = dec * exp_hw(cs.end - cs.cum);
+      qv = dec * exp_hw(end - cum);
       dc = bl + orow - ocol - qv;
     }
     const float qsum = wave_sum(qv);
     float dendt = 0.0f;
 #pragma unroll
     for (int k = 0; k < NT; ++k) dendt += pb[PB_DEND + k];
-    dendt *= exp_hw(cs.end);
+    dendt *= exp_hw(end);
     if (lane == Lc - 1) dc += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
     const float dda = wave_incl_suffix(lane < Lc ? dc : 0.0f, lane);
-    return make_float2(a.raw ? dda : (dvx + dda * Ah) * cs.sig, DA ? wave_sum(dda * cs.delta) : 0.0f);
+    return make_float2(a.raw ? dda : (dvx + dda * Ah) * sc[320 + lane], DA ? wave_sum(dda * sc[64 + lane]) : 0.0f);
   };
   const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
-  // every wave stores (dropped unless `on`): no store sits in a branch
+  // waves 0..3 store (dropped unless `on`)
   auto epi_store = [&](bool on, i64 h, float2 v) {
     bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v.x);
     if constexpr (DA) bstore_f32(dA_rsrc(a, bi, c), on && lane == 0 ? (unsigned)(h * 4) : BUF_OOB, v.y);
   };
   i64 prev_h = 0;
-  ChunkScalars prev_cs = {0.f, 0.f, 0.f, 0.f};
-  float prev_Ah = 0.0f;
 
   // the prefetched head's step scalars into the buffers of parity k (its x,
   // dy, dS_{c+1} and S_c arrive by LDS-direct loads)
-  ChunkScalars ncs = {0.f, 0.f, 0.f, 0.f};
-  float nA = 0.0f;
   auto stage = [&](int k) {
-    ncs = finish_scalars(rcs);
-    nA = rA;
-    if (w == 0) {  // per step r: cumA, delta, e^cumA (BLUE), delta e^(end-cumA) (K3), e^(end-cumA)
+    if (w == 0) {
+      const ChunkScalars ncs = finish_scalars(rcs);  // per step r: cumA, delta, e^cumA (BLUE), delta e^(end-cumA) (K3), e^(end-cumA)
       float* sc = scb + k * SC_N * 64;
       const float edec = exp_hw(ncs.end - ncs.cum);
       sc[lane] = ncs.cum;
@@ -346,6 +354,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       sc[128 + lane] = exp_hw(ncs.cum);
       sc[192 + lane] = ncs.delta * edec;
       sc[256 + lane] = edec;
+      sc[320 + lane] = ncs.sig;
+      sc[384 + lane] = rA;
     }
   };
   stage(0);
@@ -354,8 +364,6 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     const i64 h = hbase + hh;
     const int k = (int)(hh & 1);
     float* pb = pbase + k * PB_SET;
-    const ChunkScalars cs = ncs;
-    const float Ah = nA;
     const brsrc bdx = make_rsrc(dxg + (int)h * P16, xbytes);
     const float* cumL = scb + k * SC_N * 64;
     const float* delL = cumL + 64;
@@ -381,8 +389,8 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     {
       const bool on = hh > 0 && w == (int)((hh - 1) & 3);
       float2 v = make_float2(0.0f, 0.0f);
-      if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((hh - 1) & 1) * PB_SET);
-      epi_store(on, prev_h, v);
+      if (on) v = epilogue(scb + ((hh - 1) & 1) * SC_N * 64, pbase + ((hh - 1) & 1) * PB_SET);
+      if (w < 4) epi_store(on, prev_h, v);
     }
 
     // ---- phase A (1): ORANGE on this wave's tile pair ----
@@ -436,12 +444,9 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
         for (int rb = 0; rb < RB; ++rb) fb[rb] = ld_colk_xs(opB, LDP, 16 * rb, 16 * kb, lane);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mma(acc[rb], fa, fb[rb]);
-        if (!blue) {  // d_end partial: S_c (.) dS_{c+1} over this n tile
-          float vS[4], vdS[4];
-          frag_get(ld_ntv_s(Ss + tile_off(kb, nt_own), lane), vS);
-          frag_get(fa, vdS);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dend = fmaf(vS[j], vdS[j], dend);
+        if (!blue) {  // d_end partial: S_c (.) dS_{c+1} over this n tile, two bf16 products per step
+          const Frag<bf16> fs = ld_ntv_s(Ss + tile_off(kb, nt_own), lane);
+          dend = dot2_bf16(fs.v, fa.v, dend);
         }
       }
       if (blue) {
@@ -452,22 +457,20 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
           frag_get(ld_colk(Cs, LDN, 16 * rb, 16 * nt_own, lane), cv);  // C[r][n .. n+3], n = 16 nt + 4q
           float s = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
-            s = fmaf(cv[j], acc[rb][j], s);
-          }
+          for (int j = 0; j < 4; ++j) s = fmaf(cv[j], acc[rb][j], s);
           bsum[rb] = s * fcol[rb];
         }
         // row q of lanes: the sum over the n tile for row block q
         pb[PB_BLUE + nt_own * 64 + 16 * q + r16] = sum4q_x4(bsum);
       } else {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
         dend = wave_sum(dend);
         if (lane == 0) pb[PB_DEND + nt_own] = dend;
       }
+      // both roles: the product scaled by the column factor, summed over heads
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xacc[rb][j] = fmaf(acc[rb][j], fcol[rb], xacc[rb][j]);
     }
 
     __syncthreads();  // w tiles complete; Ss free
@@ -531,15 +534,13 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       }
     }
     prev_h = h;
-    prev_cs = cs;
-    prev_Ah = Ah;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no LDS-direct load outstanding past the loop
   __syncthreads();  // the last head's partial sums complete
   if (a.hph > 0) {
     const bool on = w == (int)((a.hph - 1) & 3);
     float2 v = make_float2(0.0f, 0.0f);
-    if (on) v = epilogue(prev_cs, prev_Ah, pbase + ((a.hph - 1) & 1) * PB_SET);
+    if (on) v = epilogue(scb + ((a.hph - 1) & 1) * SC_N * 64, pbase + ((a.hph - 1) & 1) * PB_SET);
     epi_store(on, prev_h, v);
   }
 
