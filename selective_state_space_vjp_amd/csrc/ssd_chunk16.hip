@@ -177,8 +177,9 @@ __device__ __forceinline__ float sum16x4(const float v[4], int r16) {
 }
 
 // DA: also the per-chunk dA partial sums (a separate instantiation, so that
-// the plain backward keeps its registers)
-template <bool DA>
+// the plain backward keeps its registers); RAW: the raw-decay form (delta = 1,
+// d_da out), the selective form otherwise
+template <bool DA, bool RAW>
 __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* CBs = (float*)(smem_raw + L_CB);
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   float rA = 0.0f;
   const i64 hbase = g * a.hpg + hs * a.hph;
   const unsigned xbytes = (unsigned)(((i64)(Lc - 1) * xrs + P16) * 2);
-  const brsrc rsA = make_rsrc(a.A, a.raw ? 0u : (unsigned)(a.H * 4));
+  const brsrc rsA = make_rsrc(a.A, RAW ? 0u : (unsigned)(a.H * 4));
   const int xy_sel = w >> 3, xw = w & 7;  // x or dy, and this wave's quarter of the rows
   // source byte offset (in the head's rows) of this lane's 4 bytes for wave load i:
   // LDS dword D = (4 xw + i) * 64 + lane of the row-major buffer, row D / 32, stored
@@ -332,7 +333,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     dendt *= exp_hw(end);
     if (lane == Lc - 1) dc += qsum + dendt;  // K3 d cumA_last and K4 d da_chunk_end
     const float dda = wave_incl_suffix(lane < Lc ? dc : 0.0f, lane);
-    return make_float2(a.raw ? dda : (dvx + dda * Ah) * sc[320 + lane], DA ? wave_sum(dda * sc[64 + lane]) : 0.0f);
+    return make_float2(RAW ? dda : (dvx + dda * Ah) * sc[320 + lane], DA ? wave_sum(dda * sc[64 + lane]) : 0.0f);
   };
   const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
   // waves 0..3 store (dropped unless `on`)
@@ -519,7 +520,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float dv = fmaf(acc3[j], edec, acc5[j]);  // d_v = d_v_k3 + d_v_orange
-        dvo[j] = a.raw ? dv : dv * dl;
+        dvo[j] = RAW ? dv : dv * dl;
         s1 = fmaf(acc3[j], xv[j], s1);  // d_decay / delta = sum_p d_decayed_v . x
         s2 = fmaf(dv, xv[j], s2);
       }
@@ -577,10 +578,12 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
 void launch_ssd_chunk16(const SsdArgs& a, hipStream_t stream) {
   const i64 grid = a.b * a.nc * a.G * a.hsplit;
-  if (a.dA_part)
-    hipLaunchKernelGGL(ssd_chunk16_kernel<true>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+  if (a.raw)  // no dA in the raw-decay form
+    hipLaunchKernelGGL((ssd_chunk16_kernel<false, true>), dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+  else if (a.dA_part)
+    hipLaunchKernelGGL((ssd_chunk16_kernel<true, false>), dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
   else
-    hipLaunchKernelGGL(ssd_chunk16_kernel<false>, dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
+    hipLaunchKernelGGL((ssd_chunk16_kernel<false, false>), dim3((unsigned)grid), dim3(NTH16), L_TOTAL, stream, a);
 }
 
 }  // namespace ssmvjp
