@@ -15,10 +15,10 @@
 //                         dC += dC_blue, the BLUE d_cumA row sums;
 //            waves 8..15  K3: dB_k3^T for n tile w-8 (dS^T . (x delta e^(end-cumA))^T),
 //                         dB += dB_k3, the d_end partial sum of S_c (.) dS_{c+1};
-//            waves 15..6  one ORANGE (t, s) tile pair each (10 pairs): G1 = dy x^T,
+//            waves 15..8, 4, 5  one ORANGE (t, s) tile pair each (10 pairs): G1 = dy x^T,
 //                         d_cb (summed over heads), masked w = CB * decay, the
 //                         ORANGE d_cumA row and column sums;
-//            one of waves 0..3 (rotating) assembles the previous head's d_cumA,
+//            wave 2 or 3 (alternating) assembles the previous head's d_cumA,
 //                         K1 suffix sum and d_dt.
 //   phase B  wave w       item (p tile w/4, row block w%4): K3 d_v = dS B^T and
 //                         ORANGE d_v = dy^T w, dx, the K3 decay and dvx row sums.
@@ -293,8 +293,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   // ---- fixed roles ----
   const bool blue = w < NT;             // phase A product: BLUE (dC) or K3 (dB)
   const int nt_own = blue ? w : w - NT;
-  const int pair = W16 - 1 - w;          // ORANGE pair of waves 15..6
-  const bool has_pair = pair >= 0 && pair < NPAIR;
+  // ORANGE pairs: waves 15..8 and 4, 5, so that each SIMD (waves w % 4) holds
+  // two or three pairs, the SIMDs with two also taking the d_cumA assembly
+  const int pair = w >= 8 ? W16 - 1 - w : (w == 4 || w == 5) ? w + 4 : -1;
+  const bool has_pair = pair >= 0;
   int prt = 0;
   while (has_pair && (prt + 1) * (prt + 2) / 2 <= pair) ++prt;
   const int prs = has_pair ? pair - prt * (prt + 1) / 2 : 0;
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     return make_float2(RAW ? dda : (dvx + dda * Ah) * sc[320 + lane], DA ? wave_sum(dda * sc[64 + lane]) : 0.0f);
   };
   const brsrc bddt = make_rsrc(ddtg, (unsigned)(Lc * a.H * 4));
-  // waves 0..3 store (dropped unless `on`)
+  // waves 2 and 3 store (dropped unless `on`)
   auto epi_store = [&](bool on, i64 h, float2 v) {
     bstore_f32(bddt, on && lane < Lc ? (unsigned)((lane * a.H + h) * 4) : BUF_OOB, v.x);
     if constexpr (DA) bstore_f32(dA_rsrc(a, bi, c), on && lane == 0 ? (unsigned)(h * 4) : BUF_OOB, v.y);
@@ -388,10 +390,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
     // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
     {
-      const bool on = hh > 0 && w == (int)((hh - 1) & 3);
+      const bool on = hh > 0 && w == 2 + (int)((hh - 1) & 1);
       float2 v = make_float2(0.0f, 0.0f);
       if (on) v = epilogue(scb + ((hh - 1) & 1) * SC_N * 64, pbase + ((hh - 1) & 1) * PB_SET);
-      if (w < 4) epi_store(on, prev_h, v);
+      if ((w >> 1) == 1) epi_store(on, prev_h, v);
     }
 
     // ---- phase A (1): ORANGE on this wave's tile pair ----
@@ -539,7 +541,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no LDS-direct load outstanding past the loop
   __syncthreads();  // the last head's partial sums complete
   if (a.hph > 0) {
-    const bool on = w == (int)((a.hph - 1) & 3);
+    const bool on = w == 2 + (int)((a.hph - 1) & 1);
     float2 v = make_float2(0.0f, 0.0f);
     if (on) v = epilogue(scb + ((a.hph - 1) & 1) * SC_N * 64, pbase + ((a.hph - 1) & 1) * PB_SET);
     epi_store(on, prev_h, v);
