@@ -26,8 +26,8 @@
 // and A) sit in LDS so that per-element values are LDS reads rather than lane
 // shuffles, and the d_cumA assembly reads them there a head later.  The next
 // head's x and dy rows and dS_{c+1} go straight from memory into the LDS
-// buffers of the other head parity (LDS-direct loads issued at the start of a
-// head); its S_c goes into Ss the same way once phase A's readers of Ss are
+// buffers of the other head parity (LDS-direct loads issued in phase A, after
+// the ORANGE products); its S_c goes into Ss the same way once phase A's readers of Ss are
 // past the second barrier, and wave 0 loads its step scalars into registers
 // and writes them, with the factors, to LDS during phase B: two barriers per
 // head.
@@ -380,13 +380,10 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-direct loads have landed
     __syncthreads();  // this head staged; the previous head's phase B done (and CB on entry)
 
-    // the next head's loads (unconditional: past the last head the last head is
+    // the next head (unconditional: past the last head the last head is
     // reloaded into buffers never read again)
-    {
-      const i64 hn = hh + 1 < a.hph ? h + 1 : hbase + a.hph - 1;
-      issue_regs(hn);
-      issue_lds(hn, k ^ 1);
-    }
+    const i64 hn = hh + 1 < a.hph ? h + 1 : hbase + a.hph - 1;
+    issue_regs(hn);
 
     // the previous head's partial sums are complete: its d_cumA on one of waves 0..3
     {
@@ -424,6 +421,11 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
       if ((r16 & 3) == 0) pb[PB_OROW + pair * 16 + 4 * q + (r16 >> 2)] = osum;
       if (q == 0) pb[PB_OCOL + pair * 16 + r16] = ocol;
     }
+
+    // the next head's x, dy and dS_{c+1}, issued after the ORANGE products: at
+    // the head's start the waves' loads would queue behind one another and hold
+    // the ORANGE waves back
+    issue_lds(hn, k ^ 1);
 
     // ---- phase A (2): BLUE (dC) or K3 (dB) on this wave's n tile, computed
     // transposed (rows n, columns the chunk's rows r) ----
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
 
     // the next head's step values, and its S_c into Ss (read in phase A only)
     stage(k ^ 1);
-    issue_s(hh + 1 < a.hph ? h + 1 : hbase + a.hph - 1);
+    issue_s(hn);
 
     // ---- phase B: K3 d_dv^T = dS_{c+1} . B^T and ORANGE d_v_or^T = dy^T . w for
     // the item (p tile ipt, row block irb); dx; K3 decay and dvx row sums ----
