@@ -377,7 +377,13 @@ __global__ void __launch_bounds__(NTH16) ssd_chunk16_kernel(SsdArgs a) {
     const bf16* dys = dysb + k * LM16 * LDP;
     const bf16* dSs = dSsb + k * PN;
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-direct loads have landed
+    // this wave's LDS-direct loads have landed: vmcnt(0) on entry; after a head,
+    // vmcnt(1), which leaves its dx store (the newest operation; the vector
+    // memory count retires in issue order) in flight
+    if (hh == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F71);
     __syncthreads();  // this head staged; the previous head's phase B done (and CB on entry)
 
     // the next head (unconditional: past the last head the last head is
