@@ -18,8 +18,14 @@
 //     the group's heads.
 //   target role (block = t): per head, BLUE (dC_blue = exp(cumA) dy.S_c and
 //     its row sums against C), then for every source block s <= t the same
-//     CB, G1, d_cb (recomputed, transposed), giving dC_k2 += d_cb.B and the
+//     G1 and d_cb (recomputed, transposed), giving dC_k2 += d_cb.B, and the
 //     row sums of d_cb * CB.  Stores dC summed over the group's heads.
+//     Those row sums need no CB tiles when a group has one head: since
+//     CB = C.B^T and dC_k2 = d_cb.B, sum_s d_cb[t,s] CB[t,s] equals
+//     sum_n C[t,n] dC_k2[t,n], so BLUE's and ORANGE's row sums are read off
+//     together from the finished dC tiles (sum_n C dC), the same refactor as
+//     BLUE's own.  With several heads per group the dC tiles hold the sum over
+//     heads, and the per-head row sums come from the recomputed CB tiles.
 //
 // Each wave owns one 16-row tile of its block (an s tile or a t tile), so the
 // d_cb and w tiles it computes are already in the MFMA operand layout that its
@@ -182,8 +188,9 @@ __device__ __forceinline__ void bk_pipeline_reads() {
 }
 
 // bf16: two workgroups per CU, at most 256 registers (VGPR + AGPR) per lane.
-// CP, CN, CM: compile-time P, N and rank M (0: from the arguments).
-template <typename T, int CP, int CN, int CM>
+// CP, CN, CM: compile-time P, N and rank M (0: from the arguments); ONEH: one
+// head per group (the target role's row sums from its dC tiles).
+template <typename T, int CP, int CN, int CM, bool ONEH>
 __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) ssd_blocked_bwd_kernel(SsdArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr bool SWZ = BF && CP && CN && CP % 64 == 0 && CN % 64 == 0;  // swizzled, unpadded tiles
@@ -548,13 +555,18 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
           f32x4 acc = zero4();
           for (int kb = 0; kb < PT; ++kb)  // A: rows n, k = p (native tile); B: k = p, columns t
             mma(acc, bk_ntv<SWZ>(STs + tile_off(kb, nt), lane), bk_colk<SWZ>(dys, LDP, 16 * w, 16 * kb, lane));
-          float cv[4];
-          frag_get(bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
+          if constexpr (ONEH) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float val = acc[j] * ecol;
-            dCT[nt][j] += val;
-            blue += cv[j] * val;
+            for (int j = 0; j < 4; ++j) dCT[nt][j] += acc[j] * ecol;
+          } else {
+            float cv[4];
+            frag_get(bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float val = acc[j] * ecol;
+              dCT[nt][j] += val;
+              blue += cv[j] * val;
+            }
           }
         }
       }
@@ -571,8 +583,9 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         f32x4 cb = zero4(), g1 = zero4();
-        for (int kb = 0; kb < NT; ++kb)
-          mma(cb, bk_colk<SWZ>(Bs, LDN, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * kb, lane));
+        if constexpr (!ONEH)
+          for (int kb = 0; kb < NT; ++kb)
+            mma(cb, bk_colk<SWZ>(Bs, LDN, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * kb, lane));
         for (int kb = 0; kb < PT; ++kb)
           mma(g1, bk_colk<SWZ>(xs, LDP, 16 * ss, 16 * kb, lane), bk_colk<SWZ>(dys, LDP, 16 * w, 16 * kb, lane));
         float dv[4];
@@ -593,7 +606,7 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
             dd = (ls <= l_col && l_col < Lc) ? d_s * exp_hw(cum_t - cs_s) : 0.0f;
           }
           const float dcb = g1[j] * dd;
-          orow += dcb * cb[j];
+          if constexpr (!ONEH) orow += dcb * cb[j];
           dv[j] = dcb;
         }
         df[ss] = frag_make<T>(dv);
@@ -608,6 +621,16 @@ __global__ void __launch_bounds__(BK_NTH) __attribute__((amdgpu_waves_per_eu(siz
       if constexpr (CP && CN) bk_pipeline_reads<4 * CN / 16, 8>();
 
       if (sb == blk) {  // the head's row sums
+        if constexpr (ONEH) {  // BLUE + ORANGE: sum_n C[t,n] dC[t,n] over the finished dC tiles
+#pragma unroll
+          for (int nt = 0; nt < BK_TMAX; ++nt) {
+            if (nt >= NT) continue;
+            float cv[4];
+            frag_get(bk_colk<SWZ>(Cs, LDN, 16 * w, 16 * nt, lane), cv);  // C[t][n .. n+3], n = 16 nt + 4q
+#pragma unroll
+            for (int j = 0; j < 4; ++j) blue += cv[j] * dCT[nt][j];
+          }
+        }
         const float bw = sum4q(blue), ow = sum4q(orow);
         float* rv = rowv_c + h * RV_N * LM;
         if (q == 0) {
@@ -678,17 +701,26 @@ bool ssd_blocked_supported(const ssmvjp_ssd_desc& d) {
   return blocked_lds_bytes(d.headdim, d.dstate, d.dtype == SSMVJP_BF16) <= 160 * 1024;
 }
 
+template <typename T, bool ONEH>
+static void launch_blocked_h(const SsdArgs& a, size_t lds, i64 grid, hipStream_t stream) {
+  const bool fixed = a.P == 64 && a.N == 128;
+  if (fixed && a.M == 4)  // the rank-4 MIMO workload shape
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 4, ONEH>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  else if (fixed)
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 0, ONEH>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  else
+    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0, 0, ONEH>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+}
+
 template <typename T>
 static void launch_blocked_t(const SsdArgs& a, hipStream_t stream) {
   const bool fixed = a.P == 64 && a.N == 128;
   const size_t lds = blocked_lds_bytes(a.P, a.N, sizeof(T) == 2, fixed && sizeof(T) == 2);
   const i64 grid = a.b * a.nc * a.G * 2 * (a.LM / BK_R);
-  if (fixed && a.M == 4)  // the rank-4 MIMO workload shape
-    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 4>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
-  else if (fixed)
-    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 64, 128, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+  if (a.hpg == 1)
+    launch_blocked_h<T, true>(a, lds, grid, stream);
   else
-    hipLaunchKernelGGL((ssd_blocked_bwd_kernel<T, 0, 0, 0>), dim3((unsigned)grid), dim3(BK_NTH), lds, stream, a);
+    launch_blocked_h<T, false>(a, lds, grid, stream);
   hipLaunchKernelGGL(ssd_blocked_epilogue_kernel, dim3((unsigned)(a.b * a.nc * a.H)), dim3(64), 0, stream, a);
 }
 
