@@ -41,7 +41,10 @@
 //    together with the slice's part of dbeta = sum over the columns of u r.
 //  * delta_reduce_kernel adds the slice partials in slice order, applies the
 //    sum over the value heads of each qk head (ascending), and forms dq, dk,
-//    dg and dbeta.
+//    dg and dbeta.  The walk's dk partials leave out the factor beta_t, which
+//    is the same for every column of a value head: the reduction applies it
+//    once per value head.  Likewise dq_e = S_t do is taken as
+//    S_dec do + beta_t k (r . do), so the walk never rebuilds S_t per element.
 // The next sub-segment's inputs and checkpoint are loaded into registers while
 // the current one runs.  Everything is float32; every sum runs in a fixed
 // order, so results are bitwise reproducible.  No float atomics.
@@ -58,7 +61,7 @@ constexpr int VT = 2;            // state columns per thread
 constexpr int NE = 4 * VT;       // state elements per thread (4 rows x VT columns)
 constexpr int VS = NW * 2 * VT;  // columns of the state per workgroup (16 column blocks of 2)
 constexpr int NS = 8;            // steps per sub-segment = checkpoint interval
-constexpr int NQ = 3;            // per-row outputs: dq_e, dk_e, dg
+constexpr int NQ = 3;            // per-row outputs: dq_e, dk_e / beta, dg
 constexpr int NO = 4 * NQ;       // per-row outputs of one thread (4 rows each)
 
 struct DeltaArgs {
@@ -331,21 +334,23 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
       ld_cols(&sdo[s][VT * vq], dd);
       ld_cols(&sr[s][VT * vq], rr);
       const float beta = sb[s];
-      float o[NO];  // per-row outputs: o[4*qd + i], qd = dq_e, dk_e, dg
+      float o[NO];  // per-row outputs: o[4*qd + i], qd = dq_e, dk_e / beta, dg
       float da[4], up[VT];
+      float rd = 0.0f;  // r . do over this thread's columns
+#pragma unroll
+      for (int c = 0; c < VT; ++c) rd = fmaf(rr[c], dd[c], rd);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ai = beta * kk[i];
         float dq_e = 0.0f, dai = 0.0f;
 #pragma unroll
         for (int c = 0; c < VT; ++c) {
           const int e = VT * i + c;
-          dS[e] = fmaf(qq[i], dd[c], dS[e]);                     // dS' = dS + (scale q) (x) do
-          dq_e = fmaf(fmaf(ai, rr[c], sd[s][e]), dd[c], dq_e);  // dq_e = S_t do
-          dai = fmaf(rr[c], dS[e], dai);                        // dS' r
+          dS[e] = fmaf(qq[i], dd[c], dS[e]);  // dS' = dS + (scale q) (x) do
+          dq_e = fmaf(sd[s][e], dd[c], dq_e); // S_dec do
+          dai = fmaf(rr[c], dS[e], dai);      // dS' r
           up[c] = i == 0 ? kk[i] * dS[e] : fmaf(kk[i], dS[e], up[c]);  // u = dS'^T k
         }
-        o[i] = dq_e;
+        o[i] = fmaf(beta * kk[i], rd, dq_e);  // dq_e = S_t do = S_dec do + beta k (r . do)
         da[i] = dai;
       }
       float u[VT], dr[VT];
@@ -357,16 +362,16 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
       const float bpart = fmaf(rr[0], u[0], rr[1] * u[1]);  // this column block's u . r
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float su = 0.0f, dg = 0.0f;
+        float dg = 0.0f;
 #pragma unroll
         for (int c = 0; c < VT; ++c) {
           const int e = VT * i + c;
-          su = fmaf(sd[s][e], u[c], su);        // S_dec u
-          dS[e] = fmaf(-kk[i], dr[c], dS[e]);   // dS_dec = dS' - k (x) dr
-          dg = fmaf(sd[s][e], dS[e], dg);       // dg = rowsum(S_dec (.) dS_dec)
-          dS[e] *= eg[i];                       // dS_{t-1} = exp(g) (.) dS_dec
+          da[i] = fmaf(sd[s][e], -u[c], da[i]);  // dS' r - S_dec u
+          dS[e] = fmaf(-kk[i], dr[c], dS[e]);    // dS_dec = dS' - k (x) dr
+          dg = fmaf(sd[s][e], dS[e], dg);        // dg = rowsum(S_dec (.) dS_dec)
+          dS[e] *= eg[i];                        // dS_{t-1} = exp(g) (.) dS_dec
         }
-        o[4 + i] = beta * (da[i] - su);         // dk_e = beta (dS' r - S_dec u)
+        o[4 + i] = da[i];  // dk_e / beta (the reduction applies beta per value head)
         o[8 + i] = dg;
       }
       // dv = dr: this column block's values, from one lane per half wave
@@ -444,10 +449,11 @@ __global__ void __launch_bounds__(256) delta_reduce_kernel(DeltaArgs a) {
       for (i64 vs = 0; vs < a.nvs; ++vs) db += pb[vs];
       a.dbeta[bt * a.HV + hv] = db;
     }
+    const float bv = a.beta[bt * a.HV + hv];  // dk_e = beta (dS' r - S_dec u): beta applied here
     dq0 += s[0][0];
     dq1 += s[0][1];
-    dk0 += s[1][0];
-    dk1 += s[1][1];
+    dk0 = fmaf(bv, s[1][0], dk0);
+    dk1 = fmaf(bv, s[1][1], dk1);
   }
   float* dqp = a.dq + (bt * a.H + h) * DK;
   float* dkp = a.dk + (bt * a.H + h) * DK;
