@@ -79,10 +79,25 @@ __global__ void seq_ckpt_kernel(SeqArgs a) {
   const T* x = (const T*)a.x;
   const T* B = (const T*)a.B;
   float s = a.s0 ? a.s0[e] : 0.0f;
-  for (i64 t = 0; t < a.T; ++t) {
-    if (t % a.K == 0) a.ck[(t / a.K) * total + e] = s;
-    const float d = a.delta[(bi * a.T + t) * a.H + h];
-    s = scan_step(s, d, acoef, ld(x, ((bi * a.T + t) * a.H + h) * a.P + p), ld(B, ((bi * a.T + t) * a.G + g) * a.N + n));
+  // the inputs of CK_GS steps are loaded together, so that their latencies
+  // overlap (steps past the end reload the last step; their values go unused)
+  constexpr int CK_GS = 8;
+  for (i64 tb = 0; tb < a.T; tb += CK_GS) {
+    float gd[CK_GS], gx[CK_GS], gb[CK_GS];
+#pragma unroll
+    for (int i = 0; i < CK_GS; ++i) {
+      const i64 t = tb + i < a.T ? tb + i : a.T - 1;
+      gd[i] = a.delta[(bi * a.T + t) * a.H + h];
+      gx[i] = ld(x, ((bi * a.T + t) * a.H + h) * a.P + p);
+      gb[i] = ld(B, ((bi * a.T + t) * a.G + g) * a.N + n);
+    }
+#pragma unroll
+    for (int i = 0; i < CK_GS; ++i) {
+      const i64 t = tb + i;
+      if (t >= a.T) break;
+      if (t % a.K == 0) a.ck[(t / a.K) * total + e] = s;
+      s = scan_step(s, gd[i], acoef, gx[i], gb[i]);
+    }
   }
 }
 
