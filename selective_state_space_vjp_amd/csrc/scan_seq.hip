@@ -19,7 +19,10 @@
 //   3. seq_bwd        one workgroup per (b,h): per segment (last first)
 //                     recompute, then the reverse walk; per-step reductions
 //                     over n (dx), over p (this head's dB, dC) and over (p,n)
-//                     (d_dt) go through LDS in a fixed order.
+//                     (d_dt) go through LDS in a fixed order.  When one
+//                     thread holds a whole column of the state (P <= 16) and
+//                     a segment fits in LDS, seq_bwd_lds stages the segment's
+//                     inputs and recomputed states there instead.
 //   4. seq_group_sum  dB, dC = sum over the heads of each group, ascending h.
 #include "common.cuh"
 #include "kernels.h"
@@ -239,6 +242,162 @@ __global__ void __launch_bounds__(1024) seq_bwd_kernel(SeqArgs a, int PPT, int N
   }
 }
 
+// The same reverse walk for small states (every p of a column in one thread,
+// NPG = 1), with each segment's inputs (delta, B, C, x, dy of its K steps) and
+// its recomputed states held in LDS: one cooperative load per segment, so the
+// steps themselves read no global memory.  Arithmetic and order are those of
+// seq_bwd_kernel, so the two give identical bits.
+template <typename T, int MAXP>
+__global__ void __launch_bounds__(1024) seq_bwd_lds_kernel(SeqArgs a) {
+  extern __shared__ float smem[];
+  const int P = (int)a.P, N = (int)a.N, K = (int)a.K;
+  const int tid = threadIdx.x, nw = (int)(blockDim.x / 64);
+  const bool active = tid < N;
+  const int n = active ? tid : 0;
+  float* red = smem;                 // [P][N+1]
+  float* colB = red + P * (N + 1);   // [N]
+  float* colC = colB + N;            // [N]
+  float* ddw = colC + N;             // [nw]
+  float* sd = ddw + nw;              // [K]        delta
+  float* sB = sd + K;                // [K][N]
+  float* sC = sB + K * N;            // [K][N]
+  float* sx = sC + K * N;            // [K][P]
+  float* sdy = sx + K * P;           // [K][P]
+  float* sseg = sdy + K * P;         // [K][P][N]  states after each step of the segment
+
+  const i64 bh = blockIdx.x;
+  const i64 bi = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+  const i64 PN = a.P * a.N, total = a.b * a.H * PN;
+  const i64 ebase = bh * PN;
+  const T* x = (const T*)a.x;
+  const T* B = (const T*)a.B;
+  const T* C = (const T*)a.C;
+  const T* dy = (const T*)a.dy;
+  T* dx = (T*)a.dx;
+  const float acoef = a.per_state ? a.A[h * a.N + n] : a.A[h];
+
+  float dS[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) dS[p] = (p < P && active && a.dsf) ? a.dsf[ebase + (i64)p * N + n] : 0.0f;
+  float dAacc = 0.0f;
+
+  for (i64 j = a.J - 1; j >= 0; --j) {
+    const i64 t0 = j * a.K;
+    const int kc = (int)((t0 + a.K < a.T) ? a.K : a.T - t0);  // steps in this segment
+    __syncthreads();  // the previous segment is done with the staged rows
+    // stage the segment's inputs (every load of the block in flight together)
+    const int per = 1 + 2 * N + 2 * P;
+    for (int idx = tid; idx < kc * per; idx += (int)blockDim.x) {
+      const int k = idx / per, r = idx % per;
+      const i64 t = t0 + k;
+      if (r == 0) {
+        sd[k] = a.delta[(bi * a.T + t) * a.H + h];
+      } else if (r <= N) {
+        sB[k * N + r - 1] = ld(B, ((bi * a.T + t) * a.G + g) * a.N + r - 1);
+      } else if (r <= 2 * N) {
+        sC[k * N + r - 1 - N] = ld(C, ((bi * a.T + t) * a.G + g) * a.N + r - 1 - N);
+      } else if (r <= 2 * N + P) {
+        sx[k * P + r - 1 - 2 * N] = ld(x, ((bi * a.T + t) * a.H + h) * a.P + r - 1 - 2 * N);
+      } else {
+        sdy[k * P + r - 1 - 2 * N - P] = ld(dy, ((bi * a.T + t) * a.H + h) * a.P + r - 1 - 2 * N - P);
+      }
+    }
+    float ck0[MAXP];  // the checkpoint: the state before step t0
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) ck0[p] = (p < P && active) ? a.ck[j * total + ebase + (i64)p * N + n] : 0.0f;
+    __syncthreads();
+    // recompute the segment's states (own column only)
+    if (active) {
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) {
+        if (p >= P) continue;
+        float s = ck0[p];
+        for (int k = 0; k < kc; ++k) {
+          s = scan_step(s, sd[k], acoef, sx[k * P + p], sB[k * N + n]);
+          sseg[(k * P + p) * N + n] = s;
+        }
+      }
+    }
+    for (int k = kc - 1; k >= 0; --k) {
+      const i64 t = t0 + k;
+      const i64 bth = (bi * a.T + t) * a.H + h;
+      const float d = sd[k];
+      const float av = expf(__fmul_rn(d, acoef));
+      const float Bn = sB[k * N + n];
+      const float Cn = sC[k * N + n];
+      float dbn = 0.0f, dcn = 0.0f, dd = 0.0f, dAs = 0.0f;
+      __syncthreads();  // previous step's readers of red/colB/colC/ddw are done
+      if (active) {
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+          if (p >= P) continue;
+          const float xp = sx[k * P + p];
+          const float dyp = sdy[k * P + p];
+          const float s_t = sseg[(k * P + p) * N + n];
+          const float s_prev = k > 0 ? sseg[((k - 1) * P + p) * N + n] : ck0[p];
+          dS[p] += dyp * Cn;                              // y_t = C_t . s_t
+          dcn += dyp * s_t;                               // dC_t uses s_t
+          dbn += dS[p] * xp;                              // dB_t (before the delta factor)
+          dd += dS[p] * (xp * Bn + acoef * av * s_prev);  // input path + decay path
+          dAs += dS[p] * s_prev;
+          red[p * (N + 1) + n] = dS[p] * Bn;
+        }
+        dAacc += d * av * dAs;
+        colB[n] = dbn;
+        colC[n] = dcn;
+      }
+      dd = wave_sum(dd);
+      if ((tid & 63) == 0) ddw[tid >> 6] = dd;
+      __syncthreads();
+      // dx row sums over n in order (as seq_bwd_kernel sums them), with the
+      // LDS reads of eight terms in flight together
+      for (int p = tid; p < P; p += (int)blockDim.x) {
+        const float* rp = red + p * (N + 1);
+        float acc = 0.0f;
+        int nn = 0;
+        for (; nn + 8 <= N; nn += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = rp[nn + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        for (; nn < N; ++nn) acc += rp[nn];
+        st(dx, bth * a.P + p, d * acc);
+      }
+      if (tid < N) {
+        a.dBh[bth * a.N + tid] = d * (0.0f + colB[tid]);
+        a.dCh[bth * a.N + tid] = 0.0f + colC[tid];
+      }
+      if (tid == 0) {
+        float s = 0.0f;
+        for (int w = 0; w < nw; ++w) s += ddw[w];
+        a.d_dt[bth] = s * a.sig[bth];
+      }
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) dS[p] *= av;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p)
+    if (p < P && active) a.d_s0[ebase + (i64)p * N + n] = dS[p];
+  if (a.dA_part) {  // uniform: one column per state (per state) or a sum over all threads (per head)
+    __syncthreads();  // the last step's readers of colB and ddw are done
+    if (a.per_state) {
+      if (tid < N) a.dA_part[bh * a.N + tid] = 0.0f + dAacc;
+    } else {
+      const float v = wave_sum(active ? dAacc : 0.0f);
+      if ((tid & 63) == 0) ddw[tid >> 6] = v;
+      __syncthreads();
+      if (tid == 0) {
+        float s = 0.0f;
+        for (int w = 0; w < nw; ++w) s += ddw[w];
+        a.dA_part[bh] = s;
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ void seq_group_sum_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh, i64 bT, i64 H,
                                      i64 G, i64 N, T* __restrict__ dB, T* __restrict__ dC) {
@@ -301,6 +460,14 @@ size_t seq_lds_bytes(const ssmvjp_scan_desc& d, const SeqPlan& plan) {
   return sizeof(float) * ((size_t)d.headdim * (d.dstate + 1) + 2 * (size_t)plan.NPG * d.dstate + nw);
 }
 
+// LDS of seq_bwd_lds_kernel: the reduction buffers plus one segment's inputs
+// and states
+static size_t seq_lds_small_bytes(const ssmvjp_scan_desc& d, const SeqPlan& plan) {
+  const i64 nw = cdiv(d.dstate, 64);
+  return sizeof(float) * ((size_t)d.headdim * (d.dstate + 1) + 2 * (size_t)d.dstate + nw +
+                          (size_t)plan.K * (1 + 2 * d.dstate + 2 * d.headdim + d.headdim * d.dstate));
+}
+
 template <typename T>
 static hipError_t launch_seq_t(const ssmvjp_scan_desc& d, const SeqPlan& plan, const SeqPointers& ptr,
                                hipStream_t stream) {
@@ -328,8 +495,16 @@ static hipError_t launch_seq_t(const ssmvjp_scan_desc& d, const SeqPlan& plan, c
   }
   if (a.b * a.H > 0) {
     const int NT = (int)cdiv(a.N * plan.NPG, 64) * 64;
-    hipLaunchKernelGGL((seq_bwd_kernel<T, 16>), dim3((unsigned)(a.b * a.H)), dim3(NT), seq_lds_bytes(d, plan),
-                       stream, a, plan.PPT, plan.NPG);
+    const size_t small = seq_lds_small_bytes(d, plan);
+    if (plan.NPG == 1 && small <= 64 * 1024) {  // one thread holds a whole column: the LDS-staged walk
+      if (a.P <= 4)
+        hipLaunchKernelGGL((seq_bwd_lds_kernel<T, 4>), dim3((unsigned)(a.b * a.H)), dim3(NT), small, stream, a);
+      else
+        hipLaunchKernelGGL((seq_bwd_lds_kernel<T, 16>), dim3((unsigned)(a.b * a.H)), dim3(NT), small, stream, a);
+    } else {
+      hipLaunchKernelGGL((seq_bwd_kernel<T, 16>), dim3((unsigned)(a.b * a.H)), dim3(NT), seq_lds_bytes(d, plan),
+                         stream, a, plan.PPT, plan.NPG);
+    }
   }
   if (bTH > 0) {
     const i64 n = a.b * a.T * a.G * a.N;
