@@ -82,14 +82,17 @@ __global__ void seq_ckpt_kernel(SeqArgs a) {
   const T* x = (const T*)a.x;
   const T* B = (const T*)a.B;
   float s = a.s0 ? a.s0[e] : 0.0f;
-  // the inputs of CK_GS steps are loaded together, so that their latencies
-  // overlap (steps past the end reload the last step; their values go unused)
+  // the walk stops at the last checkpoint, the state before step (J-1) K:
+  // the steps after it are recomputed by the reverse pass from that checkpoint.
+  // The inputs of CK_GS steps are loaded together, so that their latencies
+  // overlap (indices past the last step reload it; those values go unused).
   constexpr int CK_GS = 8;
-  for (i64 tb = 0; tb < a.T; tb += CK_GS) {
+  const i64 tlast = (a.J - 1) * a.K;
+  for (i64 tb = 0; tb < tlast; tb += CK_GS) {
     float gd[CK_GS], gx[CK_GS], gb[CK_GS];
 #pragma unroll
     for (int i = 0; i < CK_GS; ++i) {
-      const i64 t = tb + i < a.T ? tb + i : a.T - 1;
+      const i64 t = tb + i < tlast ? tb + i : tlast - 1;
       gd[i] = a.delta[(bi * a.T + t) * a.H + h];
       gx[i] = ld(x, ((bi * a.T + t) * a.H + h) * a.P + p);
       gb[i] = ld(B, ((bi * a.T + t) * a.G + g) * a.N + n);
@@ -97,11 +100,12 @@ __global__ void seq_ckpt_kernel(SeqArgs a) {
 #pragma unroll
     for (int i = 0; i < CK_GS; ++i) {
       const i64 t = tb + i;
-      if (t >= a.T) break;
+      if (t >= tlast) break;
       if (t % a.K == 0) a.ck[(t / a.K) * total + e] = s;
       s = scan_step(s, gd[i], acoef, gx[i], gb[i]);
     }
   }
+  if (a.J > 0) a.ck[(a.J - 1) * total + e] = s;
 }
 
 // Thread layout of seq_bwd: thread tid = pg * N + n owns column n and the p
