@@ -115,8 +115,8 @@ __device__ __forceinline__ Slot slot_of(const DeltaArgs& a) {
 
 // One forward step on this thread's 4 x VT block (S[VT*i+c]: row 4kq+i,
 // column VT*vq+c): sd = exp(g) (.) S, r = v - k^T sd (column sums over the
-// half wave), S = sd + (beta k) (x) r.
-__device__ __forceinline__ void fwd_step(float S[NE], float sd[NE], f32x4 eg, f32x4 kk, float beta, const float vv[VT],
+// half wave), S = sd + (beta k) (x) r, with beta k staged per step (bk).
+__device__ __forceinline__ void fwd_step(float S[NE], float sd[NE], f32x4 eg, f32x4 kk, f32x4 bk, const float vv[VT],
                                          float r[VT]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -130,11 +130,9 @@ __device__ __forceinline__ void fwd_step(float S[NE], float sd[NE], f32x4 eg, f3
     r[c] = vv[c] - sum32(p);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float ai = beta * kk[i];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int c = 0; c < VT; ++c) S[VT * i + c] = fmaf(ai, r[c], sd[VT * i + c]);
-  }
+    for (int c = 0; c < VT; ++c) S[VT * i + c] = fmaf(bk[i], r[c], sd[VT * i + c]);
 }
 
 __device__ __forceinline__ void ld_cols(const float* p, float o[VT]) {
@@ -165,9 +163,9 @@ __device__ __forceinline__ void load_block(float S[NE], const float* base, i64 V
 
 __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
   __shared__ __align__(16) float sk[NS][DK];
+  __shared__ __align__(16) float sbk[NS][DK];  // beta k
   __shared__ __align__(16) float se[NS][DK];
   __shared__ __align__(16) float sv[NS][VS];
-  __shared__ float sb[NS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kq = lane & 31, vq = 2 * w + (lane >> 5);
   const Slot sl = slot_of(a);
@@ -176,7 +174,7 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
   float S[NE];
   load_block(S, a.S0 ? a.S0 + (sl.bi * a.HV + sl.hv) * DK * V + sl.vs * VS : nullptr, V, kq, vq);
   // register prefetch of one sub-segment (threads 0..255): k and g rows (one
-  // float4 each), the slice of v (threads 0..63), beta (threads 0..NS-1)
+  // float4 each) and the row's beta, the slice of v (threads 0..63)
   u32x4 pk, pg, pv;
   float pb;
   const int srow = (tid & 255) >> 5, scol = 4 * (tid & 31);
@@ -191,7 +189,7 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
     pk = bload16(rk, stager ? (unsigned)((srow * a.H * DK + scol) * 4) : BUF_OOB);
     pg = bload16(rg, stager ? (unsigned)((srow * a.HV * DK + scol) * 4) : BUF_OOB);
     pv = bload16(rv, tid < NS * VS / 4 ? (unsigned)(((tid >> 3) * a.HV * V + 4 * (tid & 7)) * 4) : BUF_OOB);
-    pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
+    pb = bload_f32(rb, stager ? (unsigned)(srow * a.HV * 4) : BUF_OOB);
   };
   float* ckb = a.ck + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * (NE * NTH);
   float* rb = a.rres + ((sl.bi * a.HV + sl.hv) * a.nvs + sl.vs) * a.nck * NS * VS;
@@ -204,12 +202,12 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
       *(f32x4*)(ckb + (j * (NE / 4) + i) * NTH * 4 + tid * 4) = f32x4{S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]};
     __syncthreads();  // the previous sub-segment is done with the staged rows
     if (stager) {
-      *(f32x4*)&sk[srow][scol] = as_f4(pk);
-      const f32x4 gg = as_f4(pg);
+      const f32x4 kk = as_f4(pk), gg = as_f4(pg);
+      *(f32x4*)&sk[srow][scol] = kk;
+      *(f32x4*)&sbk[srow][scol] = f32x4{pb * kk[0], pb * kk[1], pb * kk[2], pb * kk[3]};
       *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
     }
     if (tid < NS * VS / 4) *(f32x4*)&sv[tid >> 3][4 * (tid & 7)] = as_f4(pv);
-    if (tid < NS) sb[tid] = pb;
     if (j + 1 < a.nck) issue(j + 1);
     __syncthreads();
 #pragma unroll
@@ -217,7 +215,7 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
       if (s >= ns) break;
       float sd[NE], r[VT], vv[VT];
       ld_cols(&sv[s][VT * vq], vv);
-      fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), sb[s], vv, r);
+      fwd_step(S, sd, lds4(&se[s][4 * kq]), lds4(&sk[s][4 * kq]), lds4(&sbk[s][4 * kq]), vv, r);
       // the residual of this step for the backward's recompute (one lane per column block)
       if (kq == 0) *(float2*)(rb + (j * NS + s) * VS + VT * vq) = make_float2(r[0], r[1]);
     }
@@ -230,6 +228,7 @@ __global__ void __launch_bounds__(NTH) delta_fwd_ckpt_kernel(DeltaArgs a) {
 __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
   __shared__ __align__(16) float sq[NS][DK];  // scale * q
   __shared__ __align__(16) float sk[NS][DK];
+  __shared__ __align__(16) float sbk[NS][DK];  // beta k
   __shared__ __align__(16) float se[NS][DK];  // exp(g)
   __shared__ __align__(16) float sdo[NS][VS];
   __shared__ __align__(16) float sr[NS][VS];  // r of each step, per column
@@ -246,9 +245,10 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
 
   // register prefetch of one sub-segment: q, k, g rows (threads 0..255, one
   // float4 each), the slices of r (threads 0..63) and do (threads 64..127),
-  // beta (threads 0..NS-1), and every thread's part of the checkpoint
+  // beta (threads 0..NS-1, and each stager its row's), and every thread's
+  // part of the checkpoint
   u32x4 pq, pk, pg, pr, pd, pc[NE / 4];
-  float pb;
+  float pb, pbr;
   const int srow = (tid & 255) >> 5, scol = 4 * (tid & 31);
   const bool stager = tid < 256;
   const int vrow = (tid & 63) >> 3, vcol = 4 * (tid & 7);
@@ -273,6 +273,7 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     pr = bload16(rr, tid < 64 ? (unsigned)((vrow * VS + vcol) * 4) : BUF_OOB);
     pd = bload16(rd, tid >= 64 && tid < 128 ? (unsigned)((vrow * a.HV * V + vcol) * 4) : BUF_OOB);
     pb = bload_f32(rb, tid < NS ? (unsigned)(tid * a.HV * 4) : BUF_OOB);
+    pbr = bload_f32(rb, stager ? (unsigned)(srow * a.HV * 4) : BUF_OOB);
 #pragma unroll
     for (int i = 0; i < NE / 4; ++i) pc[i] = bload16(rc, (unsigned)((i * NTH + tid) * 16));
   };
@@ -286,9 +287,10 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     float S[NE];
     {
       if (stager) {
-        const f32x4 qq = as_f4(pq), gg = as_f4(pg);
+        const f32x4 qq = as_f4(pq), gg = as_f4(pg), kk = as_f4(pk);
         *(f32x4*)&sq[srow][scol] = f32x4{a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]};
-        *(f32x4*)&sk[srow][scol] = as_f4(pk);
+        *(f32x4*)&sk[srow][scol] = kk;
+        *(f32x4*)&sbk[srow][scol] = f32x4{pbr * kk[0], pbr * kk[1], pbr * kk[2], pbr * kk[3]};
         *(f32x4*)&se[srow][scol] = f32x4{expf(gg[0]), expf(gg[1]), expf(gg[2]), expf(gg[3])};
       }
       if (tid < 64) *(f32x4*)&sr[vrow][vcol] = as_f4(pr);
@@ -310,17 +312,15 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s >= ns) break;
-      const f32x4 eg = lds4(&se[s][4 * kq]), kk = lds4(&sk[s][4 * kq]);
+      const f32x4 eg = lds4(&se[s][4 * kq]), bk = lds4(&sbk[s][4 * kq]);
       float rr[VT];
       ld_cols(&sr[s][VT * vq], rr);
-      const float beta = sb[s];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ai = beta * kk[i];
 #pragma unroll
         for (int c = 0; c < VT; ++c) {
           sd[s][VT * i + c] = eg[i] * S[VT * i + c];
-          S[VT * i + c] = fmaf(ai, rr[c], sd[s][VT * i + c]);
+          S[VT * i + c] = fmaf(bk[i], rr[c], sd[s][VT * i + c]);
         }
       }
     }
@@ -330,6 +330,7 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
     for (int s = NS - 1; s >= 0; --s) {
       if (s >= ns) continue;
       const f32x4 qq = lds4(&sq[s][4 * kq]), kk = lds4(&sk[s][4 * kq]), eg = lds4(&se[s][4 * kq]);
+      const f32x4 bk = lds4(&sbk[s][4 * kq]);
       float dd[VT], rr[VT];
       ld_cols(&sdo[s][VT * vq], dd);
       ld_cols(&sr[s][VT * vq], rr);
@@ -350,7 +351,7 @@ __global__ void __launch_bounds__(NTH) delta_bwd_kernel(DeltaArgs a) {
           dai = fmaf(rr[c], dS[e], dai);      // dS' r
           up[c] = i == 0 ? kk[i] * dS[e] : fmaf(kk[i], dS[e], up[c]);  // u = dS'^T k
         }
-        o[i] = fmaf(beta * kk[i], rd, dq_e);  // dq_e = S_t do = S_dec do + beta k (r . do)
+        o[i] = fmaf(bk[i], rd, dq_e);  // dq_e = S_t do = S_dec do + beta k (r . do)
         da[i] = dai;
       }
       float u[VT], dr[VT];
